@@ -1,0 +1,133 @@
+"""CPU oracle for the tiled fp16 GEMM (+ fused bias + ReLU).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the bench's CPU
+baseline may import this package.  It is a plain fp64 implementation of the
+definition C = A.B (and C = max(A.B + bias, 0)) written from the TileLang pages
+(lqnn.cn walkthrough sections 2.1 and 4.2; codechina.net article section 3.2;
+xdnf.cn article section 4.2), in C (tgref.c), bound here with ctypes.  It
+shares no code with the HIP library and never imports it.
+
+Every function is pinned by tests/test_oracle.py against closed forms, exact
+rational brute force, invariants and numpy's own fp16 conversion.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.tgref_f16_decode.argtypes = [ctypes.c_uint16]
+        L.tgref_f16_decode.restype = ctypes.c_double
+        L.tgref_f16_encode.argtypes = [ctypes.c_double]
+        L.tgref_f16_encode.restype = ctypes.c_uint16
+        L.tgref_decode_array.argtypes = [P, P, I64]
+        L.tgref_to_f32.argtypes = [P, P, I64]
+        L.tgref_to_f16.argtypes = [P, P, I64]
+        L.tgref_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int]
+        L.tgref_gemm.restype = ctypes.c_int
+        L.tgref_gemm_entries.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64]
+        L.tgref_gemm_entries.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def default_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def decode(bits):
+    """fp16 bit patterns (uint16) -> exact float64 values."""
+    bits = _u16(bits)
+    out = np.empty(bits.shape, np.float64)
+    lib().tgref_decode_array(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def encode_f16(x):
+    """float64 -> fp16 bit patterns by direct round-to-nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().tgref_to_f16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def to_f32(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.float32)
+    lib().tgref_to_f32(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def gemm_ref(A, B, M, N, K, lda=None, ldb=None, bias=None, nthreads=None):
+    """Unrounded fp64 reference C (M x N, dense) for fp16-bit operands.
+
+    A: uint16 bits, at least (M-1)*lda + K elements (row-major, leading dim lda).
+    B: uint16 bits, at least (K-1)*ldb + N elements.
+    bias: None (plain GEMM) or float32[N] (fused bias + ReLU).
+    """
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if M > 0 and K > 0:
+        assert A.size >= (M - 1) * lda + K
+    if K > 0 and N > 0:
+        assert B.size >= (K - 1) * ldb + N
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.size >= N
+    C = np.zeros((M, N), np.float64)
+    rc = lib().tgref_gemm(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, lda, ldb, N,
+                          nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("tgref_gemm rejected its arguments")
+    return C
+
+
+def gemm_entries(A, B, rows, cols, K, lda, ldb, bias=None):
+    """Unrounded fp64 reference values at the listed (row, col) positions."""
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty(rows.shape, np.float64)
+    rc = lib().tgref_gemm_entries(_ptr(A), _ptr(B), _ptr(bias), _ptr(rows), _ptr(cols),
+                                  rows.size, _ptr(out), K, lda, ldb)
+    if rc != 0:
+        raise ValueError("tgref_gemm_entries rejected its arguments")
+    return out
+
+
+def output_typed(cref, c_dtype):
+    """Round the fp64 reference to the output type: 'f32' -> float32 (RNE),
+    'f16' -> fp16 bit patterns (direct RNE from double)."""
+    if c_dtype == "f32":
+        return to_f32(cref)
+    if c_dtype == "f16":
+        return encode_f16(cref)
+    raise ValueError(c_dtype)

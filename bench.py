@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled fp16 GEMM on one MI355X, as one JSON line.
+
+A step is one launch of the whole hot path -- tg_gemm (or tg_gemm_bias_relu
+for the fused workload) over one batch of seeded synthetic fp16 input already
+resident in HBM.  The default workload is the 8192^3 GEMM (fp16 A and B with
+N(0,1)/sqrt(K) values from seed 2, fp32 accumulation, fp16 C).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--config ID]
+
+Reported: whole-job TFLOP/s (2MNK per step), the dominant kernel's MFMA
+roofline fraction measured with HIP events on the launch stream, and the
+CPU oracle timed on a bounded sample of the same workload on the host cores.
+Before timing, the output is checked against the oracle on sampled entries;
+a failing check prints no throughput.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tg_inputs as gen  # noqa: E402
+
+# MI355X dense fp16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
+# (= 2516.6 TFLOP/s; AMD's published figure rounds it to 2.5 PFLOP/s).
+PEAK_CUS, PEAK_GHZ, FLOP_PER_CLK_CU = 256, 2.4, 4096
+PEAK_TFLOPS = PEAK_CUS * PEAK_GHZ * FLOP_PER_CLK_CU / 1e3
+
+# HBM traffic of the dominant kernel from rocprofv3 PMC runs (FETCH_SIZE and
+# WRITE_SIZE per dispatch, KiB, scaled by the copy-kernel calibration factor).
+# None until measured for the current kernel.
+TRAFFIC_BYTES = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sq8192", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--samples", type=int, default=2048, help="parity-gate sample size")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    import oracle
+    import tiled_dense_gemm_08_amd as tg
+
+    w = gen.workload(a.workload)
+    M, N, K = w["M"], w["N"], w["K"]
+    fused = w["bias"] is not None
+    c_dtype = w["c_dtype"]
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
+    B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
+    bias = torch.from_numpy(w["bias"]).to(dev) if fused else None
+    tdt = torch.float16 if c_dtype == "f16" else torch.float32
+    C = torch.empty((M, N), dtype=tdt, device=dev)
+    code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    pbias = bias.data_ptr() if fused else None
+    cid = a.config
+    if cid is None:
+        cid = tg.tg_select_config(pa, pb, pbias, pc, M, N, K, K, N, N, code)
+    info = tg.tg_config_info(cid)
+
+    def step():
+        st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, K, N, N, code, s)
+        if st != tg.TG_SUCCESS:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    # ---- parity gate on sampled outputs
+    C.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(123)
+    r = rng.integers(0, M, a.samples)
+    c = rng.integers(0, N, a.samples)
+    out = C.cpu().numpy()
+    vals = out[r, c].astype(np.float64)
+    cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, K, N, bias=w["bias"])
+    tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
+                                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
+                               if c_dtype == "f16" else 0.0)
+    ok = bool(np.all(np.abs(vals - cref) <= tol)) and not np.isnan(out).any()
+    if not ok:
+        print(json.dumps({"error": "parity gate failed", "workload": a.workload,
+                          "config": info["name"]}))
+        return 1
+
+    # ---- timing: warmup, then exactly K steps between two synchronisations
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    per_launch_s = gpu_ms / 1e3 / a.steps
+    flop = 2.0 * M * N * K
+    elapsed = max(wall, gpu_ms / 1e3)
+    value = flop * a.steps / elapsed / 1e12
+    achieved = flop / per_launch_s / 1e12
+
+    # ---- CPU oracle baseline on a bounded sample (whole rows of C)
+    cpu = None
+    if a.cpu_seconds > 0:
+        threads = oracle.default_threads()
+        rows = 8
+        while True:
+            t = time.perf_counter()
+            oracle.gemm_ref(w["A"][:rows], w["B"], rows, N, K, bias=w["bias"], nthreads=threads)
+            dt = time.perf_counter() - t
+            if dt >= a.cpu_seconds / 4 or rows >= M:
+                break
+            rows = min(M, rows * max(2, int(a.cpu_seconds / 4 / max(dt, 1e-3))))
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": "first %d of %d rows of C (%dx%dx%d fp64 dot products), %.1f s"
+                         % (rows, M, rows, N, K, dt)}
+
+    traffic = TRAFFIC_BYTES.get((a.workload, info["name"]))
+    line = {
+        "metric": "GEMM TFLOP/s and % of MI355X fp16 MFMA peak at 8192^3; fused bias+ReLU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed * 1e3 / a.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
+                   "fused_bias_relu": fused, "kernel": info["name"],
+                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,135 @@
+/*
+ * tg.h — C ABI of libtg.so: a tiled fp16 matrix multiply for AMD Instinct
+ * MI355X (gfx950), with an optional fused bias + ReLU epilogue.
+ *
+ * Operation (lqnn.cn TileLang walkthrough, section 2.1, the tiled matmul
+ * listing, and section 4.2, the runnable FP16-input / FP32-accumulate GEMM;
+ * codechina.net TileLang article, section 3.2, the variant with float32 C):
+ *     C[i][j] = sum_{k<K} A[i][k] * B[k][j]
+ * with fp16 A and B, fp32 accumulation and C stored as fp16 or fp32.
+ * Fused variant (xdnf.cn TileLang article, section 4.2, GEMM + bias + ReLU):
+ *     C[i][j] = max(sum_k A[i][k] * B[k][j] + bias[j], 0)
+ *
+ * Layout: every matrix is row-major.  A is M x K with leading dimension lda
+ * (element (i,k) at A[i*lda + k]); B is K x N with ldb; C is M x N with ldc.
+ * Leading dimensions are in elements.  bias is fp32, length N, indexed by the
+ * output column.
+ *
+ * Ownership: the caller owns every buffer.  A, B, C and bias must be device
+ * memory of the current HIP device (hipMalloc, or a framework allocation on
+ * that device).  The library allocates no device memory, keeps no per-call
+ * state and is safe to call from several host threads.  Calls are
+ * asynchronous on `stream` (NULL = the default stream): the buffers must stay
+ * alive, and C must not be read, until the stream has passed the launch.
+ * C must not alias A, B or bias.
+ *
+ * Errors: arguments are validated on the host before any device work; on an
+ * error nothing is launched and C is untouched.  Execution faults surface at
+ * the caller's next synchronisation.
+ *   TG_ERROR_INVALID_VALUE     negative M/N/K; lda < K, ldb < N or ldc < N;
+ *                              a NULL pointer when the call has work to do; a
+ *                              NULL bias in the fused call; an unknown dtype;
+ *                              a pointer not aligned to its element size; an
+ *                              unknown config id
+ *   TG_ERROR_NOT_DEVICE_MEMORY a pointer that is host or unregistered memory,
+ *                              or device memory of another device (a host
+ *                              pointer would otherwise read as garbage or an
+ *                              empty result instead of failing -- the pitfall
+ *                              noted in the lqnn.cn walkthrough, section 5.2)
+ *   TG_ERROR_UNSUPPORTED       the current device is not gfx950, or an operand
+ *                              spans 2 GiB or more (32-bit buffer offsets)
+ *   TG_ERROR_LAUNCH            the HIP runtime rejected the kernel launch
+ *
+ * Edge cases: M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros
+ * (the empty sum), or relu(bias[j]) in the fused call.
+ */
+#ifndef TG_H
+#define TG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2 } tg_dtype;
+
+typedef enum {
+    TG_SUCCESS = 0,
+    TG_ERROR_INVALID_VALUE = 1,
+    TG_ERROR_NOT_DEVICE_MEMORY = 2,
+    TG_ERROR_UNSUPPORTED = 3,
+    TG_ERROR_LAUNCH = 4
+} tg_status;
+
+/* C = A.B (overwrites C; no alpha/beta scaling).  A, B: fp16; C: c_dtype. */
+tg_status tg_gemm(const void *A, const void *B, void *C,
+                  int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc,
+                  tg_dtype c_dtype, hipStream_t stream);
+
+/* C = max(A.B + bias[col], 0) (overwrites C).  bias: fp32[N], required. */
+tg_status tg_gemm_bias_relu(const void *A, const void *B, const float *bias, void *C,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc,
+                            tg_dtype c_dtype, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char *tg_status_string(tg_status s);
+
+/* ---- tuning and test entry points ---------------------------------------
+ * The kernel configurations (block tile, K step, pipeline stages, waves per
+ * workgroup, load path) compiled into the library.  The dispatcher above
+ * picks one per call from a static table chosen offline by an on-device sweep
+ * (lqnn.cn walkthrough, sections 2.3 and 5.3: search block sizes and stages on
+ * the real device, record the best per shape, read the record at run time). */
+
+typedef struct {
+    int id;
+    int block_m, block_n, block_k;   /* workgroup output tile and K step */
+    int stages;                      /* LDS ring depth of the K pipeline */
+    int waves_m, waves_n;            /* wave64 grid inside the workgroup */
+    int direct_lds;                  /* 1: 16-byte global->LDS DMA loads (aligned
+                                        operands only); 0: register-staged loads
+                                        with per-element bounds (any alignment) */
+    int lds_bytes;                   /* LDS per workgroup */
+    const char *name;                /* static string */
+} tg_config_desc;
+
+/* Number of configurations; ids are 0 .. tg_num_configs()-1. */
+int tg_num_configs(void);
+
+/* Describe configuration `id`; TG_ERROR_INVALID_VALUE for an unknown id. */
+tg_status tg_config_info(int id, tg_config_desc *out);
+
+/* Whether configuration `id` can run this problem (alignment and leading-
+ * dimension requirements of its load path): 1 yes, 0 no, -1 invalid args. */
+int tg_config_supports(int id, const void *A, const void *B, const float *bias,
+                       const void *C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
+
+/* The configuration id the dispatcher would use for this call, or -1 for
+ * invalid arguments.  Touches no device state. */
+int tg_select_config(const void *A, const void *B, const float *bias, const void *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
+
+/* Run one specific configuration.  bias == NULL: plain GEMM; bias != NULL:
+ * fused bias + ReLU.  Same validation as tg_gemm; additionally
+ * TG_ERROR_INVALID_VALUE for an unknown id and TG_ERROR_UNSUPPORTED when the
+ * configuration cannot run this problem (see tg_config_supports). */
+tg_status tg_gemm_with_config(int config_id, const void *A, const void *B,
+                              const float *bias, void *C,
+                              int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc,
+                              tg_dtype c_dtype, hipStream_t stream);
+
+/* Library version string (static). */
+const char *tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H */

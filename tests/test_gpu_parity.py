@@ -1,0 +1,243 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on gfx950.
+
+Small and medium problems are compared in full; the full-size workloads
+(8192^3 and the fused 4096 x 11008 x 4096) on sampled entries -- every output
+tile's four corners plus random positions -- in the launch configuration the
+bench times (the dispatcher's choice).  Integer inputs must match bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import parity
+import tg_inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tiled_dense_gemm_08_amd as tg  # noqa: E402  (fails loudly if libtg.so is missing)
+
+F16_NAN = 0x7E00
+
+
+def log(msg):
+    sys.stderr.write("[gpu] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def to_dev(bits_2d, rows, cols, ld, offset_elems=0):
+    """fp16 bits (rows x cols) -> device buffer with leading dimension ld and a
+    leading offset; returns (tensor, pointer to element (0,0))."""
+    n = offset_elems + ((rows - 1) * ld + cols if rows and cols else 0) + 8
+    host = np.full(n, F16_NAN, np.uint16)       # NaN padding must never be read
+    if rows and cols:
+        view = np.lib.stride_tricks.as_strided(host[offset_elems:], shape=(rows, cols),
+                                               strides=(ld * 2, 2))
+        view[...] = bits_2d
+    t = torch.from_numpy(host.view(np.int16)).cuda()
+    return t, t.data_ptr() + 2 * offset_elems
+
+
+def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=None,
+        a_off=0, b_off=0, c_off=0, what=""):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    log("%s M=%d N=%d K=%d lda=%d ldb=%d ldc=%d %s bias=%s config=%s offs=%d,%d,%d" % (
+        what, M, N, K, lda, ldb, ldc, c_dtype, bias is not None, config, a_off, b_off, c_off))
+    ta, pa = to_dev(A, M, K, lda, a_off)
+    tb, pb = to_dev(B, K, N, ldb, b_off)
+    esz = 2 if c_dtype == "f16" else 4
+    nc = c_off + ((M - 1) * ldc + N if M and N else 0) + 8
+    if c_dtype == "f16":
+        tc = torch.full((nc,), float("nan"), dtype=torch.float16, device="cuda")
+    else:
+        tc = torch.full((nc,), float("nan"), dtype=torch.float32, device="cuda")
+    pc = tc.data_ptr() + esz * c_off
+    pbias = None
+    if bias is not None:
+        tbias = torch.from_numpy(np.ascontiguousarray(bias, np.float32)).cuda()
+        pbias = tbias.data_ptr()
+    code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
+    s = torch.cuda.current_stream().cuda_stream
+    if config is not None:
+        st = tg.tg_gemm_with_config(config, pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
+    elif bias is not None:
+        st = tg.tg_gemm_bias_relu(pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
+    else:
+        st = tg.tg_gemm(pa, pb, pc, M, N, K, lda, ldb, ldc, code, s)
+    assert st == tg.TG_SUCCESS, tg.tg_status_string(st)
+    torch.cuda.synchronize()
+    host = tc.cpu().numpy()
+    if c_dtype == "f16":
+        host = host.view(np.uint16)
+    if not (M and N):
+        return np.zeros((M, N), host.dtype), host
+    out = np.lib.stride_tricks.as_strided(host[c_off:], shape=(M, N),
+                                          strides=(ldc * host.itemsize, host.itemsize)).copy()
+    return out, host
+
+
+def full_check(A, B, M, N, K, c_dtype, integer, bias=None, **kw):
+    out, _ = run(A, B, M, N, K, c_dtype, bias=bias, **kw)
+    cref = oracle.gemm_ref(A, B, M, N, K, bias=bias)
+    return parity.check(out, cref, K, c_dtype, integer, what=kw.get("what", ""))
+
+
+def supports(cid, M, N, K, lda, ldb, ldc, c_dtype, fused):
+    # the direct path's alignment checks only look at the pointers' low bits;
+    # torch allocations are 256-byte aligned
+    code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
+    return tg.tg_config_supports(cid, 1 << 20, 2 << 20, (3 << 20) if fused else None, 4 << 20,
+                                 M, N, K, lda, ldb, ldc, code) == 1
+
+
+# ------------------------------------------------------------ small shapes --
+SMALL = [(16, 16, 32), (64, 64, 64), (1, 8, 8), (200, 136, 96), (300, 520, 264), (17, 40, 48),
+         (256, 256, 256), (130, 260, 136)]
+ODD = [(3, 5, 7), (37, 45, 29), (129, 257, 65), (100, 70, 1031)]
+
+
+@pytest.mark.parametrize("cid", range(tg.tg_num_configs()))
+def test_small_shapes_every_config(cid):
+    name = tg.tg_config_info(cid)["name"]
+    n = 0
+    for (M, N, K) in SMALL + ODD:
+        for kind, c_dtype, fused in [("uniform", "f32", False), ("int", "f16", True),
+                                     ("normal_scaled", "f16", False), ("int", "f32", False)]:
+            if not supports(cid, M, N, K, K, N, N, c_dtype, fused):
+                continue
+            A, B = gen.operands(M, N, K, kind, 1000 + M + N + K)
+            bias = gen.bias_vector(N, 7, integer=(kind == "int")) if fused else None
+            full_check(A, B, M, N, K, c_dtype, kind == "int", bias=bias, config=cid,
+                       what="%s %s" % (name, kind))
+            n += 1
+    assert n > 0
+
+
+# --------------------------------------------------- the five workloads --
+def sample_positions(M, N, bm, bn, count, seed):
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    for m0 in range(0, M, bm):
+        for n0 in range(0, N, bn):
+            m1, n1 = min(M, m0 + bm) - 1, min(N, n0 + bn) - 1
+            rows += [m0, m0, m1, m1]
+            cols += [n0, n1, n0, n1]
+    rows += list(rng.integers(0, M, count))
+    cols += list(rng.integers(0, N, count))
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+@pytest.mark.parametrize("name", ["sq256", "sq1024", "ragged3001x5003x1031"])
+@pytest.mark.parametrize("integer", [False, True])
+def test_workload_full(name, integer):
+    w = gen.workload(name, integer=integer)
+    rep = full_check(w["A"], w["B"], w["M"], w["N"], w["K"], w["c_dtype"], integer,
+                     bias=w["bias"], what=name)
+    log("%s integer=%s %s" % (name, integer, rep))
+
+
+@pytest.mark.parametrize("name", ["sq8192", "fused4096x11008x4096"])
+@pytest.mark.parametrize("integer", [False, True])
+def test_workload_sampled(name, integer):
+    w = gen.workload(name, integer=integer)
+    M, N, K = w["M"], w["N"], w["K"]
+    out, _ = run(w["A"], w["B"], M, N, K, w["c_dtype"], bias=w["bias"], what=name)
+    code = tg.TG_DTYPE_F16 if w["c_dtype"] == "f16" else tg.TG_DTYPE_F32
+    cid = tg.tg_select_config(1 << 20, 2 << 20, (3 << 20) if w["bias"] is not None else None,
+                              4 << 20, M, N, K, K, N, N, code)
+    info = tg.tg_config_info(cid)
+    r, c = sample_positions(M, N, info["block_m"], info["block_n"], 6000, 17)
+    cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, K, N, bias=w["bias"])
+    rep = parity.check(out[r, c], cref, K, w["c_dtype"], integer, what=name)
+    vals = parity.gpu_values(out, w["c_dtype"])
+    assert not np.any(np.isnan(vals)), "unwritten (NaN) outputs"
+    if w["bias"] is not None:
+        assert np.all(vals >= 0)
+    log("%s integer=%s config=%s sampled=%d %s" % (name, integer, info["name"], r.size, rep))
+
+
+# ------------------------------------------------ cross-config equality --
+def test_all_configs_bit_identical_on_integer_inputs():
+    M, N, K = 300, 520, 264
+    A, B = gen.operands(M, N, K, "int", 55)
+    bias = gen.bias_vector(N, 56, integer=True)
+    for c_dtype in ("f32", "f16"):
+        outs = {}
+        for cid in range(tg.tg_num_configs()):
+            if supports(cid, M, N, K, K, N, N, c_dtype, True):
+                outs[cid], _ = run(A, B, M, N, K, c_dtype, bias=bias, config=cid, what="xcfg")
+        ids = sorted(outs)
+        assert len(ids) >= 2
+        for i in ids[1:]:
+            assert np.array_equal(outs[i], outs[ids[0]]), (i, ids[0])
+
+
+def test_repeated_runs_are_bitwise_identical():
+    w = gen.workload("sq1024")
+    a, _ = run(w["A"], w["B"], 1024, 1024, 1024, "f32", what="repeat1")
+    b, _ = run(w["A"], w["B"], 1024, 1024, 1024, "f32", what="repeat2")
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------- layouts and edge cases --
+@pytest.mark.parametrize("M,N,K", [(37, 45, 29), (300, 520, 264), (129, 257, 1031)])
+@pytest.mark.parametrize("offs", [(0, 0, 0), (1, 3, 1)])
+def test_padded_leading_dims_and_unaligned_bases(M, N, K, offs):
+    A, B = gen.operands(M, N, K, "uniform", 77)
+    bias = gen.bias_vector(N, 78)
+    for c_dtype in ("f32", "f16"):
+        full_check(A, B, M, N, K, c_dtype, False, bias=bias, lda=K + 3, ldb=N + 5, ldc=N + 7,
+                   a_off=offs[0], b_off=offs[1], c_off=offs[2], what="padded")
+    Ai, Bi = gen.operands(M, N, K, "int", 79)
+    full_check(Ai, Bi, M, N, K, "f16", True, lda=K + 8, ldb=N + 8, ldc=N + 4,
+               a_off=offs[0], b_off=offs[1], c_off=offs[2], what="padded-int")
+
+
+def test_K0_writes_zero_or_relu_bias():
+    M, N = 70, 90
+    A = np.zeros((M, 0), np.uint16)
+    B = np.zeros((0, N), np.uint16)
+    out, _ = run(A, B, M, N, 0, "f32", what="K0")
+    assert np.all(out == 0)
+    bias = gen.bias_vector(N, 5)
+    out, _ = run(A, B, M, N, 0, "f16", bias=bias, what="K0-bias")
+    want = oracle.output_typed(np.broadcast_to(np.maximum(bias.astype(np.float64), 0), (M, N)),
+                               "f16")
+    assert np.array_equal(np.where(out == 0x8000, 0, out), want)
+
+
+def test_M0_leaves_C_untouched():
+    A = np.zeros((0, 16), np.uint16)
+    B = np.zeros((16, 16), np.uint16)
+    _, host = run(A, B, 0, 16, 16, "f32", what="M0")
+    assert np.all(np.isnan(host))
+
+
+def test_host_pointer_is_rejected():
+    a = np.zeros(64 * 64, np.float16)
+    b = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    c = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
+    st = tg.tg_gemm(a.ctypes.data, b.data_ptr(), c.data_ptr(), 64, 64, 64, 64, 64, 64,
+                    tg.TG_DTYPE_F32, 0)
+    assert st == tg.TG_ERROR_NOT_DEVICE_MEMORY
+    st = tg.tg_gemm(b.data_ptr(), b.data_ptr(), c.data_ptr(), 64, 64, 64, 64, 64, 64,
+                    tg.TG_DTYPE_F32, 0)
+    assert st == tg.TG_SUCCESS
+    torch.cuda.synchronize()
+
+
+def test_torch_marshalling_wrapper():
+    w = gen.workload("sq256")
+    a = torch.from_numpy(w["A"].view(np.float16)).cuda()
+    b = torch.from_numpy(w["B"].view(np.float16)).cuda()
+    c = tg.gemm(a, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cref = oracle.gemm_ref(w["A"], w["B"], 256, 256, 256)
+    parity.check(c.cpu().numpy(), cref, 256, "f32", False, what="wrapper")

@@ -1,0 +1,183 @@
+"""Python binding of libtg.so, the gfx950 tiled fp16 GEMM (+ fused bias + ReLU).
+
+The functions named tg_* mirror the C ABI in include/tg.h one to one: they
+take raw device pointers (ints) and sizes and return the tg_status code.
+`gemm` and `gemm_bias_relu` marshal torch tensors (device memory and the
+current stream only) into those calls; every step of the computation runs in
+the library's HIP kernels.  The library must be built (see build.py); there
+is no fallback: importing this package fails if libtg.so is missing.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtg.so")
+
+TG_DTYPE_F16 = 1
+TG_DTYPE_F32 = 2
+
+TG_SUCCESS = 0
+TG_ERROR_INVALID_VALUE = 1
+TG_ERROR_NOT_DEVICE_MEMORY = 2
+TG_ERROR_UNSUPPORTED = 3
+TG_ERROR_LAUNCH = 4
+
+# every function declared in include/tg.h
+EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_status_string", "tg_num_configs",
+            "tg_config_info", "tg_config_supports", "tg_select_config",
+            "tg_gemm_with_config", "tg_version")
+
+
+class TgError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s" % (what, tg_status_string(status)))
+
+
+class ConfigDesc(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("waves_m", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("direct_lds", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtg.so is not built (%s); run "
+                          "`python -m tiled_dense_gemm_08_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    gemm_args = [I64, I64, I64, I64, I64, I64, I, P]
+    L.tg_gemm.argtypes = [P, P, P] + gemm_args
+    L.tg_gemm.restype = I
+    L.tg_gemm_bias_relu.argtypes = [P, P, P, P] + gemm_args
+    L.tg_gemm_bias_relu.restype = I
+    L.tg_gemm_with_config.argtypes = [I, P, P, P, P] + gemm_args
+    L.tg_gemm_with_config.restype = I
+    L.tg_status_string.argtypes = [I]
+    L.tg_status_string.restype = ctypes.c_char_p
+    L.tg_num_configs.argtypes = []
+    L.tg_num_configs.restype = I
+    L.tg_config_info.argtypes = [I, ctypes.POINTER(ConfigDesc)]
+    L.tg_config_info.restype = I
+    shape_args = [P, P, P, P, I64, I64, I64, I64, I64, I64, I]
+    L.tg_config_supports.argtypes = [I] + shape_args
+    L.tg_config_supports.restype = I
+    L.tg_select_config.argtypes = shape_args
+    L.tg_select_config.restype = I
+    L.tg_version.argtypes = []
+    L.tg_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------ raw C ABI --
+def tg_gemm(A, B, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
+    return lib.tg_gemm(A, B, C, M, N, K, lda, ldb, ldc, c_dtype, stream or None)
+
+
+def tg_gemm_bias_relu(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
+    return lib.tg_gemm_bias_relu(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream or None)
+
+
+def tg_gemm_with_config(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
+    return lib.tg_gemm_with_config(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                                   stream or None)
+
+
+def tg_status_string(status):
+    return lib.tg_status_string(status).decode()
+
+
+def tg_num_configs():
+    return lib.tg_num_configs()
+
+
+def tg_config_info(config_id):
+    d = ConfigDesc()
+    st = lib.tg_config_info(config_id, ctypes.byref(d))
+    if st != TG_SUCCESS:
+        raise TgError(st, "tg_config_info(%d)" % config_id)
+    return {f: (getattr(d, f).decode() if f == "name" else getattr(d, f)) for f, _ in d._fields_}
+
+
+def tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype):
+    return lib.tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+
+
+def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype):
+    return lib.tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+
+
+def tg_version():
+    return lib.tg_version().decode()
+
+
+def configs():
+    return [tg_config_info(i) for i in range(tg_num_configs())]
+
+
+# --------------------------------------------------- torch marshalling --
+def _dtype_code(t):
+    import torch
+    if t == torch.float16:
+        return TG_DTYPE_F16
+    if t == torch.float32:
+        return TG_DTYPE_F32
+    raise TypeError("output dtype must be float16 or float32, got %s" % t)
+
+
+def _matrix(t, name):
+    import torch
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.size(0) > 1 and t.stride(1) != 1 or t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major (unit column stride)" % name)
+    ld = t.stride(0) if t.size(0) > 1 else t.size(1)
+    return t.data_ptr(), max(ld, t.size(1))
+
+
+def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
+    """C = A.B (or max(A.B + bias, 0) when bias is given) with libtg.
+
+    a: (M, K) float16, b: (K, N) float16, both row-major on the current device;
+    out: optional preallocated (M, N) float16/float32 row-major tensor.
+    config: None (dispatcher's choice) or a configuration id.
+    """
+    import torch
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (M, N)))
+    pa, lda = _matrix(a, "A")
+    pb, ldb = _matrix(b, "B")
+    pc, ldc = _matrix(out, "C")
+    code = _dtype_code(out.dtype)
+    pbias = 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 1 or bias.numel() < N or bias.stride(0) != 1:
+            raise ValueError("bias must be a contiguous float32 vector of length N")
+        pbias = bias.data_ptr()
+    s = (stream if stream is not None else torch.cuda.current_stream(a.device)).cuda_stream
+    if config is not None:
+        st = tg_gemm_with_config(config, pa, pb, pbias or None, pc, M, N, K, lda, ldb, ldc,
+                                 code, s)
+    elif bias is not None:
+        st = tg_gemm_bias_relu(pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
+    else:
+        st = tg_gemm(pa, pb, pc, M, N, K, lda, ldb, ldc, code, s)
+    if st != TG_SUCCESS:
+        raise TgError(st, "tg_gemm")
+    return out
+
+
+def gemm_bias_relu(a, b, bias, out=None, out_dtype=None, config=None, stream=None):
+    return gemm(a, b, out=out, out_dtype=out_dtype, bias=bias, config=config, stream=stream)

@@ -1,0 +1,43 @@
+// tg_kernels.h — internal interface between the host dispatcher (tg_api.cpp)
+// and the gfx950 kernels (tg_kernels.hip).  Not installed, not part of the ABI.
+#ifndef TG_KERNELS_H
+#define TG_KERNELS_H
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace tg {
+
+// Kernel arguments.  Sizes are validated by the host to fit 32-bit ints; the
+// byte spans a_bytes / b_bytes are the buffer-descriptor ranges of A and B.
+struct Params {
+    const _Float16 *A;
+    const _Float16 *B;
+    const float *bias;
+    void *C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int tiles_m, tiles_n, group_m;
+    uint32_t a_bytes, b_bytes;
+    int vec_store;   // C rows allow 4-element vector stores (alignment)
+    int vec_bias;    // bias allows 16-byte loads
+    int a_vec, b_vec;  // staged path: rows allow 16-byte loads
+};
+
+typedef hipError_t (*LaunchFn)(const Params &p, bool f16_out, bool bias, hipStream_t s);
+
+struct KernelConfig {
+    int id;
+    int bm, bn, bk, stages, waves_m, waves_n;
+    int direct;       // 1: direct global->LDS path, 0: register-staged path
+    int lds_bytes;
+    const char *name;
+    LaunchFn launch;
+};
+
+extern const KernelConfig kConfigs[];
+extern const int kNumConfigs;
+
+}  // namespace tg
+
+#endif

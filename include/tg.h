@@ -90,6 +90,8 @@ typedef struct {
     int block_m, block_n, block_k;   /* workgroup output tile and K step */
     int stages;                      /* LDS ring depth of the K pipeline */
     int waves_m, waves_n;            /* wave64 grid inside the workgroup */
+    int mfma;                        /* MFMA block edge: 16 (v_mfma_f32_16x16x32_f16)
+                                        or 32 (v_mfma_f32_32x32x16_f16) */
     int direct_lds;                  /* 1: 16-byte global->LDS DMA loads (aligned
                                         operands only); 0: register-staged loads
                                         with per-element bounds (any alignment) */

@@ -40,7 +40,9 @@ def test_config_table_is_consistent():
     for i, c in enumerate(tg.configs()):
         assert c["id"] == i
         assert c["lds_bytes"] <= 160 * 1024
-        assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
+        assert c["mfma"] in (16, 32)
+        assert c["block_m"] % (c["mfma"] * c["waves_m"]) == 0
+        assert c["block_n"] % (c["mfma"] * c["waves_n"]) == 0
         assert c["name"] not in names
         names.add(c["name"])
     with pytest.raises(tg.TgError):

@@ -37,11 +37,19 @@ class TgError(RuntimeError):
 class ConfigDesc(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("waves_m", ctypes.c_int),
-                ("waves_n", ctypes.c_int), ("direct_lds", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("mfma", ctypes.c_int), ("direct_lds", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p)]
 
 
 def _load():
+    # The library must run on the same HIP runtime as the framework that owns
+    # the device memory.  PyTorch ships its own libamdhip64; importing it
+    # first makes libtg.so bind to that copy instead of loading a second
+    # runtime that would not know torch's allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError("libtg.so is not built (%s); run "
                           "`python -m tiled_dense_gemm_08_amd.build`" % LIB_PATH)

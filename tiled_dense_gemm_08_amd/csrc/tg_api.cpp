@@ -250,6 +250,7 @@ tg_status tg_config_info(int id, tg_config_desc *out)
     out->stages = c.stages;
     out->waves_m = c.waves_m;
     out->waves_n = c.waves_n;
+    out->mfma = c.mfma;
     out->direct_lds = c.direct;
     out->lds_bytes = c.lds_bytes;
     out->name = c.name;

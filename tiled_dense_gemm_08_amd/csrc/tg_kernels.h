@@ -29,6 +29,7 @@ typedef hipError_t (*LaunchFn)(const Params &p, bool f16_out, bool bias, hipStre
 struct KernelConfig {
     int id;
     int bm, bn, bk, stages, waves_m, waves_n;
+    int mfma;         // MFMA block edge: 16 (16x16x32) or 32 (32x32x16)
     int direct;       // 1: direct global->LDS path, 0: register-staged path
     int lds_bytes;
     const char *name;

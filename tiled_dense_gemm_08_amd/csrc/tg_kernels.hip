@@ -10,23 +10,24 @@
 // written for CDNA4 instead:
 //
 //  * workgroups of 64-lane waves; each wave owns a TM x TN slab of the output
-//    tile as 16x16 blocks of v_mfma_f32_16x16x32_f16 accumulators (4 fp32 per
-//    lane per block);
+//    tile as MI x MI blocks of MFMA accumulators, MI = 16
+//    (v_mfma_f32_16x16x32_f16, 4 fp32 per lane per block) or MI = 32
+//    (v_mfma_f32_32x32x16_f16, 16 fp32 per lane per block);
 //  * operands reach LDS either by 16-byte direct global->LDS DMA through
 //    buffer descriptors (bounds give zeros for free), or through registers
 //    with per-element bounds checks for operands of any alignment;
 //  * a ring of STAGES LDS buffers over the K loop, one workgroup barrier per
 //    K step, LDS-only fences so that prefetches stay in flight across it;
 //  * XOR swizzles on the 16-byte chunk index of each LDS row, chosen so that
-//    the fragment reads of a wave spread over all LDS banks (the pages use a
+//    the fragment reads of a wave spread over the LDS banks (the pages use a
 //    swizzle or row padding for the same purpose: pwwt.cn article, section
 //    3.3; codechina.net article, section 4.1);
 //  * A fragments come from ds_read_b128 on k-contiguous rows; B is row-major
 //    (n-contiguous), and its fragments come from ds_read_b64_tr_b16, the
 //    gfx950 LDS transpose read, so B is never transposed in memory;
 //  * the MFMA is issued with the operands swapped (B fragment as the first
-//    source) so that each lane ends with 4 consecutive columns of one output
-//    row: 16-byte fp32 or 8-byte fp16 stores and a 16-byte bias load;
+//    source) so that each lane ends with runs of 4 consecutive columns of one
+//    output row: 16-byte fp32 or 8-byte fp16 stores and a 16-byte bias load;
 //  * workgroup ids are remapped so that each of the 8 XCDs (each with its own
 //    L2) works on a contiguous, grouped band of output tiles.
 #include <hip/hip_runtime.h>
@@ -39,9 +40,8 @@ namespace tg {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
-typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
-typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
 #define TG_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -73,23 +73,26 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // ---------------------------------------------------------------- swizzles --
 // A tile in LDS: BM rows of BK fp16 (k contiguous), 16-byte chunks XOR-
-// swizzled by row.  A fragment read has 16 lanes on 16 consecutive rows at the
-// same logical chunk; the swizzle sends them to 16 distinct 16-byte slots of
-// any 256-byte window (and 8 consecutive rows to 8 slots of 128 bytes).
+// swizzled by row.  A fragment read has MI lanes on MI consecutive rows at
+// the same logical chunk.  With 128-byte rows, XOR by (row & 7) reads at the
+// full ds_read_b128 rate on gfx950 (measured: about 200 B/clk/CU, against
+// about 60 without a swizzle).  64-byte rows (BK = 32) use a 2-bit analogue.
+// Both are unchanged by row += 16, so one per-lane offset serves every block.
 template <int BK>
 __device__ __forceinline__ int swz_a(int row)
 {
     if constexpr (BK == 64)
-        return (row & 7) ^ ((row >> 3) & 1);
-    else  // BK == 32: 4 chunks per 64-byte row
-        return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+        return row & 7;
+    else
+        return (row >> 1) & 3;
 }
 
 // B tile in LDS: BK rows of BN fp16 (n contiguous).  A transpose read has, per
-// 16-lane group, 4 rows (k % 4 = 0..3) of 32 bytes, and the 4 groups sit on
-// rows 8 apart; the swizzle (multiples of 2 chunks, so the 32-byte pairs stay
-// whole) spreads rows {0..3, 8..11} over 8 distinct 32-byte slots.  It must
-// stay below the BN/8 chunks of a row, so 64-wide tiles use only the k % 4 part.
+// 16-lane group, 4 rows (k % 4 = 0..3) of 32 bytes, and groups sit on rows 8
+// apart; the swizzle (multiples of 2 chunks, so the 32-byte pairs stay whole)
+// spreads rows {0..3, 8..11} over 8 distinct 32-byte slots.  It must stay
+// below the BN/8 chunks of a row, so 64-wide tiles use only the k % 4 part.
+// It is unchanged by k += 4 and k += 16.
 template <int BN>
 __device__ __forceinline__ int swz_b(int k)
 {
@@ -101,7 +104,7 @@ __device__ __forceinline__ int swz_b(int k)
 
 // ------------------------------------------------------------- tile order --
 // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
-// contiguous range of logical tiles, then walk tiles in groups of GROUP_M
+// contiguous range of logical tiles, then walk tiles in groups of group_m
 // tile-rows so that concurrently running tiles share A rows and B columns.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_m,
                                             int &tm, int &tn)
@@ -121,16 +124,23 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_
 }
 
 // ---------------------------------------------------------------- configs --
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+template <int MI> struct AccT;
+template <> struct AccT<16> { typedef float4v type; };
+template <> struct AccT<32> { typedef float16v type; };
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WM_, WAVES_N = WN_;
     static constexpr int STAGES = STAGES_;
+    static constexpr int MI = MI_;                         // MFMA block edge
+    static constexpr int KI = 512 / MI;                    // k per MFMA: 32 or 16
+    static constexpr int ACC = MI * MI / 64;               // fp32 per lane per block
     static constexpr int WAVES = WM_ * WN_;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int TM = BM / WM_, TN = BN / WN_;     // wave tile
-    static constexpr int MT = TM / 16, NT = TN / 16;       // MFMA blocks per wave
-    static constexpr int KS = BK / 32;                     // MFMA k-steps per K step
+    static constexpr int MT = TM / MI, NT = TN / MI;       // MFMA blocks per wave
+    static constexpr int KS = BK / KI;                     // MFMA k-steps per K step
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -141,134 +151,156 @@ struct Cfg {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int A_ROWS_PER_LOAD = 1024 / (BK * 2);
     static constexpr int B_ROWS_PER_LOAD = 1024 / (BN * 2);
+    typedef typename AccT<MI>::type acc_t;
+    static_assert(MI == 16 || MI == 32, "MI");
     static_assert(BK == 32 || BK == 64, "BK");
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+    static_assert(TM % MI == 0 && TN % MI == 0, "wave tile");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "copy split");
     static_assert(BN * 2 <= 1024 && BN % 64 == 0, "BN");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// ------------------------------------------------------- fragment compute --
-// One K step out of LDS stage `as` (A) / `bs` (B): KS MFMA k-steps of 32.
-template <class C>
-__device__ __forceinline__ void compute_stage(const char *as, const char *bs,
-                                              const int (&a_off)[C::KS],
-                                              const int (&b_off)[C::NT],
-                                              float4v (&acc)[C::MT][C::NT])
-{
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ks++) {
-        half8 af[C::MT];
-        half8 bf[C::NT];
-#pragma unroll
-        for (int mt = 0; mt < C::MT; mt++)
-            af[mt] = *(const half8 *)(as + a_off[ks] + mt * 16 * C::BK * 2);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; nt++) {
-            const char *p = bs + b_off[nt] + ks * 32 * C::BN * 2;
-            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4v *)TG_LDS(p));
-            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4v *)TG_LDS(p + 4 * C::BN * 2));
-            bf[nt] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int mt = 0; mt < C::MT; mt++)
-#pragma unroll
-            for (int nt = 0; nt < C::NT; nt++)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[nt], af[mt],
-                                                                    acc[mt][nt], 0, 0, 0);
-    }
-}
-
-// ---------------------------------------------------------------- epilogue --
-// Lane l holds, for block (mt, nt), row (l % 16) and columns 4*(l/16) .. +3.
-template <class C, typename OutT, bool BIAS>
-__device__ __forceinline__ void epilogue(const Params &p, int m_base, int n_base,
-                                         float4v (&acc)[C::MT][C::NT])
-{
-    const int lane = threadIdx.x & 63;
-    const bool vec_ok = p.vec_store != 0;
-#pragma unroll
-    for (int nt = 0; nt < C::NT; nt++) {
-        const int col = n_base + nt * 16 + 4 * (lane >> 4);
-        float4v bv = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BIAS) {
-            if (p.vec_bias && col + 3 < p.N) {
-                bv = *(const float4v *)(p.bias + col);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    bv[r] = (col + r < p.N) ? p.bias[col + r] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < C::MT; mt++) {
-            const int row = m_base + mt * 16 + (lane & 15);
-            if (row >= p.M)
-                continue;
-            float4v v = acc[mt][nt];
-            if constexpr (BIAS) {
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    v[r] = fmaxf(v[r] + bv[r], 0.f);
-            }
-            OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
-            if (vec_ok && col + 3 < p.N) {
-                if constexpr (sizeof(OutT) == 4) {
-                    *(float4v *)dst = v;
-                } else {
-                    half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                    *(half4 *)dst = h;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if (col + r < p.N)
-                        dst[r] = (OutT)v[r];
-            }
-        }
-    }
-}
-
-// --------------------------------------------- per-lane LDS read offsets --
+// ------------------------------------------------------------- fragments --
+// Per-lane LDS byte offsets of the fragment reads (stage-relative).
+//  A (MFMA second source): lane l holds row l % MI, k = 8 (l / MI) .. +7 of
+//    the k-step: one ds_read_b128.  a_off[ks] + mt * MI * BK * 2 for block mt.
+//  B (MFMA first source): lane l holds column l % MI, the same 8 k.  Two
+//    transpose reads of 4 k each: lane L = 16 G + 4 e + q reads row
+//    k = 8 (L / MI) + e (+4 for the second read, + KI per k-step) at columns
+//    16 ((L % MI) / 16) + 4 q .. +3 of the block; the hardware hands lane
+//    16 G + j the 4 rows' column j.  b_off[nt] for block nt.
 template <class C>
 __device__ __forceinline__ void fragment_offsets(int wm, int wn, int (&a_off)[C::KS],
                                                  int (&b_off)[C::NT])
 {
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;     // 16-lane group: which 8 k of the 32
-    const int i = lane & 15;
+    const int kgroup = lane / C::MI;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ks++) {
-        const int row = wm * C::TM + i;                  // + mt * 16 (swizzle-neutral)
-        const int chunk = ks * 4 + g;
+        const int row = wm * C::TM + lane % C::MI;
+        const int chunk = ks * (C::KI / 8) + kgroup;
         a_off[ks] = row * C::BK * 2 + ((chunk ^ swz_a<C::BK>(row)) * 16);
     }
-    // transpose read: lane 16g + 4e + q supplies row k = 8g + e (+4 for the
-    // second read, + 32 per MFMA k-step), columns 4q .. 4q+3 of the 16-wide
-    // slice; the hardware hands lane 16g + j the column j of those 4 rows.
+    const int i = lane & 15;
     const int e = i >> 2, q = i & 3;
-    const int k = 8 * g + e;
+    const int k = 8 * kgroup + e;
+    const int sub = (lane % C::MI) >> 4;
 #pragma unroll
     for (int nt = 0; nt < C::NT; nt++) {
-        const int col = wn * C::TN + nt * 16 + 4 * q;
-        const int chunk = col >> 3;
-        b_off[nt] = k * C::BN * 2 + ((chunk ^ swz_b<C::BN>(k)) * 16) + (col & 7) * 2;
+        const int col = wn * C::TN + nt * C::MI + sub * 16 + 4 * q;
+        b_off[nt] = k * C::BN * 2 + (((col >> 3) ^ swz_b<C::BN>(k)) * 16) + (col & 7) * 2;
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void read_frags(const char *as, const char *bs, int ks,
+                                           const int (&a_off)[C::KS], const int (&b_off)[C::NT],
+                                           half8 (&fa)[C::MT], half8 (&fb)[C::NT])
+{
+#pragma unroll
+    for (int nt = 0; nt < C::NT; nt++) {
+        const char *q = bs + b_off[nt] + ks * C::KI * C::BN * 2;
+        short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v *)TG_LDS(q));
+        short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * C::BN * 2));
+        fb[nt] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++)
+        fa[mt] = *(const half8 *)(as + a_off[ks] + mt * C::MI * C::BK * 2);
+}
+
+template <class C>
+__device__ __forceinline__ typename C::acc_t mfma(half8 b, half8 a, typename C::acc_t c)
+{
+    if constexpr (C::MI == 16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+}
+
+template <class C, int LO, int HI>
+__device__ __forceinline__ void mfma_range(const half8 (&fa)[C::MT], const half8 (&fb)[C::NT],
+                                           typename C::acc_t (&acc)[C::MT][C::NT])
+{
+#pragma unroll
+    for (int i = LO; i < HI; i++) {
+        const int mt = i / C::NT, nt = i % C::NT;
+        acc[mt][nt] = mfma<C>(fb[nt], fa[mt], acc[mt][nt]);
+    }
+}
+
+// ---------------------------------------------------------------- epilogue --
+// After the operand swap, lane l holds for block (mt, nt) row l % MI of the
+// block and, for each run r4 < ACC / 4, the 4 consecutive columns
+// 8 r4 + 4 (l / 32) .. +3 (MI = 32) or 4 (l / 16) .. +3 (MI = 16).
+template <class C, typename OutT, bool BIAS>
+__device__ __forceinline__ void epilogue(const Params &p, int m_base, int n_base,
+                                         typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    const int lane = threadIdx.x & 63;
+    const bool vec_ok = p.vec_store != 0;
+    constexpr int RUNS = C::ACC / 4;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; nt++) {
+#pragma unroll
+        for (int run = 0; run < RUNS; run++) {
+            const int col = n_base + nt * C::MI + 8 * run + 4 * (lane / C::MI);
+            float4v bv = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BIAS) {
+                if (p.vec_bias && col + 3 < p.N) {
+                    bv = *(const float4v *)(p.bias + col);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        bv[r] = (col + r < p.N) ? p.bias[col + r] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < C::MT; mt++) {
+                const int row = m_base + mt * C::MI + lane % C::MI;
+                if (row >= p.M)
+                    continue;
+                float4v v;
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    v[r] = acc[mt][nt][4 * run + r];
+                if constexpr (BIAS) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        v[r] = fmaxf(v[r] + bv[r], 0.f);
+                }
+                OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
+                if (vec_ok && col + 3 < p.N) {
+                    if constexpr (sizeof(OutT) == 4) {
+                        *(float4v *)dst = v;
+                    } else {
+                        half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(half4 *)dst = h;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        if (col + r < p.N)
+                            dst[r] = (OutT)v[r];
+                }
+            }
+        }
     }
 }
 
 // ============================================================================
-// Direct path: 16-byte global->LDS DMA.  Requires 16-byte aligned A and B,
+// Direct copies: 16-byte global->LDS DMA.  Requires 16-byte aligned A and B,
 // lda % 8 == 0, ldb % 8 == 0, K % 8 == 0 and N % 8 == 0 so that every 16-byte
 // chunk is either entirely inside the matrix or entirely outside it.
 // ============================================================================
-// 16-byte global->LDS DMA: lane i's 16 bytes from buffer offset `voff` land
-// at LDS address `lds` + 16 i.  Written as inline assembly so that the
-// compiler does not treat every later LDS read as dependent on the copy (it
-// would wait for all outstanding copies before each one); the kernel waits on
-// vmcnt itself, before the barrier that publishes a stage.  M0 is written here
-// and nowhere else in these kernels.
+// Lane i's 16 bytes from buffer offset `voff` land at LDS address lds + 16 i.
+// Written as inline assembly so that the compiler does not treat every later
+// LDS read as dependent on the copy (it would wait for all outstanding copies
+// before each one); the kernels wait on vmcnt themselves, before the barrier
+// that publishes a stage.  M0 is written here and nowhere else in these
+// kernels (the build checks the device assembly for that).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -282,70 +314,145 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
 }
 
+// Wave w's copy instruction t of a K step fills LDS bytes [1 KiB * (w *
+// LOADS + t), +1 KiB) of the A (or B) tile: A_ROWS_PER_LOAD rows of the A tile
+// (lane -> row lane / (BK/8), physical chunk lane % (BK/8)), or
+// B_ROWS_PER_LOAD k-rows of the B tile.  The swizzle is applied on the global
+// side: each lane fetches the logical chunk that belongs at its physical slot.
+// Only lane constants are kept in registers; per-instruction offsets are
+// recomputed at issue.
 template <class C>
 struct DirectLoader {
     __amdgpu_buffer_rsrc_t ra, rb;
-    uint32_t a_base[C::A_LOADS];   // byte offset at k0 = 0, or kOOB
-    uint32_t b_base[C::B_LOADS];
-    int a_kchunk[C::A_LOADS];      // logical k-chunk of this lane's A load
-    int b_krow[C::B_LOADS];        // k row (within the tile) of this lane's B load
-    uint32_t a_step, b_step;       // bytes per K step
+    uint32_t a_lane;   // byte offset of this lane's A chunk in instruction 0 at k0 = 0
+    int a_row, a_kc;   // row within an instruction; logical k chunk
+    int b_row, b_phys; // k-row within an instruction; physical chunk
 
-    __device__ __forceinline__ void init(const Params &p, int m0, int n0)
+    __device__ __forceinline__ void init(const Params &p, int m0)
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63;
         ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, 0, p.a_bytes, kRsrcWord3);
         rb = __builtin_amdgcn_make_buffer_rsrc((void *)p.B, 0, p.b_bytes, kRsrcWord3);
+        a_row = lane / (C::BK / 8);
+        // the A swizzle depends on row % A_ROWS_PER_LOAD only (8 or 16 rows)
+        a_kc = (lane % (C::BK / 8)) ^ swz_a<C::BK>(a_row);
+        a_lane = (uint32_t)(((int64_t)(m0 + a_row) * p.lda + a_kc * 8) * 2);
+        b_row = lane / (C::BN / 8);
+        b_phys = lane % (C::BN / 8);
+    }
+
+    // Issue the copies of K step kt into LDS stage base `dst`.  Steps at or
+    // beyond nk are issued as dummies whose every lane reads out of range
+    // (zeros, no memory traffic), so that every K step has the same number
+    // of outstanding copies.
+    __device__ __forceinline__ void issue(const Params &p, int kt, char *dst, int nk, int m0,
+                                          int n0)
+    {
+        const int wave = threadIdx.x >> 6;
+        const uint32_t dst_lds = lds_addr(dst);
+        const bool valid = kt < nk;
+        const int k0 = kt * C::BK;
+        const bool tail = kt == nk - 1 && (p.K % C::BK) != 0;
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++) {
             const int inst = wave * C::A_LOADS + t;
-            const int row = inst * C::A_ROWS_PER_LOAD + lane / (C::BK / 8);
-            const int phys = lane % (C::BK / 8);
-            const int chunk = phys ^ swz_a<C::BK>(row);
-            a_kchunk[t] = chunk;
-            const int gm = m0 + row;
-            a_base[t] = (gm < p.M) ? (uint32_t)(((int64_t)gm * p.lda + chunk * 8) * 2) : kOOB;
+            const int row0 = inst * C::A_ROWS_PER_LOAD;
+            const uint32_t off = a_lane + (uint32_t)(row0 * p.lda * 2) + (uint32_t)(k0 * 2);
+            const bool ok = valid & (a_row < p.M - m0 - row0) & (!tail | (k0 + a_kc * 8 < p.K));
+            dma16(ra, off | ((uint32_t)!ok * kOOB),
+                  __builtin_amdgcn_readfirstlane(dst_lds + inst * 1024));
         }
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++) {
             const int inst = wave * C::B_LOADS + t;
-            const int k = inst * C::B_ROWS_PER_LOAD + lane / (C::BN / 8);
-            const int phys = lane % (C::BN / 8);
-            const int chunk = phys ^ swz_b<C::BN>(k);
-            b_krow[t] = k;
-            const int gn = n0 + chunk * 8;
-            b_base[t] = (gn < p.N) ? (uint32_t)(((int64_t)k * p.ldb + gn) * 2) : kOOB;
-        }
-        a_step = C::BK * 2;
-        b_step = (uint32_t)(C::BK * p.ldb * 2);
-    }
-
-    // Issue the copies of K step kt into LDS stage base `dst`.
-    __device__ __forceinline__ void issue(const Params &p, int kt, char *dst, bool tail)
-    {
-        const int wave = threadIdx.x >> 6;
-        const uint32_t dst_lds = lds_addr(dst);
-        const int k0 = kt * C::BK;
-#pragma unroll
-        for (int t = 0; t < C::A_LOADS; t++) {
-            uint32_t off = a_base[t] + (uint32_t)kt * a_step;
-            if (tail && k0 + a_kchunk[t] * 8 >= p.K)
-                off = kOOB;
-            dma16(ra, off, __builtin_amdgcn_readfirstlane(dst_lds + (wave * C::A_LOADS + t) * 1024));
-        }
-#pragma unroll
-        for (int t = 0; t < C::B_LOADS; t++) {
-            uint32_t off = b_base[t] + (uint32_t)kt * b_step;
-            if (tail && k0 + b_krow[t] >= p.K)
-                off = kOOB;
-            dma16(rb, off,
-                  __builtin_amdgcn_readfirstlane(dst_lds + C::A_BYTES + (wave * C::B_LOADS + t) * 1024));
+            const int k = inst * C::B_ROWS_PER_LOAD + b_row;
+            const int col = n0 + (b_phys ^ swz_b<C::BN>(k)) * 8;
+            const uint32_t off = (uint32_t)(((int64_t)(k0 + k) * p.ldb + col) * 2);
+            const bool ok = valid & (col < p.N) & (!tail | (k0 + k < p.K));
+            dma16(rb, off | ((uint32_t)!ok * kOOB),
+                  __builtin_amdgcn_readfirstlane(dst_lds + C::A_BYTES + inst * 1024));
         }
     }
 };
 
+// ============================================================================
+// Pipelined direct kernel.  The K loop is software-pipelined at MFMA k-step
+// granularity:
+//  * fragments are double-buffered in registers: while the MFMAs of k-step u
+//    run, the LDS reads for k-step u+1 are in flight;
+//  * the workgroup barrier that publishes K step kt+1 sits in the middle of
+//    the last k-step of K step kt: half of its MFMAs are issued before the
+//    barrier and half after, covering the barrier and the first fragment
+//    reads of step kt+1;
+//  * right after that barrier the copy of step kt+STAGES is issued into the
+//    stage that step kt just vacated, so STAGES-1 K steps of compute cover
+//    each copy's latency; copies past the end are zero-reading dummies, which
+//    keeps the outstanding-copy count (and so the vmcnt wait) constant.
+// ============================================================================
+template <int N, int R>
+__device__ __forceinline__ void sched_interleave_reads()
+{
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, R, 0);   // then R MFMAs
+        sched_interleave_reads<N - 1, R>();
+    }
+}
+
+template <class C, int P, bool LAST_IN_STEP, bool HAS_NEXT>
+__device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld, char *smem,
+                                           int kt, int ks, int nk, int m0, int n0,
+                                           const int (&a_off)[C::KS], const int (&b_off)[C::NT],
+                                           half8 (&fa)[2][C::MT], half8 (&fb)[2][C::NT],
+                                           typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    constexpr int NMF = C::MT * C::NT;
+    constexpr int NRD = C::MT + 2 * C::NT;
+    constexpr int H = NMF / 2;
+    constexpr int R = H / NRD > 0 ? H / NRD : 1;
+    if constexpr (!LAST_IN_STEP) {
+        // next k-step of the same K step: prefetch its fragments
+        const char *as = smem + (kt % C::STAGES) * C::STAGE_BYTES;
+        read_frags<C>(as, as + C::A_BYTES, ks + 1, a_off, b_off, fa[1 - P], fb[1 - P]);
+        mfma_range<C, 0, NMF>(fa[P], fb[P], acc);
+        sched_interleave_reads<NRD, R>();
+    } else if constexpr (HAS_NEXT) {
+        mfma_range<C, 0, H>(fa[P], fb[P], acc);
+        wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of step kt+1 landed
+        lds_barrier();                               // everyone's did; step kt is free
+        const char *as = smem + ((kt + 1) % C::STAGES) * C::STAGE_BYTES;
+        read_frags<C>(as, as + C::A_BYTES, 0, a_off, b_off, fa[1 - P], fb[1 - P]);
+        ld.issue(p, kt + C::STAGES, smem + (kt % C::STAGES) * C::STAGE_BYTES, nk, m0, n0);
+        mfma_range<C, H, NMF>(fa[P], fb[P], acc);
+        sched_interleave_reads<NRD, R>();
+    } else {
+        mfma_range<C, 0, NMF>(fa[P], fb[P], acc);
+    }
+}
+
+// One loop unit: UNIT = max(2, KS) consecutive k-steps starting at u0 (a
+// multiple of UNIT), so register-buffer parity and position inside the K
+// step are compile-time constants.  HAS_NEXT = false for the final unit.
+template <class C, bool HAS_NEXT, int J = 0>
+__device__ __forceinline__ void pipe_unit(const Params &p, DirectLoader<C> &ld, char *smem, int u0,
+                                          int nk, int m0, int n0, const int (&a_off)[C::KS],
+                                          const int (&b_off)[C::NT], half8 (&fa)[2][C::MT],
+                                          half8 (&fb)[2][C::NT],
+                                          typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    constexpr int UNIT = C::KS > 2 ? C::KS : 2;
+    if constexpr (J < UNIT) {
+        constexpr int ks = J % C::KS;
+        constexpr bool last = ks == C::KS - 1;
+        const int kt = u0 / C::KS + J / C::KS;
+        pipe_kstep<C, J % 2, last, (J + 1 < UNIT) || HAS_NEXT>(p, ld, smem, kt, ks, nk, m0, n0,
+                                                               a_off, b_off, fa, fb, acc);
+        pipe_unit<C, HAS_NEXT, J + 1>(p, ld, smem, u0, nk, m0, n0, a_off, b_off, fa, fb, acc);
+    }
+}
+
 template <class C, typename OutT, bool BIAS>
-__global__ void __launch_bounds__(C::THREADS, 1) gemm_direct(Params p)
+__global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     int tm, tn;
@@ -354,46 +461,44 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_direct(Params p)
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    float4v acc[C::MT][C::NT];
+    typename C::acc_t acc[C::MT][C::NT];
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
         for (int j = 0; j < C::NT; j++)
-            acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+            acc[i][j] = typename C::acc_t{};
 
-    int a_off[C::KS], b_off[C::NT];
-    fragment_offsets<C>(wm, wn, a_off, b_off);
-
-    DirectLoader<C> ld;
-    ld.init(p, m0, n0);
     const int nk = (p.K + C::BK - 1) / C::BK;
-    const bool ragged_k = (p.K % C::BK) != 0;
-
+    if (nk > 0) {
+        int a_off[C::KS], b_off[C::NT];
+        fragment_offsets<C>(wm, wn, a_off, b_off);
+        DirectLoader<C> ld;
+        ld.init(p, m0);
 #pragma unroll
-    for (int s = 0; s < C::STAGES - 1; s++)
-        if (s < nk)
-            ld.issue(p, s, smem + s * C::STAGE_BYTES, ragged_k && s == nk - 1);
+        for (int s = 0; s < C::STAGES; s++)
+            ld.issue(p, s, smem + s * C::STAGE_BYTES, nk, m0, n0);
+        wait_vmcnt<(C::STAGES - 1) * C::LOADS>();
+        lds_barrier();
+        half8 fa[2][C::MT], fb[2][C::NT];
+        read_frags<C>(smem, smem + C::A_BYTES, 0, a_off, b_off, fa[0], fb[0]);
 
-    for (int kt = 0; kt < nk; kt++) {
-        // this lane's copies of step kt are done once at most the copies of
-        // the STAGES-2 later steps are still outstanding
-        if (kt + C::STAGES - 2 < nk)
-            wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier();   // everyone's copies of step kt landed; stage (kt-1) is free
-        const int kn = kt + C::STAGES - 1;
-        if (kn < nk)
-            ld.issue(p, kn, smem + (kn % C::STAGES) * C::STAGE_BYTES, ragged_k && kn == nk - 1);
-        const char *as = smem + (kt % C::STAGES) * C::STAGE_BYTES;
-        compute_stage<C>(as, as + C::A_BYTES, a_off, b_off, acc);
+        // MFMA k-steps 0 .. nsub-1 in units of UNIT; with KS = 1 an odd K-step
+        // count is padded by one all-zero K step (its copies read out of range)
+        constexpr int UNIT = C::KS > 2 ? C::KS : 2;
+        const int nsub = (C::KS == 1) ? ((nk + 1) & ~1) : nk * C::KS;
+        for (int u = 0; u + UNIT < nsub; u += UNIT)
+            pipe_unit<C, true>(p, ld, smem, u, nk, m0, n0, a_off, b_off, fa, fb, acc);
+        pipe_unit<C, false>(p, ld, smem, nsub - UNIT, nk, m0, n0, a_off, b_off, fa, fb, acc);
+        // drain the dummy copies before the workgroup exits
+        wait_vmcnt<0>();
     }
     epilogue<C, OutT, BIAS>(p, m0 + wm * C::TM, n0 + wn * C::TN, acc);
 }
 
 // ============================================================================
 // General path: register-staged copies with per-element bounds; any pointer
-// alignment (2-byte) and any leading dimensions.  Same LDS layout and compute.
+// alignment (2-byte) and any leading dimensions.  Same LDS layout and
+// fragment reads, two LDS stages.
 // ============================================================================
 template <class C>
 struct StagedLoader {
@@ -478,12 +583,12 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    float4v acc[C::MT][C::NT];
+    typename C::acc_t acc[C::MT][C::NT];
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
         for (int j = 0; j < C::NT; j++)
-            acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+            acc[i][j] = typename C::acc_t{};
 
     int a_off[C::KS], b_off[C::NT];
     fragment_offsets<C>(wm, wn, a_off, b_off);
@@ -499,7 +604,12 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
         if (kt + 1 < nk)
             ld.load(p, m0, n0, kt + 1);
         const char *as = smem + (kt & 1) * C::STAGE_BYTES;
-        compute_stage<C>(as, as + C::A_BYTES, a_off, b_off, acc);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ks++) {
+            half8 fa[C::MT], fb[C::NT];
+            read_frags<C>(as, as + C::A_BYTES, ks, a_off, b_off, fa, fb);
+            mfma_range<C, 0, C::MT * C::NT>(fa, fb, acc);
+        }
         if (kt + 1 < nk)
             ld.store(smem + ((kt + 1) & 1) * C::STAGE_BYTES);
         lds_barrier();
@@ -508,7 +618,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
 }
 
 // ------------------------------------------------------------ instances --
-template <class C, bool DIRECT>
+template <class C, int KIND>
 hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 {
     const dim3 grid(p.tiles_m * p.tiles_n), block(C::THREADS);
@@ -517,9 +627,9 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
         hipLaunchKernelGGL((KERNEL<C, OUT, B>), grid, block, 0, s, p);               \
         return hipGetLastError();                                                    \
     } while (0)
-    if constexpr (DIRECT) {
-        if (f16_out) { if (bias) TG_GO(gemm_direct, _Float16, true); else TG_GO(gemm_direct, _Float16, false); }
-        else { if (bias) TG_GO(gemm_direct, float, true); else TG_GO(gemm_direct, float, false); }
+    if constexpr (KIND == 2) {
+        if (f16_out) { if (bias) TG_GO(gemm_pipe, _Float16, true); else TG_GO(gemm_pipe, _Float16, false); }
+        else { if (bias) TG_GO(gemm_pipe, float, true); else TG_GO(gemm_pipe, float, false); }
     } else {
         if (f16_out) { if (bias) TG_GO(gemm_staged, _Float16, true); else TG_GO(gemm_staged, _Float16, false); }
         else { if (bias) TG_GO(gemm_staged, float, true); else TG_GO(gemm_staged, float, false); }
@@ -528,8 +638,8 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 }
 
 // Explicit instantiation: both compile passes see every kernel instance.
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, DIRECT)                            \
-    template hipError_t launch_cfg<Cfg<BM, BN, BK, WM, WN, ST>, DIRECT>(             \
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
+    template hipError_t launch_cfg<Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>(           \
         const Params &, bool, bool, hipStream_t);
 #include "tg_config_list.inc"
 #undef TG_CONFIG_ROW
@@ -537,16 +647,18 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 // The launch table is host data (the device pass would otherwise turn the
 // const array into device constant memory).
 #if !defined(__HIP_DEVICE_COMPILE__)
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, DIRECT)                            \
-    {ID, BM, BN, BK, ST, WM, WN, DIRECT, Cfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES,       \
-     (DIRECT ? "direct_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN                \
-             : "staged_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN),             \
-     &launch_cfg<Cfg<BM, BN, BK, WM, WN, ST>, DIRECT>},
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
+    {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
+     Cfg<BM, BN, BK, WM, WN, ST, MI>::LDS_BYTES,                                     \
+     (KIND == 2 ? "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI    \
+                : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI),         \
+     &launch_cfg<Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>},
 
 const KernelConfig kConfigs[] = {
 #include "tg_config_list.inc"
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+#undef TG_CONFIG_ROW
 #endif
 
 }  // namespace tg

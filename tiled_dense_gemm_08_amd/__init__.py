@@ -52,7 +52,7 @@ def _load():
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError("libtg.so is not built (%s); run "
-                          "`python -m tiled_dense_gemm_08_amd.build`" % LIB_PATH)
+                          "`python tiled_dense_gemm_08_amd/build.py`" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     gemm_args = [I64, I64, I64, I64, I64, I64, I, P]

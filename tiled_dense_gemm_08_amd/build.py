@@ -1,8 +1,10 @@
 """Build libtg.so for gfx950 in-tree with hipcc.
 
-    python -m tiled_dense_gemm_08_amd.build          # library
-    python -m tiled_dense_gemm_08_amd.build --asm    # also write the device asm
+    python tiled_dense_gemm_08_amd/build.py          # library
+    python tiled_dense_gemm_08_amd/build.py --asm    # also write the device asm
                                                      # and print register use
+
+(run by path: importing the package itself needs the built library)
 
 The device assembly is also checked for M0: the direct-load kernels write M0
 from inline assembly right before each global->LDS copy, so no other

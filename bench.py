@@ -32,10 +32,24 @@ import tg_inputs as gen  # noqa: E402
 PEAK_CUS, PEAK_GHZ, FLOP_PER_CLK_CU = 256, 2.4, 4096
 PEAK_TFLOPS = PEAK_CUS * PEAK_GHZ * FLOP_PER_CLK_CU / 1e3
 
-# HBM traffic of the dominant kernel from rocprofv3 PMC runs (FETCH_SIZE and
-# WRITE_SIZE per dispatch, KiB, scaled by the copy-kernel calibration factor).
-# None until measured for the current kernel.
+# Memory-side traffic of the dominant kernel per launch, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (--copy-calibration 1024: FETCH_SIZE reads 0.5 GiB, WRITE_SIZE 1 GiB, so the
+# factors are 2.0 and 1.0).  Keyed by workload, kernel configuration and a
+# digest of the kernel sources: a kernel changed since the counters were
+# taken reports null.
 TRAFFIC_BYTES = {}
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_gemm_08_amd", "csrc")
+    for name in ("tg_kernels.hip", "tg_kernels.h", "tg_config_list.inc"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -48,7 +62,25 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--samples", type=int, default=2048, help="parity-gate sample size")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (the "
+                         "known-size reference for scaling the HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """Plain copies of a known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    they give the factor between the counters and the bytes actually moved."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": 3}))
+    return 0
 
 
 def main():
@@ -57,6 +89,8 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         return 2
+    if a.copy_calibration:
+        return copy_calibration(a.copy_calibration)
     import torch
 
     import oracle
@@ -143,7 +177,7 @@ def main():
                "sample": "first %d of %d rows of C (%dx%dx%d fp64 dot products), %.1f s"
                          % (rows, M, rows, N, K, dt)}
 
-    traffic = TRAFFIC_BYTES.get((a.workload, info["name"]))
+    traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest()))
     line = {
         "metric": "GEMM TFLOP/s and % of MI355X fp16 MFMA peak at 8192^3; fused bias+ReLU",
         "value": round(value, 2),

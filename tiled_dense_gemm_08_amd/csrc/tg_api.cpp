@@ -183,6 +183,7 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     k.b_bytes = (uint32_t)(b_span < kMaxSpan ? b_span : 0);
     const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
     k.vec_store = (p.ldc % 4 == 0) && aligned(p.C, 4 * c_elem);
+    k.line_store = ((p.ldc * c_elem) % 16 == 0) && aligned(p.C, 16);
     k.vec_bias = p.fused && aligned(p.bias, 16);
     k.a_vec = (p.lda % 8 == 0) && aligned(p.A, 16);
     k.b_vec = (p.ldb % 8 == 0) && aligned(p.B, 16);

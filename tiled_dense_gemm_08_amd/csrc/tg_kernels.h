@@ -20,6 +20,7 @@ struct Params {
     int tiles_m, tiles_n, group_m;
     uint32_t a_bytes, b_bytes;
     int vec_store;   // C rows allow 4-element vector stores (alignment)
+    int line_store;  // C rows allow 16-byte stores: staged, full-line epilogue
     int vec_bias;    // bias allows 16-byte loads
     int a_vec, b_vec;  // staged path: rows allow 16-byte loads
 };

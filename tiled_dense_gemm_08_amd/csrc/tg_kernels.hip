@@ -235,9 +235,47 @@ __device__ __forceinline__ void mfma_range(const half8 (&fa)[C::MT], const half8
 // After the operand swap, lane l holds for block (mt, nt) row l % MI of the
 // block and, for each run r4 < ACC / 4, the 4 consecutive columns
 // 8 r4 + 4 (l / 32) .. +3 (MI = 32) or 4 (l / 16) .. +3 (MI = 16).
+template <class C>
+__device__ __forceinline__ int run_col(int nt, int run)
+{
+    const int lane = threadIdx.x & 63;
+    return nt * C::MI + 8 * run + 4 * (lane / C::MI);
+}
+
+// Bias for 4 consecutive columns starting at col (zeros past N).
+__device__ __forceinline__ float4v load_bias4(const Params &p, int col)
+{
+    float4v bv = {0.f, 0.f, 0.f, 0.f};
+    if (p.vec_bias && col + 3 < p.N) {
+        bv = *(const float4v *)(p.bias + col);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            bv[r] = (col + r < p.N) ? p.bias[col + r] : 0.f;
+    }
+    return bv;
+}
+
+template <class C, bool BIAS>
+__device__ __forceinline__ float4v epi_value(const typename C::acc_t &a, int run, float4v bv)
+{
+    float4v v;
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        v[r] = a[4 * run + r];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            v[r] = fmaxf(v[r] + bv[r], 0.f);
+    }
+    return v;
+}
+
+// Direct epilogue: each lane stores its 4-column runs straight to C.  Used when
+// C's rows do not allow 16-byte stores (unaligned base or leading dimension).
 template <class C, typename OutT, bool BIAS>
-__device__ __forceinline__ void epilogue(const Params &p, int m_base, int n_base,
-                                         typename C::acc_t (&acc)[C::MT][C::NT])
+__device__ __forceinline__ void epilogue_direct(const Params &p, int m_base, int n_base,
+                                                typename C::acc_t (&acc)[C::MT][C::NT])
 {
     const int lane = threadIdx.x & 63;
     const bool vec_ok = p.vec_store != 0;
@@ -246,31 +284,16 @@ __device__ __forceinline__ void epilogue(const Params &p, int m_base, int n_base
     for (int nt = 0; nt < C::NT; nt++) {
 #pragma unroll
         for (int run = 0; run < RUNS; run++) {
-            const int col = n_base + nt * C::MI + 8 * run + 4 * (lane / C::MI);
+            const int col = n_base + run_col<C>(nt, run);
             float4v bv = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS) {
-                if (p.vec_bias && col + 3 < p.N) {
-                    bv = *(const float4v *)(p.bias + col);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        bv[r] = (col + r < p.N) ? p.bias[col + r] : 0.f;
-                }
-            }
+            if constexpr (BIAS)
+                bv = load_bias4(p, col);
 #pragma unroll
             for (int mt = 0; mt < C::MT; mt++) {
                 const int row = m_base + mt * C::MI + lane % C::MI;
                 if (row >= p.M)
                     continue;
-                float4v v;
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    v[r] = acc[mt][nt][4 * run + r];
-                if constexpr (BIAS) {
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        v[r] = fmaxf(v[r] + bv[r], 0.f);
-                }
+                const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
                 OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
                 if (vec_ok && col + 3 < p.N) {
                     if constexpr (sizeof(OutT) == 4) {
@@ -288,6 +311,105 @@ __device__ __forceinline__ void epilogue(const Params &p, int m_base, int n_base
             }
         }
     }
+}
+
+// Largest power-of-two fraction of the wave tile's rows that fits the budget.
+constexpr int pass_rows(int tm, int fit)
+{
+    int r = tm;
+    while (r > fit && r > 1)
+        r /= 2;
+    return r;
+}
+
+// Staged epilogue: the wave writes its converted tile, PR rows at a time, into
+// a private LDS region in row-major order (rows padded by 16 bytes so that the
+// 32 rows one MFMA block spans spread over the banks), then reads it back so
+// that consecutive lanes hold consecutive 16-byte chunks of a row, and stores
+// those: every store instruction writes whole 128-byte lines of C instead of
+// 16 bytes in each of 32 rows.  The caller has made the workgroup's LDS free
+// (no copy in flight, every wave past its last fragment read).
+template <class C, typename OutT, bool BIAS>
+__device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_base, int n_base,
+                                             typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    constexpr int ES = sizeof(OutT);
+    constexpr int ROWB = C::TN * ES + 16;                  // padded LDS row
+    constexpr int REGION = (C::LDS_BYTES / C::WAVES) & ~15;
+    constexpr int PR = pass_rows(C::TM, REGION / ROWB);   // rows per pass
+    static_assert(PR >= C::MI && C::TM % PR == 0, "epilogue staging region");
+    constexpr int CPR = C::TN * ES / 16;                   // 16-byte chunks per row
+    static_assert((PR * CPR) % 64 == 0, "whole read-back instructions");
+    constexpr int RUNS = C::ACC / 4;
+    constexpr int MT_PASS = PR / C::MI;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char *region = smem + wave * REGION;
+
+    float4v bias_run[C::NT][RUNS];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; nt++)
+#pragma unroll
+        for (int run = 0; run < RUNS; run++) {
+            bias_run[nt][run] = float4v{0.f, 0.f, 0.f, 0.f};
+            if constexpr (BIAS)
+                bias_run[nt][run] = load_bias4(p, n_base + run_col<C>(nt, run));
+        }
+
+#pragma unroll
+    for (int pass = 0; pass < C::TM / PR; pass++) {
+        // registers -> LDS (row-major, padded rows)
+#pragma unroll
+        for (int i = 0; i < MT_PASS; i++) {
+            const int mt = pass * MT_PASS + i;
+            const int row = i * C::MI + lane % C::MI;
+#pragma unroll
+            for (int nt = 0; nt < C::NT; nt++)
+#pragma unroll
+                for (int run = 0; run < RUNS; run++) {
+                    const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bias_run[nt][run]);
+                    char *dst = region + row * ROWB + run_col<C>(nt, run) * ES;
+                    if constexpr (ES == 4) {
+                        *(float4v *)dst = v;
+                    } else {
+                        half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(half4 *)dst = h;
+                    }
+                }
+        }
+        // LDS -> C, 16 bytes per lane, consecutive lanes along a row.  A wave's
+        // LDS accesses complete in order, so no barrier is needed: the region
+        // is private to this wave.
+#pragma unroll
+        for (int it = 0; it < PR * CPR / 64; it++) {
+            const int q = it * 64 + lane;
+            const int r = q / CPR, cc = q % CPR;
+            const float4v v = *(const float4v *)(region + r * ROWB + cc * 16);
+            const int row = m_base + pass * PR + r;
+            const int col = n_base + cc * (16 / ES);
+            if (row < p.M) {
+                OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
+                if (col + 16 / ES <= p.N) {
+                    *(float4v *)dst = v;
+                } else {
+                    const OutT *e = (const OutT *)&v;
+#pragma unroll
+                    for (int j = 0; j < 16 / ES; j++)
+                        if (col + j < p.N)
+                            dst[j] = e[j];
+                }
+            }
+        }
+    }
+}
+
+template <class C, typename OutT, bool BIAS>
+__device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base, int n_base,
+                                         typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    if (p.line_store)
+        epilogue_lds<C, OutT, BIAS>(p, smem, m_base, n_base, acc);
+    else
+        epilogue_direct<C, OutT, BIAS>(p, m_base, n_base, acc);
 }
 
 // ============================================================================
@@ -489,10 +611,12 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
         for (int u = 0; u + UNIT < nsub; u += UNIT)
             pipe_unit<C, true>(p, ld, smem, u, nk, m0, n0, a_off, b_off, fa, fb, acc);
         pipe_unit<C, false>(p, ld, smem, nsub - UNIT, nk, m0, n0, a_off, b_off, fa, fb, acc);
-        // drain the dummy copies before the workgroup exits
+        // drain the dummy copies (they write zeros into LDS) and let every
+        // wave finish its fragment reads before LDS is reused for the epilogue
         wait_vmcnt<0>();
+        lds_barrier();
     }
-    epilogue<C, OutT, BIAS>(p, m0 + wm * C::TM, n0 + wn * C::TN, acc);
+    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, acc);
 }
 
 // ============================================================================
@@ -614,7 +738,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
             ld.store(smem + ((kt + 1) & 1) * C::STAGE_BYTES);
         lds_barrier();
     }
-    epilogue<C, OutT, BIAS>(p, m0 + wm * C::TM, n0 + wn * C::TN, acc);
+    // the loop ends on a barrier: LDS is free for the epilogue
+    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, acc);
 }
 
 // ------------------------------------------------------------ instances --

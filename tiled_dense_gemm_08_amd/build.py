@@ -21,7 +21,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtg.so")
-SOURCES = [os.path.join(CSRC, "tg_api.cpp"), os.path.join(CSRC, "tg_kernels.hip")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -31,28 +30,79 @@ FLAGS = ["-O3", "-std=c++20", "--offload-arch=" + ARCH,
          "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-command-line-argument"]
 
 
+SHARDS = 8   # kernel compilations run in parallel (tg_kernels.hip, TG_SHARD=i)
+BUILD_DIR = os.path.join(HERE, "_build")
+
+
+def _filter(out):
+    return "\n".join(l for l in out.splitlines()
+                     if "packed-fp32-ops" not in l and "hip-link" not in l)
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines()
-                    if "packed-fp32-ops" not in l and "hip-link" not in l)
+    out = _filter(r.stdout)
     if r.returncode != 0:
         sys.stderr.write(out + "\n")
         raise RuntimeError("build failed: " + " ".join(cmd))
     return out
 
 
+def _run_all(cmds):
+    """Run the commands concurrently; raise if any fails."""
+    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+             for c in cmds]
+    failed = []
+    for c, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            failed.append((c, _filter(out)))
+    for c, out in failed:
+        sys.stderr.write(out + "\n")
+    if failed:
+        raise RuntimeError("build failed: " + " ".join(failed[0][0]))
+
+
+def _shard_flags(i):
+    return ["-DTG_SHARD=%d" % i, "-DTG_SHARDS=%d" % SHARDS]
+
+
 def build_lib():
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC] + FLAGS + ["-fPIC", "-shared", "-o", tmp] + SOURCES)
-    os.replace(tmp, LIB)
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    kern = os.path.join(CSRC, "tg_kernels.hip")
+    objs, cmds = [], []
+    for i in range(SHARDS):
+        o = os.path.join(BUILD_DIR, "tg_kernels_%d.%s.o" % (i, tag))
+        objs.append(o)
+        cmds.append([HIPCC] + FLAGS + _shard_flags(i) + ["-fPIC", "-c", "-o", o, kern])
+    api = os.path.join(BUILD_DIR, "tg_api.%s.o" % tag)
+    objs.append(api)
+    cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", api, os.path.join(CSRC, "tg_api.cpp")])
+    try:
+        _run_all(cmds)
+        tmp = LIB + ".tmp" + tag
+        _run([HIPCC, "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", tmp] + objs)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 
 def device_asm(path=None):
-    path = path or os.path.join(HERE, "_build", "tg_kernels.s")
+    """Device assembly of every shard, concatenated into one file."""
+    path = path or os.path.join(BUILD_DIR, "tg_kernels.s")
     os.makedirs(os.path.dirname(path), exist_ok=True)
-    _run([HIPCC] + FLAGS + ["--cuda-device-only", "-S", "-o", path,
-                            os.path.join(CSRC, "tg_kernels.hip")])
+    kern = os.path.join(CSRC, "tg_kernels.hip")
+    parts = [path + ".%d" % i for i in range(SHARDS)]
+    _run_all([[HIPCC] + FLAGS + _shard_flags(i) + ["--cuda-device-only", "-S", "-o", parts[i], kern]
+              for i in range(SHARDS)])
+    with open(path, "w") as f:
+        for q in parts:
+            f.write(open(q).read())
+            os.remove(q)
     return path
 
 

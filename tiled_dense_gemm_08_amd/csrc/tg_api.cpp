@@ -82,6 +82,10 @@ bool supports(const KernelConfig &c, const Problem &p)
         return false;
     if (2 * span_elems(p.M, p.K, p.lda) >= kMaxSpan || 2 * span_elems(p.K, p.N, p.ldb) >= kMaxSpan)
         return false;
+    // lane offsets of rows past the edge (M + block_m rows of A, block_k + 1
+    // rows of B) must stay below 2^32 so that the range check sees them
+    if (2 * (p.M + c.bm) * p.lda >= (int64_t(1) << 32) || 2 * (c.bk + 1) * p.ldb >= kMaxSpan)
+        return false;
     return true;
 }
 
@@ -191,7 +195,10 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
         return TG_ERROR_UNSUPPORTED;
 
     (void)hipGetLastError();   // do not report an earlier, unrelated error
-    const hipError_t e = cfg.launch(k, p.c_dtype == TG_DTYPE_F16, p.fused, stream);
+    const tg::LaunchFn launch = tg::config_launch(id);
+    if (launch == nullptr)
+        return TG_ERROR_UNSUPPORTED;
+    const hipError_t e = launch(k, p.c_dtype == TG_DTYPE_F16, p.fused, stream);
     return e == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
 }
 

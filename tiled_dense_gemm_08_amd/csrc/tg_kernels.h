@@ -34,11 +34,16 @@ struct KernelConfig {
     int direct;       // 1: direct global->LDS path, 0: register-staged path
     int lds_bytes;
     const char *name;
-    LaunchFn launch;
 };
 
 extern const KernelConfig kConfigs[];
 extern const int kNumConfigs;
+
+// The kernels are compiled in up to kMaxShards separate translation units.
+constexpr int kMaxShards = 8;
+
+// Launcher of configuration id, or nullptr for an unknown id.
+LaunchFn config_launch(int id);
 
 }  // namespace tg
 

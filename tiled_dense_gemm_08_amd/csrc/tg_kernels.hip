@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "tg_kernels.h"
 
 namespace tg {
@@ -441,64 +443,98 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // (lane -> row lane / (BK/8), physical chunk lane % (BK/8)), or
 // B_ROWS_PER_LOAD k-rows of the B tile.  The swizzle is applied on the global
 // side: each lane fetches the logical chunk that belongs at its physical slot.
-// Only lane constants are kept in registers; per-instruction offsets are
-// recomputed at issue.
+//
+// The K position is carried by the buffer descriptors, not by the lane
+// offsets: for K step kt the A descriptor starts at A + kt*BK with its range
+// shortened by as much, and likewise for B, so the lane offsets are constants
+// of the tile and a K step costs a few scalar instructions.  The range check
+// of the descriptor gives zeros for the rows of A past M and the rows of B
+// past K (the host guarantees that those offsets do not wrap 32 bits);
+// columns of B past N and the columns of A past K in the last K step lie
+// inside the buffer and are pushed out of range explicitly.  Steps at or past
+// nk get a zero-length descriptor: every lane reads zeros without touching
+// memory, so each K step keeps the same number of outstanding copies.
 template <class C>
 struct DirectLoader {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    uint32_t a_lane;   // byte offset of this lane's A chunk in instruction 0 at k0 = 0
-    int a_row, a_kc;   // row within an instruction; logical k chunk
-    int b_row, b_phys; // k-row within an instruction; physical chunk
+    // Per-instruction lane offsets are kept in registers when there are few
+    // of them; otherwise they are rebuilt at issue from lane constants.
+    static constexpr bool KEEP = C::LOADS <= 8;
+    uint32_t voff[KEEP ? C::LOADS : 1];
+    uint32_t a_lane;   // A: byte offset of this lane's chunk in instruction 0
+    int a_kc8;         // A: logical k offset of this lane's chunk in the tile
+    int b_row, b_phys; // B: k-row within an instruction; physical chunk
+    uint32_t lds0;     // LDS byte address of the workgroup's buffer
 
-    __device__ __forceinline__ void init(const Params &p, int m0)
+    __device__ __forceinline__ uint32_t a_off(const Params &p, int t) const
     {
-        const int lane = threadIdx.x & 63;
-        ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, 0, p.a_bytes, kRsrcWord3);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void *)p.B, 0, p.b_bytes, kRsrcWord3);
-        a_row = lane / (C::BK / 8);
-        // the A swizzle depends on row % A_ROWS_PER_LOAD only (8 or 16 rows)
-        a_kc = (lane % (C::BK / 8)) ^ swz_a<C::BK>(a_row);
-        a_lane = (uint32_t)(((int64_t)(m0 + a_row) * p.lda + a_kc * 8) * 2);
-        b_row = lane / (C::BN / 8);
-        b_phys = lane % (C::BN / 8);
+        const int inst = (threadIdx.x >> 6) * C::A_LOADS + t;
+        return a_lane + (uint32_t)(inst * C::A_ROWS_PER_LOAD) * (uint32_t)p.lda * 2u;
     }
 
-    // Issue the copies of K step kt into LDS stage base `dst`.  Steps at or
-    // beyond nk are issued as dummies whose every lane reads out of range
-    // (zeros, no memory traffic), so that every K step has the same number
-    // of outstanding copies.
-    __device__ __forceinline__ void issue(const Params &p, int kt, char *dst, int nk, int m0,
-                                          int n0)
+    __device__ __forceinline__ uint32_t b_off(const Params &p, int t, int n0) const
     {
-        const int wave = threadIdx.x >> 6;
-        const uint32_t dst_lds = lds_addr(dst);
+        const int inst = (threadIdx.x >> 6) * C::B_LOADS + t;
+        const int k = inst * C::B_ROWS_PER_LOAD + b_row;
+        const int col = n0 + (b_phys ^ swz_b<C::BN>(k)) * 8;
+        return col < p.N ? ((uint32_t)k * (uint32_t)p.ldb + (uint32_t)col) * 2u : kOOB;
+    }
+
+    __device__ __forceinline__ void init(const Params &p, const char *smem, int m0, int n0)
+    {
+        const int lane = threadIdx.x & 63;
+        const int a_row = lane / (C::BK / 8);
+        // the A swizzle depends on row % A_ROWS_PER_LOAD only (8 or 16 rows)
+        a_kc8 = ((lane % (C::BK / 8)) ^ swz_a<C::BK>(a_row)) * 8;
+        a_lane = (uint32_t)(((int64_t)(m0 + a_row) * p.lda + a_kc8) * 2);
+        b_row = lane / (C::BN / 8);
+        b_phys = lane % (C::BN / 8);
+        lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int t = 0; t < C::A_LOADS; t++)
+                voff[t] = a_off(p, t);
+#pragma unroll
+            for (int t = 0; t < C::B_LOADS; t++)
+                voff[C::A_LOADS + t] = b_off(p, t, n0);
+        }
+    }
+
+    // Issue the copies of K step kt into LDS stage S (compile-time).
+    template <int S>
+    __device__ __forceinline__ void issue(const Params &p, int kt, int nk, int n0)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const bool valid = kt < nk;
         const int k0 = kt * C::BK;
-        const bool tail = kt == nk - 1 && (p.K % C::BK) != 0;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.A + k0), 0, valid ? (int)(p.a_bytes - (uint32_t)k0 * 2u) : 0, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.B + (int64_t)k0 * p.ldb), 0,
+            valid ? (int)(p.b_bytes - (uint32_t)k0 * (uint32_t)p.ldb * 2u) : 0, kRsrcWord3);
+        const uint32_t a_dst = lds0 + S * C::A_BYTES + wave * C::A_LOADS * 1024;
+        const uint32_t b_dst = lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES +
+                               wave * C::B_LOADS * 1024;
+        // K tail: this lane's A chunk lies past K (inside the row's padding or
+        // the next row), so it is pushed out of range
+        const bool a_dead = (kt == nk - 1) && (a_kc8 >= p.K - k0);
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++) {
-            const int inst = wave * C::A_LOADS + t;
-            const int row0 = inst * C::A_ROWS_PER_LOAD;
-            const uint32_t off = a_lane + (uint32_t)(row0 * p.lda * 2) + (uint32_t)(k0 * 2);
-            const bool ok = valid & (a_row < p.M - m0 - row0) & (!tail | (k0 + a_kc * 8 < p.K));
-            dma16(ra, off | ((uint32_t)!ok * kOOB),
-                  __builtin_amdgcn_readfirstlane(dst_lds + inst * 1024));
+            const uint32_t o = KEEP ? voff[t] : a_off(p, t);
+            dma16(ra, a_dead ? kOOB : o, a_dst + t * 1024);
         }
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++) {
-            const int inst = wave * C::B_LOADS + t;
-            const int k = inst * C::B_ROWS_PER_LOAD + b_row;
-            const int col = n0 + (b_phys ^ swz_b<C::BN>(k)) * 8;
-            const uint32_t off = (uint32_t)(((int64_t)(k0 + k) * p.ldb + col) * 2);
-            const bool ok = valid & (col < p.N) & (!tail | (k0 + k < p.K));
-            dma16(rb, off | ((uint32_t)!ok * kOOB),
-                  __builtin_amdgcn_readfirstlane(dst_lds + C::A_BYTES + inst * 1024));
+            const uint32_t o = KEEP ? voff[C::A_LOADS + t] : b_off(p, t, n0);
+            dma16(rb, o, b_dst + t * 1024);
         }
     }
 };
 
 // ============================================================================
-// Pipelined direct kernel.  The K loop is software-pipelined at MFMA k-step
+// Pipelined direct kernel.  LDS holds STAGES A tiles followed by STAGES B
+// tiles, so every fragment read of a stage is a lane base register plus an
+// immediate offset.  The K loop is unrolled by STAGES K steps (stage indices
+// are compile-time constants) and software-pipelined at MFMA k-step
 // granularity:
 //  * fragments are double-buffered in registers: while the MFMAs of k-step u
 //    run, the LDS reads for k-step u+1 are in flight;
@@ -510,6 +546,7 @@ struct DirectLoader {
 //    stage that step kt just vacated, so STAGES-1 K steps of compute cover
 //    each copy's latency; copies past the end are zero-reading dummies, which
 //    keeps the outstanding-copy count (and so the vmcnt wait) constant.
+// The K-step count is padded to a multiple of STAGES with all-zero steps.
 // ============================================================================
 template <int N, int R>
 __device__ __forceinline__ void sched_interleave_reads()
@@ -521,61 +558,71 @@ __device__ __forceinline__ void sched_interleave_reads()
     }
 }
 
-template <class C, int P, bool LAST_IN_STEP, bool HAS_NEXT>
-__device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld, char *smem,
-                                           int kt, int ks, int nk, int m0, int n0,
-                                           const int (&a_off)[C::KS], const int (&b_off)[C::NT],
-                                           half8 (&fa)[2][C::MT], half8 (&fb)[2][C::NT],
-                                           typename C::acc_t (&acc)[C::MT][C::NT])
+template <class C>
+struct PipeState {
+    int a_off[C::KS], b_off[C::NT];
+    half8 fa[2][C::MT], fb[2][C::NT];
+    typename C::acc_t acc[C::MT][C::NT];
+};
+
+template <class C, int S>
+__device__ __forceinline__ const char *a_stage(const char *smem)
 {
+    return smem + S * C::A_BYTES;
+}
+
+template <class C, int S>
+__device__ __forceinline__ const char *b_stage(const char *smem)
+{
+    return smem + C::STAGES * C::A_BYTES + S * C::B_BYTES;
+}
+
+// k-step U (0 .. STAGES*KS-1) of a loop body; FINAL: the body that ends the
+// K loop (no barrier, reads or copies after its last k-step).
+template <class C, int U, bool FINAL>
+__device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld, const char *smem,
+                                           int kt0, int nk, int n0, PipeState<C> &st)
+{
+    constexpr int S = U / C::KS, ks = U % C::KS, P = U % 2;
     constexpr int NMF = C::MT * C::NT;
     constexpr int NRD = C::MT + 2 * C::NT;
     constexpr int H = NMF / 2;
     constexpr int R = H / NRD > 0 ? H / NRD : 1;
-    if constexpr (!LAST_IN_STEP) {
+    if constexpr (ks + 1 < C::KS) {
         // next k-step of the same K step: prefetch its fragments
-        const char *as = smem + (kt % C::STAGES) * C::STAGE_BYTES;
-        read_frags<C>(as, as + C::A_BYTES, ks + 1, a_off, b_off, fa[1 - P], fb[1 - P]);
-        mfma_range<C, 0, NMF>(fa[P], fb[P], acc);
+        read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off, st.b_off,
+                      st.fa[1 - P], st.fb[1 - P]);
+        mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
         sched_interleave_reads<NRD, R>();
-    } else if constexpr (HAS_NEXT) {
-        mfma_range<C, 0, H>(fa[P], fb[P], acc);
-        wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of step kt+1 landed
-        lds_barrier();                               // everyone's did; step kt is free
-        const char *as = smem + ((kt + 1) % C::STAGES) * C::STAGE_BYTES;
-        read_frags<C>(as, as + C::A_BYTES, 0, a_off, b_off, fa[1 - P], fb[1 - P]);
-        ld.issue(p, kt + C::STAGES, smem + (kt % C::STAGES) * C::STAGE_BYTES, nk, m0, n0);
-        mfma_range<C, H, NMF>(fa[P], fb[P], acc);
+    } else if constexpr (!FINAL || S + 1 < C::STAGES) {
+        constexpr int SN = (S + 1) % C::STAGES;
+        mfma_range<C, 0, H>(st.fa[P], st.fb[P], st.acc);
+        wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
+        lds_barrier();                               // everyone's did; stage S is free
+        read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
+                      st.fa[1 - P], st.fb[1 - P]);
+        ld.template issue<S>(p, kt0 + S + C::STAGES, nk, n0);
+        mfma_range<C, H, NMF>(st.fa[P], st.fb[P], st.acc);
         sched_interleave_reads<NRD, R>();
     } else {
-        mfma_range<C, 0, NMF>(fa[P], fb[P], acc);
+        mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
     }
 }
 
-// One loop unit: UNIT = max(2, KS) consecutive k-steps starting at u0 (a
-// multiple of UNIT), so register-buffer parity and position inside the K
-// step are compile-time constants.  HAS_NEXT = false for the final unit.
-template <class C, bool HAS_NEXT, int J = 0>
-__device__ __forceinline__ void pipe_unit(const Params &p, DirectLoader<C> &ld, char *smem, int u0,
-                                          int nk, int m0, int n0, const int (&a_off)[C::KS],
-                                          const int (&b_off)[C::NT], half8 (&fa)[2][C::MT],
-                                          half8 (&fb)[2][C::NT],
-                                          typename C::acc_t (&acc)[C::MT][C::NT])
+template <class C, bool FINAL, int U = 0>
+__device__ __forceinline__ void pipe_body(const Params &p, DirectLoader<C> &ld, const char *smem,
+                                          int kt0, int nk, int n0, PipeState<C> &st)
 {
-    constexpr int UNIT = C::KS > 2 ? C::KS : 2;
-    if constexpr (J < UNIT) {
-        constexpr int ks = J % C::KS;
-        constexpr bool last = ks == C::KS - 1;
-        const int kt = u0 / C::KS + J / C::KS;
-        pipe_kstep<C, J % 2, last, (J + 1 < UNIT) || HAS_NEXT>(p, ld, smem, kt, ks, nk, m0, n0,
-                                                               a_off, b_off, fa, fb, acc);
-        pipe_unit<C, HAS_NEXT, J + 1>(p, ld, smem, u0, nk, m0, n0, a_off, b_off, fa, fb, acc);
+    if constexpr (U < C::STAGES * C::KS) {
+        pipe_kstep<C, U, FINAL>(p, ld, smem, kt0, nk, n0, st);
+        pipe_body<C, FINAL, U + 1>(p, ld, smem, kt0, nk, n0, st);
     }
 }
 
 template <class C, typename OutT, bool BIAS>
 __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 {
+    static_assert((C::STAGES * C::KS) % 2 == 0, "register double buffer parity per loop body");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -583,40 +630,36 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    typename C::acc_t acc[C::MT][C::NT];
+    PipeState<C> st;
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
         for (int j = 0; j < C::NT; j++)
-            acc[i][j] = typename C::acc_t{};
+            st.acc[i][j] = typename C::acc_t{};
 
     const int nk = (p.K + C::BK - 1) / C::BK;
     if (nk > 0) {
-        int a_off[C::KS], b_off[C::NT];
-        fragment_offsets<C>(wm, wn, a_off, b_off);
+        fragment_offsets<C>(wm, wn, st.a_off, st.b_off);
         DirectLoader<C> ld;
-        ld.init(p, m0);
-#pragma unroll
-        for (int s = 0; s < C::STAGES; s++)
-            ld.issue(p, s, smem + s * C::STAGE_BYTES, nk, m0, n0);
+        ld.init(p, smem, m0, n0);
+        [&]<int... S>(std::integer_sequence<int, S...>) {
+            (ld.template issue<S>(p, S, nk, n0), ...);
+        }(std::make_integer_sequence<int, C::STAGES>{});
         wait_vmcnt<(C::STAGES - 1) * C::LOADS>();
         lds_barrier();
-        half8 fa[2][C::MT], fb[2][C::NT];
-        read_frags<C>(smem, smem + C::A_BYTES, 0, a_off, b_off, fa[0], fb[0]);
-
-        // MFMA k-steps 0 .. nsub-1 in units of UNIT; with KS = 1 an odd K-step
-        // count is padded by one all-zero K step (its copies read out of range)
-        constexpr int UNIT = C::KS > 2 ? C::KS : 2;
-        const int nsub = (C::KS == 1) ? ((nk + 1) & ~1) : nk * C::KS;
-        for (int u = 0; u + UNIT < nsub; u += UNIT)
-            pipe_unit<C, true>(p, ld, smem, u, nk, m0, n0, a_off, b_off, fa, fb, acc);
-        pipe_unit<C, false>(p, ld, smem, nsub - UNIT, nk, m0, n0, a_off, b_off, fa, fb, acc);
+        read_frags<C>(a_stage<C, 0>(smem), b_stage<C, 0>(smem), 0, st.a_off, st.b_off, st.fa[0],
+                      st.fb[0]);
+        const int nsteps = (nk + C::STAGES - 1) / C::STAGES * C::STAGES;
+        int kt = 0;
+        for (; kt + C::STAGES < nsteps; kt += C::STAGES)
+            pipe_body<C, false>(p, ld, smem, kt, nk, n0, st);
+        pipe_body<C, true>(p, ld, smem, kt, nk, n0, st);
         // drain the dummy copies (they write zeros into LDS) and let every
         // wave finish its fragment reads before LDS is reused for the epilogue
         wait_vmcnt<0>();
         lds_barrier();
     }
-    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, acc);
+    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, st.acc);
 }
 
 // ============================================================================
@@ -762,28 +805,78 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 #undef TG_GO
 }
 
-// Explicit instantiation: both compile passes see every kernel instance.
+// The library is built from TG_SHARDS compilations of this file (so they
+// can run in parallel); compilation TG_SHARD instantiates the configurations
+// whose id is TG_SHARD modulo TG_SHARDS and publishes their launchers in its
+// own table.  Compilation 0 also holds the description table.
+#ifndef TG_SHARD
+#define TG_SHARD 0
+#endif
+#ifndef TG_SHARDS
+#define TG_SHARDS 1
+#endif
+static_assert(TG_SHARDS >= 1 && TG_SHARDS <= kMaxShards && TG_SHARD < TG_SHARDS, "shards");
+
+template <int ID, class CFG, int KIND>
+LaunchFn shard_launch()
+{
+    if constexpr (ID % TG_SHARDS == TG_SHARD)
+        return &launch_cfg<CFG, KIND>;
+    else
+        return nullptr;
+}
+
+#define TG_CAT2(a, b) a##b
+#define TG_CAT(a, b) TG_CAT2(a, b)
+
+// The launch tables are host data (the device pass would otherwise turn the
+// const arrays into device constant memory).
+#if !defined(__HIP_DEVICE_COMPILE__)
+// every shard's table, weakly referenced: shards beyond TG_SHARDS do not exist
+#define TG_SHARD_DECL(i) extern const LaunchFn kShardLaunch##i[] __attribute__((weak));
+TG_SHARD_DECL(0) TG_SHARD_DECL(1) TG_SHARD_DECL(2) TG_SHARD_DECL(3)
+TG_SHARD_DECL(4) TG_SHARD_DECL(5) TG_SHARD_DECL(6) TG_SHARD_DECL(7)
+#undef TG_SHARD_DECL
+
 #define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
-    template hipError_t launch_cfg<Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>(           \
-        const Params &, bool, bool, hipStream_t);
+    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>(),
+const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
+#include "tg_config_list.inc"
+};
+#undef TG_CONFIG_ROW
+#else
+// device pass: instantiate the kernels of this shard
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
+    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>();
 #include "tg_config_list.inc"
 #undef TG_CONFIG_ROW
+#endif
 
-// The launch table is host data (the device pass would otherwise turn the
-// const array into device constant memory).
-#if !defined(__HIP_DEVICE_COMPILE__)
+#if TG_SHARD == 0 && !defined(__HIP_DEVICE_COMPILE__)
 #define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
      Cfg<BM, BN, BK, WM, WN, ST, MI>::LDS_BYTES,                                     \
      (KIND == 2 ? "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI    \
-                : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI),         \
-     &launch_cfg<Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>},
+                : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI)},
 
 const KernelConfig kConfigs[] = {
 #include "tg_config_list.inc"
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 #undef TG_CONFIG_ROW
+
+LaunchFn config_launch(int id)
+{
+    static const LaunchFn *const shards[kMaxShards] = {
+        kShardLaunch0, kShardLaunch1, kShardLaunch2, kShardLaunch3,
+        kShardLaunch4, kShardLaunch5, kShardLaunch6, kShardLaunch7};
+    if (id < 0 || id >= kNumConfigs)
+        return nullptr;
+    for (int s = 0; s < kMaxShards; s++)
+        if (shards[s] && shards[s][id])
+            return shards[s][id];
+    return nullptr;
+}
 #endif
 
 }  // namespace tg

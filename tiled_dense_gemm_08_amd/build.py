@@ -107,15 +107,16 @@ def device_asm(path=None):
 
 
 def check_m0(asm_text):
-    """Every M0 use must be `s_mov_b32 m0, sX` directly followed by a
-    buffer_load ... lds (the copy that consumes it)."""
+    """Every M0 use must be `s_mov_b32 m0, sX`, one wait state (`s_nop 0`),
+    then the buffer_load ... lds that consumes it."""
     lines = [l.strip() for l in asm_text.splitlines()
              if l.strip() and not l.strip().startswith((";", "."))]
     bad = []
     for i, l in enumerate(lines):
         if re.search(r"\bm0\b", l):
-            ok = (l.startswith("s_mov_b32 m0,") and i + 1 < len(lines)
-                  and lines[i + 1].startswith("buffer_load_dword") and lines[i + 1].endswith("lds"))
+            ok = (l.startswith("s_mov_b32 m0,") and i + 2 < len(lines)
+                  and lines[i + 1] == "s_nop 0"
+                  and lines[i + 2].startswith("buffer_load_dword") and lines[i + 2].endswith("lds"))
             if not ok:
                 bad.append(l)
     return bad

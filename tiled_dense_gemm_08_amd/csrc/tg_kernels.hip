@@ -130,8 +130,9 @@ template <int MI> struct AccT;
 template <> struct AccT<16> { typedef float4v type; };
 template <> struct AccT<32> { typedef float16v type; };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_, int SCHED_>
 struct Cfg {
+    static constexpr int SCHED = SCHED_;   // copy issue: 0 burst after the barrier, 1 spread
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WM_, WAVES_N = WN_;
     static constexpr int STAGES = STAGES_;
@@ -347,28 +348,21 @@ __device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     char *region = smem + wave * REGION;
 
-    float4v bias_run[C::NT][RUNS];
-#pragma unroll
-    for (int nt = 0; nt < C::NT; nt++)
-#pragma unroll
-        for (int run = 0; run < RUNS; run++) {
-            bias_run[nt][run] = float4v{0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS)
-                bias_run[nt][run] = load_bias4(p, n_base + run_col<C>(nt, run));
-        }
-
 #pragma unroll
     for (int pass = 0; pass < C::TM / PR; pass++) {
         // registers -> LDS (row-major, padded rows)
 #pragma unroll
-        for (int i = 0; i < MT_PASS; i++) {
-            const int mt = pass * MT_PASS + i;
-            const int row = i * C::MI + lane % C::MI;
+        for (int nt = 0; nt < C::NT; nt++)
 #pragma unroll
-            for (int nt = 0; nt < C::NT; nt++)
+            for (int run = 0; run < RUNS; run++) {
+                float4v bv = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS)
+                    bv = load_bias4(p, n_base + run_col<C>(nt, run));
 #pragma unroll
-                for (int run = 0; run < RUNS; run++) {
-                    const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bias_run[nt][run]);
+                for (int i = 0; i < MT_PASS; i++) {
+                    const int mt = pass * MT_PASS + i;
+                    const int row = i * C::MI + lane % C::MI;
+                    const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
                     char *dst = region + row * ROWB + run_col<C>(nt, run) * ES;
                     if constexpr (ES == 4) {
                         *(float4v *)dst = v;
@@ -424,10 +418,11 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
 // LDS read as dependent on the copy (it would wait for all outstanding copies
 // before each one); the kernels wait on vmcnt themselves, before the barrier
 // that publishes a stage.  M0 is written here and nowhere else in these
-// kernels (the build checks the device assembly for that).
+// kernels (the build checks the device assembly for that).  A scalar write of
+// M0 needs one wait state before a load that uses it as the LDS address.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(lds)
                  : "memory");
@@ -499,33 +494,42 @@ struct DirectLoader {
         }
     }
 
-    // Issue the copies of K step kt into LDS stage S (compile-time).
-    template <int S>
-    __device__ __forceinline__ void issue(const Params &p, int kt, int nk, int n0)
+    // Issue copy instruction T (A copies first, then B) of K step kt into
+    // LDS stage S.
+    template <int S, int T>
+    __device__ __forceinline__ void issue_one(const Params &p, int kt, int nk, int n0)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const bool valid = kt < nk;
         const int k0 = kt * C::BK;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.A + k0), 0, valid ? (int)(p.a_bytes - (uint32_t)k0 * 2u) : 0, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.B + (int64_t)k0 * p.ldb), 0,
-            valid ? (int)(p.b_bytes - (uint32_t)k0 * (uint32_t)p.ldb * 2u) : 0, kRsrcWord3);
-        const uint32_t a_dst = lds0 + S * C::A_BYTES + wave * C::A_LOADS * 1024;
-        const uint32_t b_dst = lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES +
-                               wave * C::B_LOADS * 1024;
-        // K tail: this lane's A chunk lies past K (inside the row's padding or
-        // the next row), so it is pushed out of range
-        const bool a_dead = (kt == nk - 1) && (a_kc8 >= p.K - k0);
-#pragma unroll
-        for (int t = 0; t < C::A_LOADS; t++) {
-            const uint32_t o = KEEP ? voff[t] : a_off(p, t);
-            dma16(ra, a_dead ? kOOB : o, a_dst + t * 1024);
+        if constexpr (T < C::A_LOADS) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.A + k0), 0, valid ? (int)(p.a_bytes - (uint32_t)k0 * 2u) : 0,
+                kRsrcWord3);
+            // K tail: this lane's A chunk lies past K (inside the row's padding
+            // or the next row), so it is pushed out of range
+            const bool a_dead = (kt == nk - 1) && (a_kc8 >= p.K - k0);
+            const uint32_t o = KEEP ? voff[T] : a_off(p, T);
+            dma16(ra, a_dead ? kOOB : o,
+                  lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024);
+        } else {
+            constexpr int t = T - C::A_LOADS;
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.B + (int64_t)k0 * p.ldb), 0,
+                valid ? (int)(p.b_bytes - (uint32_t)k0 * (uint32_t)p.ldb * 2u) : 0, kRsrcWord3);
+            const uint32_t o = KEEP ? voff[T] : b_off(p, t, n0);
+            dma16(rb, o,
+                  lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024);
         }
-#pragma unroll
-        for (int t = 0; t < C::B_LOADS; t++) {
-            const uint32_t o = KEEP ? voff[C::A_LOADS + t] : b_off(p, t, n0);
-            dma16(rb, o, b_dst + t * 1024);
+    }
+
+    // Copy instructions [T0, T1) of K step kt into LDS stage S.
+    template <int S, int T0 = 0, int T1 = C::LOADS>
+    __device__ __forceinline__ void issue(const Params &p, int kt, int nk, int n0)
+    {
+        if constexpr (T0 < T1) {
+            issue_one<S, T0>(p, kt, nk, n0);
+            issue<S, T0 + 1, T1>(p, kt, nk, n0);
         }
     }
 };
@@ -577,6 +581,54 @@ __device__ __forceinline__ const char *b_stage(const char *smem)
     return smem + C::STAGES * C::A_BYTES + S * C::B_BYTES;
 }
 
+// Spread copy schedule (SCHED = 1).  The barrier in the last k-step of K step
+// S frees stage S; the copies that refill it (K step kt0 + S + STAGES) are
+// issued one at a time between the MFMAs that follow, up to the next barrier
+// (the "window" of stage S), instead of in one burst: in-order issue would
+// otherwise hold every later MFMA behind copies waiting for the vector memory
+// pipeline.  With two stages the next barrier waits for these very copies,
+// so they are packed into the first half of the window.  Window positions
+// count MFMAs from the barrier; a window that starts in the last k-step of a
+// loop body ends in the next body (window -1 of that body).
+template <class C>
+struct Spread {
+    static constexpr int NMF = C::MT * C::NT;
+    static constexpr int H = NMF / 2;
+    static constexpr int SPAN = C::STAGES == 2 ? C::KS * NMF / 2 : C::KS * NMF;
+    static constexpr int pos(int t) { return t * SPAN / C::LOADS; }
+};
+
+// MFMA I of the current k-step, then the copies of window W whose position is
+// OFF (window W refills stage (W + STAGES) % STAGES with K step kt0+W+STAGES).
+template <class C, int W, int OFF, int T = 0>
+__device__ __forceinline__ void window_copies(const Params &p, DirectLoader<C> &ld, int kt0, int nk,
+                                              int n0)
+{
+    if constexpr (T < C::LOADS) {
+        if constexpr (Spread<C>::pos(T) == OFF) {
+            __builtin_amdgcn_sched_barrier(0);
+            ld.template issue_one<(W + C::STAGES) % C::STAGES, T>(p, kt0 + W + C::STAGES, nk, n0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        window_copies<C, W, OFF, T + 1>(p, ld, kt0, nk, n0);
+    }
+}
+
+// MFMAs [I, HI) of the k-step; MFMA I sits at position OFF of window W.
+template <class C, int W, int OFF, int I, int HI>
+__device__ __forceinline__ void mfma_window(const Params &p, DirectLoader<C> &ld, int kt0, int nk,
+                                            int n0, const half8 (&fa)[C::MT],
+                                            const half8 (&fb)[C::NT],
+                                            typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    if constexpr (I < HI) {
+        constexpr int mt = I / C::NT, nt = I % C::NT;
+        acc[mt][nt] = mfma<C>(fb[nt], fa[mt], acc[mt][nt]);
+        window_copies<C, W, OFF>(p, ld, kt0, nk, n0);
+        mfma_window<C, W, OFF + 1, I + 1, HI>(p, ld, kt0, nk, n0, fa, fb, acc);
+    }
+}
+
 // k-step U (0 .. STAGES*KS-1) of a loop body; FINAL: the body that ends the
 // K loop (no barrier, reads or copies after its last k-step).
 template <class C, int U, bool FINAL>
@@ -588,13 +640,32 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
     constexpr int NRD = C::MT + 2 * C::NT;
     constexpr int H = NMF / 2;
     constexpr int R = H / NRD > 0 ? H / NRD : 1;
-    if constexpr (ks + 1 < C::KS) {
+    constexpr bool BARRIER = ks + 1 == C::KS && (!FINAL || S + 1 < C::STAGES);
+    if constexpr (C::SCHED == 1) {
+        // position of this k-step's first MFMA in window S-1
+        constexpr int OFF = H + ks * NMF;
+        if constexpr (!BARRIER) {
+            if constexpr (ks + 1 < C::KS)
+                read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off,
+                              st.b_off, st.fa[1 - P], st.fb[1 - P]);
+            mfma_window<C, S - 1, OFF, 0, NMF>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+        } else {
+            constexpr int SN = (S + 1) % C::STAGES;
+            mfma_window<C, S - 1, OFF, 0, H>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
+            lds_barrier();                               // everyone's did; stage S is free
+            read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
+                          st.fa[1 - P], st.fb[1 - P]);
+            mfma_window<C, S, 0, H, NMF>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+        }
+    } else if constexpr (ks + 1 < C::KS) {
         // next k-step of the same K step: prefetch its fragments
         read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off, st.b_off,
                       st.fa[1 - P], st.fb[1 - P]);
         mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
         sched_interleave_reads<NRD, R>();
-    } else if constexpr (!FINAL || S + 1 < C::STAGES) {
+    } else if constexpr (BARRIER) {
         constexpr int SN = (S + 1) % C::STAGES;
         mfma_range<C, 0, H>(st.fa[P], st.fb[P], st.acc);
         wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
@@ -606,6 +677,20 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
         sched_interleave_reads<NRD, R>();
     } else {
         mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
+    }
+}
+
+// Copies the prologue issues after those of K step 0.
+template <class C>
+constexpr int prologue_after_step0()
+{
+    if constexpr (C::SCHED == 1) {
+        int early = 0;
+        for (int t = 0; t < C::LOADS; t++)
+            early += Spread<C>::pos(t) < Spread<C>::H;
+        return (C::STAGES - 2) * C::LOADS + early;
+    } else {
+        return (C::STAGES - 1) * C::LOADS;
     }
 }
 
@@ -642,10 +727,25 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
         fragment_offsets<C>(wm, wn, st.a_off, st.b_off);
         DirectLoader<C> ld;
         ld.init(p, smem, m0, n0);
-        [&]<int... S>(std::integer_sequence<int, S...>) {
-            (ld.template issue<S>(p, S, nk, n0), ...);
-        }(std::make_integer_sequence<int, C::STAGES>{});
-        wait_vmcnt<(C::STAGES - 1) * C::LOADS>();
+        if constexpr (C::SCHED == 1) {
+            // steps 0 .. STAGES-2 whole; of step STAGES-1 the copies whose
+            // window position precedes the loop (the rest come from window -1
+            // of the first loop body)
+            [&]<int... S>(std::integer_sequence<int, S...>) {
+                (ld.template issue<S>(p, S, nk, n0), ...);
+            }(std::make_integer_sequence<int, C::STAGES - 1>{});
+            [&]<int... T>(std::integer_sequence<int, T...>) {
+                ((Spread<C>::pos(T) < Spread<C>::H
+                      ? ld.template issue_one<C::STAGES - 1, T>(p, C::STAGES - 1, nk, n0)
+                      : void()),
+                 ...);
+            }(std::make_integer_sequence<int, C::LOADS>{});
+        } else {
+            [&]<int... S>(std::integer_sequence<int, S...>) {
+                (ld.template issue<S>(p, S, nk, n0), ...);
+            }(std::make_integer_sequence<int, C::STAGES>{});
+        }
+        wait_vmcnt<prologue_after_step0<C>()>();   // step 0 landed
         lds_barrier();
         read_frags<C>(a_stage<C, 0>(smem), b_stage<C, 0>(smem), 0, st.a_off, st.b_off, st.fa[0],
                       st.fb[0]);
@@ -838,25 +938,26 @@ TG_SHARD_DECL(0) TG_SHARD_DECL(1) TG_SHARD_DECL(2) TG_SHARD_DECL(3)
 TG_SHARD_DECL(4) TG_SHARD_DECL(5) TG_SHARD_DECL(6) TG_SHARD_DECL(7)
 #undef TG_SHARD_DECL
 
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
-    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>(),
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
+    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND>(),
 const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
 #include "tg_config_list.inc"
 };
 #undef TG_CONFIG_ROW
 #else
 // device pass: instantiate the kernels of this shard
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
-    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI>, KIND>();
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
+    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND>();
 #include "tg_config_list.inc"
 #undef TG_CONFIG_ROW
 #endif
 
 #if TG_SHARD == 0 && !defined(__HIP_DEVICE_COMPILE__)
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND)                          \
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
-     Cfg<BM, BN, BK, WM, WN, ST, MI>::LDS_BYTES,                                     \
+     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>::LDS_BYTES,                                     \
      (KIND == 2 ? "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI    \
+                      "_c" #SCH                                                      \
                 : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI)},
 
 const KernelConfig kConfigs[] = {

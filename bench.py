@@ -39,7 +39,10 @@ PEAK_TFLOPS = PEAK_CUS * PEAK_GHZ * FLOP_PER_CLK_CU / 1e3
 # factors are 2.0 and 1.0).  Keyed by workload, kernel configuration and a
 # digest of the kernel sources: a kernel changed since the counters were
 # taken reports null.
-TRAFFIC_BYTES = {}
+TRAFFIC_BYTES = {
+    # FETCH_SIZE 802587 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x4_mi32_c0", "7180bc0f9dbe81f6"): 1777897000,
+}
 
 
 def kernel_source_digest():
@@ -169,9 +172,9 @@ def main():
             t = time.perf_counter()
             oracle.gemm_ref(w["A"][:rows], w["B"], rows, N, K, bias=w["bias"], nthreads=threads)
             dt = time.perf_counter() - t
-            if dt >= a.cpu_seconds / 4 or rows >= M:
+            if dt >= 0.8 * a.cpu_seconds or rows >= M:
                 break
-            rows = min(M, rows * max(2, int(a.cpu_seconds / 4 / max(dt, 1e-3))))
+            rows = min(M, max(rows + 1, int(rows * a.cpu_seconds / max(dt, 1e-3))))
         cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
                "sample": "first %d of %d rows of C (%dx%dx%d fp64 dot products), %.1f s"

@@ -74,8 +74,8 @@ tg_status validate(const Problem &p)
 // Whether a configuration's load path can serve this problem.
 bool supports(const KernelConfig &c, const Problem &p)
 {
-    if (!c.direct)
-        return true;   // register-staged path: any alignment, any sizes
+    if (!c.direct)   // register-staged path: any alignment; in-tile offsets fit 31 bits
+        return int64_t(c.bm) * p.lda < kMaxSpan && int64_t(c.bk) * p.ldb < kMaxSpan;
     if (!aligned(p.A, 16) || !aligned(p.B, 16))
         return false;
     if (p.lda % 8 || p.ldb % 8 || p.K % 8 || p.N % 8)
@@ -189,8 +189,6 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     k.vec_store = (p.ldc % 4 == 0) && aligned(p.C, 4 * c_elem);
     k.line_store = ((p.ldc * c_elem) % 16 == 0) && aligned(p.C, 16);
     k.vec_bias = p.fused && aligned(p.bias, 16);
-    k.a_vec = (p.lda % 8 == 0) && aligned(p.A, 16);
-    k.b_vec = (p.ldb % 8 == 0) && aligned(p.B, 16);
     if ((int64_t)k.tiles_m * k.tiles_n > kMaxDim)
         return TG_ERROR_UNSUPPORTED;
 

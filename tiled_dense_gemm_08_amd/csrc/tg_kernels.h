@@ -22,7 +22,6 @@ struct Params {
     int vec_store;   // C rows allow 4-element vector stores (alignment)
     int line_store;  // C rows allow 16-byte stores: staged, full-line epilogue
     int vec_bias;    // bias allows 16-byte loads
-    int a_vec, b_vec;  // staged path: rows allow 16-byte loads
 };
 
 typedef hipError_t (*LaunchFn)(const Params &p, bool f16_out, bool bias, hipStream_t s);

@@ -763,81 +763,155 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 }
 
 // ============================================================================
-// General path: register-staged copies with per-element bounds; any pointer
-// alignment (2-byte) and any leading dimensions.  Same LDS layout and
-// fragment reads, two LDS stages.
+// General path: register-staged copies; any pointer alignment (2-byte) and any
+// leading dimensions.  Whole 16-byte chunks are read with one unaligned vector
+// load (the memory system serves misaligned vector loads of global memory);
+// chunks that cross the K or N edge are read element by element.  Same LDS
+// layout and fragment reads as the direct path, two LDS stages.
 // ============================================================================
 template <class C>
 struct StagedLoader {
-    half8 ra[C::A_LOADS];
-    half8 rb[C::B_LOADS];
+    half8 r[C::LOADS];     // one K step of this thread's chunks: A first, then B
+    uint32_t off[C::LOADS];  // element offset of each chunk from the tile corner
+                           // (host: bm * lda and bk * ldb stay below 2^31)
 
+    __device__ __forceinline__ static int a_row(int t)
+    {
+        return ((threadIdx.x >> 6) * C::A_LOADS + t) * C::A_ROWS_PER_LOAD +
+               (threadIdx.x & 63) / (C::BK / 8);
+    }
+    __device__ __forceinline__ static int a_kc(int t)
+    {
+        return (((threadIdx.x & 63) % (C::BK / 8)) ^ swz_a<C::BK>(a_row(t))) * 8;
+    }
+    __device__ __forceinline__ static int b_k(int t)
+    {
+        return ((threadIdx.x >> 6) * C::B_LOADS + t) * C::B_ROWS_PER_LOAD +
+               (threadIdx.x & 63) / (C::BN / 8);
+    }
+    __device__ __forceinline__ static int b_col(int t)
+    {
+        return (((threadIdx.x & 63) % (C::BN / 8)) ^ swz_b<C::BN>(b_k(t))) * 8;
+    }
+
+    __device__ __forceinline__ void init(const Params &p)
+    {
+#pragma unroll
+        for (int t = 0; t < C::A_LOADS; t++)
+            off[t] = (uint32_t)(a_row(t) * p.lda + a_kc(t));
+#pragma unroll
+        for (int t = 0; t < C::B_LOADS; t++)
+            off[C::A_LOADS + t] = (uint32_t)(b_k(t) * p.ldb + b_col(t));
+    }
+
+    // Load K step kt into registers; zeros past M, N and K (so steps past the
+    // end load zeros).  Whole 16-byte chunks are one unaligned vector load.
     __device__ __forceinline__ void load(const Params &p, int m0, int n0, int kt)
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int k0 = kt * C::BK;
-        const _Float16 *A = p.A, *B = p.B;
+        const _Float16 *a0 = p.A + (int64_t)m0 * p.lda + k0;
+        const _Float16 *b0 = p.B + (int64_t)k0 * p.ldb + n0;
+        if (m0 + C::BM <= p.M && n0 + C::BN <= p.N && k0 + C::BK <= p.K) {
+            // interior: every chunk is whole
+#pragma unroll
+            for (int t = 0; t < C::LOADS; t++)
+                __builtin_memcpy(&r[t], (t < C::A_LOADS ? a0 : b0) + off[t], 16);
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++) {
-            const int inst = wave * C::A_LOADS + t;
-            const int row = inst * C::A_ROWS_PER_LOAD + lane / (C::BK / 8);
-            const int phys = lane % (C::BK / 8);
-            const int kc = k0 + (phys ^ swz_a<C::BK>(row)) * 8;
-            const int gm = m0 + row;
-            half8 v;
-            if (gm < p.M) {
-                const _Float16 *src = A + (int64_t)gm * p.lda + kc;
-                if (p.a_vec && kc + 7 < p.K) {
-                    v = *(const half8 *)src;
+            const int kleft = p.K - k0 - a_kc(t);   // valid elements of the chunk
+            half8 v = {};
+            if (m0 + a_row(t) < p.M && kleft > 0) {
+                const _Float16 *src = a0 + off[t];
+                if (kleft >= 8) {
+                    __builtin_memcpy(&v, src, 16);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; e++)
-                        v[e] = (kc + e < p.K) ? src[e] : (_Float16)0.f;
+                        v[e] = e < kleft ? src[e] : (_Float16)0.f;
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++)
-                    v[e] = (_Float16)0.f;
             }
-            ra[t] = v;
+            r[t] = v;
         }
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++) {
-            const int inst = wave * C::B_LOADS + t;
-            const int k = inst * C::B_ROWS_PER_LOAD + lane / (C::BN / 8);
-            const int phys = lane % (C::BN / 8);
-            const int gn = n0 + (phys ^ swz_b<C::BN>(k)) * 8;
-            const int gk = k0 + k;
-            half8 v;
-            if (gk < p.K) {
-                const _Float16 *src = B + (int64_t)gk * p.ldb + gn;
-                if (p.b_vec && gn + 7 < p.N) {
-                    v = *(const half8 *)src;
+            const int nleft = p.N - n0 - b_col(t);
+            half8 v = {};
+            if (k0 + b_k(t) < p.K && nleft > 0) {
+                const _Float16 *src = b0 + off[C::A_LOADS + t];
+                if (nleft >= 8) {
+                    __builtin_memcpy(&v, src, 16);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; e++)
-                        v[e] = (gn + e < p.N) ? src[e] : (_Float16)0.f;
+                        v[e] = e < nleft ? src[e] : (_Float16)0.f;
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++)
-                    v[e] = (_Float16)0.f;
             }
-            rb[t] = v;
+            r[C::A_LOADS + t] = v;
         }
     }
 
-    __device__ __forceinline__ void store(char *dst)
+    // Registers -> LDS stage S, in the layout the direct copies produce.
+    template <int S>
+    __device__ __forceinline__ void store(char *smem) const
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++)
-            *(half8 *)(dst + (wave * C::A_LOADS + t) * 1024 + lane * 16) = ra[t];
+            *(half8 *)(smem + S * C::A_BYTES + (wave * C::A_LOADS + t) * 1024 + lane * 16) = r[t];
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++)
-            *(half8 *)(dst + C::A_BYTES + (wave * C::B_LOADS + t) * 1024 + lane * 16) = rb[t];
+            *(half8 *)(smem + C::STAGES * C::A_BYTES + S * C::B_BYTES +
+                       (wave * C::B_LOADS + t) * 1024 + lane * 16) = r[C::A_LOADS + t];
     }
 };
+
+// k-step U of a loop body of the register-staged kernel (two LDS stages).
+// The loads of K step j+1 are issued right after the barrier that starts K
+// step j and written to LDS in the first half of the last k-step of step j,
+// before the barrier that publishes them.  LAST: the k-step that ends the K
+// loop.
+template <class C, int U, bool LAST>
+__device__ __forceinline__ void staged_kstep(const Params &p, StagedLoader<C> &ld, char *smem,
+                                             int kt0, int nk, int m0, int n0, PipeState<C> &st)
+{
+    constexpr int S = U / C::KS, ks = U % C::KS, P = U % 2;
+    constexpr int NMF = C::MT * C::NT;
+    constexpr int NRD = C::MT + 2 * C::NT;
+    constexpr int H = NMF / 2;
+    constexpr int R = H / NRD > 0 ? H / NRD : 1;
+    if constexpr (ks + 1 < C::KS) {
+        read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off, st.b_off,
+                      st.fa[1 - P], st.fb[1 - P]);
+        mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
+        sched_interleave_reads<NRD, R>();
+    } else if constexpr (!LAST) {
+        constexpr int SN = (S + 1) % 2;
+        mfma_range<C, 0, H>(st.fa[P], st.fb[P], st.acc);
+        ld.template store<SN>(smem);                 // K step kt0+S+1 (its stage is free)
+        lds_barrier();                               // publishes it; stage S is free
+        read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
+                      st.fa[1 - P], st.fb[1 - P]);
+        if (kt0 + S + 2 < nk)
+            ld.load(p, m0, n0, kt0 + S + 2);
+        mfma_range<C, H, NMF>(st.fa[P], st.fb[P], st.acc);
+        sched_interleave_reads<NRD, R>();
+    } else {
+        mfma_range<C, 0, NMF>(st.fa[P], st.fb[P], st.acc);
+    }
+}
+
+// NS K steps (1 or 2) from kt0; LASTBODY: the K loop ends with this body.
+template <class C, int NS, bool LASTBODY, int U = 0>
+__device__ __forceinline__ void staged_body(const Params &p, StagedLoader<C> &ld, char *smem,
+                                            int kt0, int nk, int m0, int n0, PipeState<C> &st)
+{
+    if constexpr (U < NS * C::KS) {
+        staged_kstep<C, U, LASTBODY && U + 1 == NS * C::KS>(p, ld, smem, kt0, nk, m0, n0, st);
+        staged_body<C, NS, LASTBODY, U + 1>(p, ld, smem, kt0, nk, m0, n0, st);
+    }
+}
 
 template <class C, typename OutT, bool BIAS>
 __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
@@ -850,39 +924,38 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    typename C::acc_t acc[C::MT][C::NT];
+    PipeState<C> st;
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
         for (int j = 0; j < C::NT; j++)
-            acc[i][j] = typename C::acc_t{};
-
-    int a_off[C::KS], b_off[C::NT];
-    fragment_offsets<C>(wm, wn, a_off, b_off);
+            st.acc[i][j] = typename C::acc_t{};
 
     const int nk = (p.K + C::BK - 1) / C::BK;
-    StagedLoader<C> ld;
     if (nk > 0) {
+        fragment_offsets<C>(wm, wn, st.a_off, st.b_off);
+        StagedLoader<C> ld;
+        ld.init(p);
         ld.load(p, m0, n0, 0);
-        ld.store(smem);
-    }
-    lds_barrier();
-    for (int kt = 0; kt < nk; kt++) {
-        if (kt + 1 < nk)
-            ld.load(p, m0, n0, kt + 1);
-        const char *as = smem + (kt & 1) * C::STAGE_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ks++) {
-            half8 fa[C::MT], fb[C::NT];
-            read_frags<C>(as, as + C::A_BYTES, ks, a_off, b_off, fa, fb);
-            mfma_range<C, 0, C::MT * C::NT>(fa, fb, acc);
-        }
-        if (kt + 1 < nk)
-            ld.store(smem + ((kt + 1) & 1) * C::STAGE_BYTES);
+        ld.template store<0>(smem);
+        if (nk > 1)
+            ld.load(p, m0, n0, 1);
         lds_barrier();
+        read_frags<C>(a_stage<C, 0>(smem), b_stage<C, 0>(smem), 0, st.a_off, st.b_off, st.fa[0],
+                      st.fb[0]);
+        // bodies of two K steps; an odd count ends with a one-step body (the
+        // register parity of a body is even when KS is even, and a one-step
+        // body is only ever the last)
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2)
+            staged_body<C, 2, false>(p, ld, smem, kt, nk, m0, n0, st);
+        if (nk - kt == 2)
+            staged_body<C, 2, true>(p, ld, smem, kt, nk, m0, n0, st);
+        else
+            staged_body<C, 1, true>(p, ld, smem, kt, nk, m0, n0, st);
+        lds_barrier();   // every wave past its last fragment read
     }
-    // the loop ends on a barrier: LDS is free for the epilogue
-    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, acc);
+    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, st.acc);
 }
 
 // ------------------------------------------------------------ instances --

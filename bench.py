@@ -114,13 +114,16 @@ def main():
     s = stream.cuda_stream
     pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
     pbias = bias.data_ptr() if fused else None
+    op_a, op_b, lda, ldb = w["op_a"], w["op_b"], w["lda"], w["ldb"]
     cid = a.config
     if cid is None:
-        cid = tg.tg_select_config(pa, pb, pbias, pc, M, N, K, K, N, N, code)
+        cid = tg.tg_select_config(pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, op_a=op_a,
+                                  op_b=op_b)
     info = tg.tg_config_info(cid)
 
     def step():
-        st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, K, N, N, code, s)
+        st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s,
+                                    op_a=op_a, op_b=op_b)
         if st != tg.TG_SUCCESS:
             raise RuntimeError(tg.tg_status_string(st))
 
@@ -133,7 +136,8 @@ def main():
     c = rng.integers(0, N, a.samples)
     out = C.cpu().numpy()
     vals = out[r, c].astype(np.float64)
-    cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, K, N, bias=w["bias"])
+    cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, lda, ldb, bias=w["bias"], op_a=op_a,
+                               op_b=op_b)
     tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
                                         2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
                                if c_dtype == "f16" else 0.0)
@@ -170,7 +174,8 @@ def main():
         rows = 8
         while True:
             t = time.perf_counter()
-            oracle.gemm_ref(w["A"][:rows], w["B"], rows, N, K, bias=w["bias"], nthreads=threads)
+            oracle.gemm_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K, lda=lda,
+                            ldb=ldb, bias=w["bias"], nthreads=threads, op_a=op_a, op_b=op_b)
             dt = time.perf_counter() - t
             if dt >= 0.8 * a.cpu_seconds or rows >= M:
                 break
@@ -195,7 +200,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": a.workload, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
-                   "fused_bias_relu": fused, "kernel": info["name"],
+                   "fused_bias_relu": fused, "op_a": "T" if op_a else "N",
+                   "op_b": "T" if op_b else "N", "kernel": info["name"],
                    "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",

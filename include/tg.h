@@ -26,7 +26,8 @@
  * Errors: arguments are validated on the host before any device work; on an
  * error nothing is launched and C is untouched.  Execution faults surface at
  * the caller's next synchronisation.
- *   TG_ERROR_INVALID_VALUE     negative M/N/K; lda < K, ldb < N or ldc < N;
+ *   TG_ERROR_INVALID_VALUE     negative M/N/K; lda < K, ldb < N or ldc < N
+ *                              (the stored widths for tg_gemm_ex);
  *                              a NULL pointer when the call has work to do; a
  *                              NULL bias in the fused call; an unknown dtype;
  *                              a pointer not aligned to its element size; an
@@ -55,6 +56,10 @@ extern "C" {
 
 typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2 } tg_dtype;
 
+/* Operand orientation for tg_gemm_ex: TG_OP_N uses the stored matrix as is,
+ * TG_OP_T uses its transpose. */
+typedef enum { TG_OP_N = 0, TG_OP_T = 1 } tg_op;
+
 typedef enum {
     TG_SUCCESS = 0,
     TG_ERROR_INVALID_VALUE = 1,
@@ -74,6 +79,25 @@ tg_status tg_gemm_bias_relu(const void *A, const void *B, const float *bias, voi
                             int64_t M, int64_t N, int64_t K,
                             int64_t lda, int64_t ldb, int64_t ldc,
                             tg_dtype c_dtype, hipStream_t stream);
+
+/* C = op(A).op(B), or max(op(A).op(B) + bias[col], 0) when bias != NULL
+ * (overwrites C).  The operand layouts of the backward products of a linear
+ * layer (codechina.net TileLang article, section 5.1: dA = G.B^T, dB = A^T.G;
+ * xdnf.cn article, section 4.3: the layout decides the access path):
+ *   op_a == TG_OP_N: A is M x K row-major, lda >= K;
+ *   op_a == TG_OP_T: A is stored K x M row-major (element (i,k) of op(A) at
+ *                    A[k*lda + i]), lda >= M;
+ *   op_b == TG_OP_N: B is K x N row-major, ldb >= N;
+ *   op_b == TG_OP_T: B is stored N x K row-major (element (k,j) of op(B) at
+ *                    B[j*ldb + k]), ldb >= K.
+ * C is M x N row-major with ldc >= N.  Same ownership, validation and errors
+ * as tg_gemm; an op outside {TG_OP_N, TG_OP_T} is TG_ERROR_INVALID_VALUE.
+ * tg_gemm(...) equals tg_gemm_ex(TG_OP_N, TG_OP_N, A, B, NULL, C, ...). */
+tg_status tg_gemm_ex(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                     const float *bias, void *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc,
+                     tg_dtype c_dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *tg_status_string(tg_status s);
@@ -96,6 +120,7 @@ typedef struct {
                                         operands only); 0: register-staged loads
                                         with per-element bounds (any alignment) */
     int lds_bytes;                   /* LDS per workgroup */
+    int ops;                         /* orientations compiled: bit (1 << (2*op_a + op_b)) */
     const char *name;                /* static string */
 } tg_config_desc;
 
@@ -105,24 +130,24 @@ int tg_num_configs(void);
 /* Describe configuration `id`; TG_ERROR_INVALID_VALUE for an unknown id. */
 tg_status tg_config_info(int id, tg_config_desc *out);
 
-/* Whether configuration `id` can run this problem (alignment and leading-
- * dimension requirements of its load path): 1 yes, 0 no, -1 invalid args. */
-int tg_config_supports(int id, const void *A, const void *B, const float *bias,
-                       const void *C, int64_t M, int64_t N, int64_t K,
+/* Whether configuration `id` can run this problem (orientation compiled;
+ * alignment and leading-dimension requirements of its load path): 1 yes,
+ * 0 no, -1 invalid arguments.  Arguments as for tg_gemm_ex. */
+int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void *B,
+                       const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
 
 /* The configuration id the dispatcher would use for this call, or -1 for
  * invalid arguments.  Touches no device state. */
-int tg_select_config(const void *A, const void *B, const float *bias, const void *C,
-                     int64_t M, int64_t N, int64_t K,
+int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
+                     const void *C, int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
 
-/* Run one specific configuration.  bias == NULL: plain GEMM; bias != NULL:
- * fused bias + ReLU.  Same validation as tg_gemm; additionally
+/* Run one specific configuration; otherwise as tg_gemm_ex.  Additionally
  * TG_ERROR_INVALID_VALUE for an unknown id and TG_ERROR_UNSUPPORTED when the
  * configuration cannot run this problem (see tg_config_supports). */
-tg_status tg_gemm_with_config(int config_id, const void *A, const void *B,
-                              const float *bias, void *C,
+tg_status tg_gemm_with_config(int config_id, tg_op op_a, tg_op op_b, const void *A,
+                              const void *B, const float *bias, void *C,
                               int64_t M, int64_t N, int64_t K,
                               int64_t lda, int64_t ldb, int64_t ldc,
                               tg_dtype c_dtype, hipStream_t stream);

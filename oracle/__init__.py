@@ -38,6 +38,11 @@ def lib():
         L.tgref_gemm.restype = ctypes.c_int
         L.tgref_gemm_entries.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64]
         L.tgref_gemm_entries.restype = ctypes.c_int
+        I = ctypes.c_int
+        L.tgref_gemm_ex.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I]
+        L.tgref_gemm_ex.restype = I
+        L.tgref_gemm_entries_ex.argtypes = [I, I, P, P, P, P, P, I64, P, I64, I64, I64]
+        L.tgref_gemm_entries_ex.restype = I
         _lib = L
     return _lib
 
@@ -81,34 +86,39 @@ def to_f32(x):
     return out
 
 
-def gemm_ref(A, B, M, N, K, lda=None, ldb=None, bias=None, nthreads=None):
-    """Unrounded fp64 reference C (M x N, dense) for fp16-bit operands.
+def gemm_ref(A, B, M, N, K, lda=None, ldb=None, bias=None, nthreads=None, op_a=0, op_b=0):
+    """Unrounded fp64 reference C (M x N, dense) of op(A).op(B) for fp16-bit
+    operands.
 
-    A: uint16 bits, at least (M-1)*lda + K elements (row-major, leading dim lda).
-    B: uint16 bits, at least (K-1)*ldb + N elements.
+    A: uint16 bits, row-major with leading dim lda: M x K (op_a = 0) or stored
+       K x M (op_a = 1).
+    B: uint16 bits: K x N (op_b = 0) or stored N x K (op_b = 1).
     bias: None (plain GEMM) or float32[N] (fused bias + ReLU).
     """
-    lda = K if lda is None else lda
-    ldb = N if ldb is None else ldb
+    ar, ac = (K, M) if op_a else (M, K)
+    br, bc = (N, K) if op_b else (K, N)
+    lda = ac if lda is None else lda
+    ldb = bc if ldb is None else ldb
     A = _u16(A).reshape(-1)
     B = _u16(B).reshape(-1)
-    if M > 0 and K > 0:
-        assert A.size >= (M - 1) * lda + K
-    if K > 0 and N > 0:
-        assert B.size >= (K - 1) * ldb + N
+    if ar > 0 and ac > 0:
+        assert A.size >= (ar - 1) * lda + ac
+    if br > 0 and bc > 0:
+        assert B.size >= (br - 1) * ldb + bc
     if bias is not None:
         bias = np.ascontiguousarray(bias, dtype=np.float32)
         assert bias.size >= N
     C = np.zeros((M, N), np.float64)
-    rc = lib().tgref_gemm(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, lda, ldb, N,
-                          nthreads or default_threads())
+    rc = lib().tgref_gemm_ex(op_a, op_b, _ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, lda,
+                             ldb, N, nthreads or default_threads())
     if rc != 0:
-        raise ValueError("tgref_gemm rejected its arguments")
+        raise ValueError("tgref_gemm_ex rejected its arguments")
     return C
 
 
-def gemm_entries(A, B, rows, cols, K, lda, ldb, bias=None):
-    """Unrounded fp64 reference values at the listed (row, col) positions."""
+def gemm_entries(A, B, rows, cols, K, lda, ldb, bias=None, op_a=0, op_b=0):
+    """Unrounded fp64 reference values of op(A).op(B) at the listed (row, col)
+    positions."""
     A = _u16(A).reshape(-1)
     B = _u16(B).reshape(-1)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -116,10 +126,10 @@ def gemm_entries(A, B, rows, cols, K, lda, ldb, bias=None):
     if bias is not None:
         bias = np.ascontiguousarray(bias, dtype=np.float32)
     out = np.empty(rows.shape, np.float64)
-    rc = lib().tgref_gemm_entries(_ptr(A), _ptr(B), _ptr(bias), _ptr(rows), _ptr(cols),
-                                  rows.size, _ptr(out), K, lda, ldb)
+    rc = lib().tgref_gemm_entries_ex(op_a, op_b, _ptr(A), _ptr(B), _ptr(bias), _ptr(rows),
+                                     _ptr(cols), rows.size, _ptr(out), K, lda, ldb)
     if rc != 0:
-        raise ValueError("tgref_gemm_entries rejected its arguments")
+        raise ValueError("tgref_gemm_entries_ex rejected its arguments")
     return out
 
 

@@ -14,6 +14,10 @@
  * The fused variant is the one sketched in the xdnf.cn TileLang article,
  * section 4.2 (GEMM, then per element max(acc + Bias[column], 0)):
  *   C[i][j] = max(sum_k A[i][k] * B[k][j] + bias[j], 0)
+ * The _ex entry points take either operand transposed (the backward products
+ * of a linear layer, codechina.net TileLang article, section 5.1): with
+ * op_a = 1, A is stored K x M and the product uses A[k*lda + i] for element
+ * (i, k); with op_b = 1, B is stored N x K and uses B[j*ldb + k] for (k, j).
  *
  * Arithmetic, step by step:
  *  1. every fp16 bit pattern is decoded to a double exactly (subnormals too);
@@ -138,14 +142,28 @@ static void *gemm_worker(void *p)
     return NULL;
 }
 
-/* C_ref (double, row-major, leading dimension ldc) for all M x N entries.
- * bias == NULL gives the plain GEMM; otherwise the fused bias + ReLU.
- * Returns 0 on success, -1 on bad arguments or allocation failure. */
-int tgref_gemm(const uint16_t *A, const uint16_t *B, const float *bias, double *C,
-               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-               int64_t ldc, int nthreads)
+/* Element (i, k) of op(A) and (k, j) of op(B), as fp16 bits. */
+static uint16_t elem_a(const uint16_t *A, int op_a, int64_t lda, int64_t i, int64_t k)
 {
-    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N)
+    return op_a ? A[k * lda + i] : A[i * lda + k];
+}
+
+static uint16_t elem_b(const uint16_t *B, int op_b, int64_t ldb, int64_t k, int64_t j)
+{
+    return op_b ? B[j * ldb + k] : B[k * ldb + j];
+}
+
+/* C_ref (double, row-major, leading dimension ldc) for all M x N entries of
+ * op(A).op(B).  bias == NULL gives the plain GEMM; otherwise the fused
+ * bias + ReLU.  Returns 0 on success, -1 on bad arguments or allocation
+ * failure. */
+int tgref_gemm_ex(int op_a, int op_b, const uint16_t *A, const uint16_t *B, const float *bias,
+                  double *C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                  int64_t ldc, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || ldc < N || (op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return -1;
+    if (lda < (op_a ? M : K) || ldb < (op_b ? K : N))
         return -1;
     if (M == 0 || N == 0)
         return 0;
@@ -160,10 +178,10 @@ int tgref_gemm(const uint16_t *A, const uint16_t *B, const float *bias, double *
     }
     for (int64_t i = 0; i < M; i++)
         for (int64_t k = 0; k < K; k++)
-            a[i * K + k] = tgref_f16_decode(A[i * lda + k]);
+            a[i * K + k] = tgref_f16_decode(elem_a(A, op_a, lda, i, k));
     for (int64_t k = 0; k < K; k++)
         for (int64_t j = 0; j < N; j++)
-            bt[j * K + k] = tgref_f16_decode(B[k * ldb + j]);
+            bt[j * K + k] = tgref_f16_decode(elem_b(B, op_b, ldb, k, j));
 
     if (nthreads > M)
         nthreads = (int)M;
@@ -194,13 +212,21 @@ int tgref_gemm(const uint16_t *A, const uint16_t *B, const float *bias, double *
     return rc;
 }
 
-/* Selected entries only (rows[t], cols[t]) -> out[t]; for checks at sizes where
- * the full product is too slow on the CPU.  Same arithmetic as tgref_gemm. */
-int tgref_gemm_entries(const uint16_t *A, const uint16_t *B, const float *bias,
-                       const int64_t *rows, const int64_t *cols, int64_t count,
-                       double *out, int64_t K, int64_t lda, int64_t ldb)
+/* The plain row-major product: tgref_gemm_ex with both operands as stored. */
+int tgref_gemm(const uint16_t *A, const uint16_t *B, const float *bias, double *C,
+               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+               int64_t ldc, int nthreads)
 {
-    if (K < 0)
+    return tgref_gemm_ex(0, 0, A, B, bias, C, M, N, K, lda, ldb, ldc, nthreads);
+}
+
+/* Selected entries only (rows[t], cols[t]) -> out[t]; for checks at sizes where
+ * the full product is too slow on the CPU.  Same arithmetic as tgref_gemm_ex. */
+int tgref_gemm_entries_ex(int op_a, int op_b, const uint16_t *A, const uint16_t *B,
+                          const float *bias, const int64_t *rows, const int64_t *cols,
+                          int64_t count, double *out, int64_t K, int64_t lda, int64_t ldb)
+{
+    if (K < 0 || (op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
         return -1;
     double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
     double *bcol = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
@@ -212,12 +238,19 @@ int tgref_gemm_entries(const uint16_t *A, const uint16_t *B, const float *bias,
     for (int64_t t = 0; t < count; t++) {
         int64_t i = rows[t], j = cols[t];
         for (int64_t k = 0; k < K; k++) {
-            arow[k] = tgref_f16_decode(A[i * lda + k]);
-            bcol[k] = tgref_f16_decode(B[k * ldb + j]);
+            arow[k] = tgref_f16_decode(elem_a(A, op_a, lda, i, k));
+            bcol[k] = tgref_f16_decode(elem_b(B, op_b, ldb, k, j));
         }
         out[t] = dot_entry(arow, bcol, K, bias, j);
     }
     free(arow);
     free(bcol);
     return 0;
+}
+
+int tgref_gemm_entries(const uint16_t *A, const uint16_t *B, const float *bias,
+                       const int64_t *rows, const int64_t *cols, int64_t count,
+                       double *out, int64_t K, int64_t lda, int64_t ldb)
+{
+    return tgref_gemm_entries_ex(0, 0, A, B, bias, rows, cols, count, out, K, lda, ldb);
 }

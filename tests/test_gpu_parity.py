@@ -44,14 +44,19 @@ def to_dev(bits_2d, rows, cols, ld, offset_elems=0):
 
 
 def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=None,
-        a_off=0, b_off=0, c_off=0, what=""):
-    lda = K if lda is None else lda
-    ldb = N if ldb is None else ldb
+        a_off=0, b_off=0, c_off=0, what="", op_a=0, op_b=0):
+    """A, B: the stored operands (M x K or, with op_a, K x M; K x N or, with
+    op_b, N x K)."""
+    ar, ac = (K, M) if op_a else (M, K)
+    br, bc = (N, K) if op_b else (K, N)
+    lda = ac if lda is None else lda
+    ldb = bc if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    log("%s M=%d N=%d K=%d lda=%d ldb=%d ldc=%d %s bias=%s config=%s offs=%d,%d,%d" % (
-        what, M, N, K, lda, ldb, ldc, c_dtype, bias is not None, config, a_off, b_off, c_off))
-    ta, pa = to_dev(A, M, K, lda, a_off)
-    tb, pb = to_dev(B, K, N, ldb, b_off)
+    log("%s M=%d N=%d K=%d ops=%d%d lda=%d ldb=%d ldc=%d %s bias=%s config=%s offs=%d,%d,%d" % (
+        what, M, N, K, op_a, op_b, lda, ldb, ldc, c_dtype, bias is not None, config, a_off, b_off,
+        c_off))
+    ta, pa = to_dev(A, ar, ac, lda, a_off)
+    tb, pb = to_dev(B, br, bc, ldb, b_off)
     esz = 2 if c_dtype == "f16" else 4
     nc = c_off + ((M - 1) * ldc + N if M and N else 0) + 8
     if c_dtype == "f16":
@@ -66,7 +71,10 @@ def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=
     code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
     s = torch.cuda.current_stream().cuda_stream
     if config is not None:
-        st = tg.tg_gemm_with_config(config, pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
+        st = tg.tg_gemm_with_config(config, pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s,
+                                    op_a=op_a, op_b=op_b)
+    elif op_a or op_b:
+        st = tg.tg_gemm_ex(op_a, op_b, pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
     elif bias is not None:
         st = tg.tg_gemm_bias_relu(pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
     else:
@@ -85,16 +93,22 @@ def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=
 
 def full_check(A, B, M, N, K, c_dtype, integer, bias=None, **kw):
     out, _ = run(A, B, M, N, K, c_dtype, bias=bias, **kw)
-    cref = oracle.gemm_ref(A, B, M, N, K, bias=bias)
+    cref = oracle.gemm_ref(A, B, M, N, K, bias=bias, op_a=kw.get("op_a", 0),
+                           op_b=kw.get("op_b", 0))
     return parity.check(out, cref, K, c_dtype, integer, what=kw.get("what", ""))
 
 
-def supports(cid, M, N, K, lda, ldb, ldc, c_dtype, fused):
+def supports(cid, M, N, K, lda, ldb, ldc, c_dtype, fused, op_a=0, op_b=0):
     # the direct path's alignment checks only look at the pointers' low bits;
     # torch allocations are 256-byte aligned
     code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
     return tg.tg_config_supports(cid, 1 << 20, 2 << 20, (3 << 20) if fused else None, 4 << 20,
-                                 M, N, K, lda, ldb, ldc, code) == 1
+                                 M, N, K, lda, ldb, ldc, code, op_a=op_a, op_b=op_b) == 1
+
+
+def stored(A, B, op_a, op_b):
+    """Stored forms of logical operands A (M x K) and B (K x N)."""
+    return (np.ascontiguousarray(A.T) if op_a else A, np.ascontiguousarray(B.T) if op_b else B)
 
 
 # ------------------------------------------------------------ small shapes --
@@ -241,3 +255,79 @@ def test_torch_marshalling_wrapper():
     torch.cuda.synchronize()
     cref = oracle.gemm_ref(w["A"], w["B"], 256, 256, 256)
     parity.check(c.cpu().numpy(), cref, 256, "f32", False, what="wrapper")
+
+
+# ----------------------------------------------- transposed orientations --
+OPS = [(0, 1), (1, 0), (1, 1)]
+
+
+@pytest.mark.parametrize("cid", range(tg.tg_num_configs()))
+def test_transposed_small_shapes_every_config(cid):
+    info = tg.tg_config_info(cid)
+    n = 0
+    for op_a, op_b in OPS:
+        if not info["ops"] & (1 << (2 * op_a + op_b)):
+            continue
+        for (M, N, K) in SMALL + ODD:
+            for kind, c_dtype, fused in [("uniform", "f32", False), ("int", "f16", True)]:
+                lda = M if op_a else K
+                ldb = K if op_b else N
+                if not supports(cid, M, N, K, lda, ldb, N, c_dtype, fused, op_a, op_b):
+                    continue
+                A, B = gen.operands(M, N, K, kind, 2000 + M + N + K)
+                As, Bs = stored(A, B, op_a, op_b)
+                bias = gen.bias_vector(N, 9, integer=(kind == "int")) if fused else None
+                full_check(As, Bs, M, N, K, c_dtype, kind == "int", bias=bias, config=cid,
+                           op_a=op_a, op_b=op_b, what="%s ops=%d%d" % (info["name"], op_a, op_b))
+                n += 1
+    if info["ops"] != 1:
+        assert n > 0
+
+
+@pytest.mark.parametrize("op_a,op_b", OPS)
+def test_transposed_padded_and_unaligned(op_a, op_b):
+    M, N, K = 129, 257, 131
+    A, B = gen.operands(M, N, K, "uniform", 91)
+    As, Bs = stored(A, B, op_a, op_b)
+    bias = gen.bias_vector(N, 92)
+    ac = M if op_a else K
+    bc = K if op_b else N
+    full_check(As, Bs, M, N, K, "f16", False, bias=bias, lda=ac + 3, ldb=bc + 5, ldc=N + 1,
+               a_off=1, b_off=3, c_off=1, op_a=op_a, op_b=op_b, what="T-padded")
+    Ai, Bi = gen.operands(M, N, K, "int", 93)
+    Ais, Bis = stored(Ai, Bi, op_a, op_b)
+    full_check(Ais, Bis, M, N, K, "f32", True, lda=ac + 8, ldb=bc + 8, op_a=op_a, op_b=op_b,
+               what="T-padded-int")
+
+
+@pytest.mark.parametrize("op_a,op_b", OPS)
+@pytest.mark.parametrize("integer", [False, True])
+def test_transposed_large_sampled(op_a, op_b, integer):
+    # the backward products of the 4096 x 11008 x 4096 layer shape, through
+    # the dispatcher: M = N = 4096, K = 11008 (dA = G.B^T-like, dB = A^T.G-like)
+    M, N, K = 4096, 4096, 11008
+    kind = "int" if integer else "normal_scaled"
+    A, B = gen.operands(M, N, K, kind, 95 + 2 * op_a + op_b)
+    As, Bs = stored(A, B, op_a, op_b)
+    out, _ = run(As, Bs, M, N, K, "f16", op_a=op_a, op_b=op_b, what="T-large")
+    cid = tg.tg_select_config(1 << 20, 2 << 20, None, 4 << 20, M, N, K,
+                              M if op_a else K, K if op_b else N, N, tg.TG_DTYPE_F16,
+                              op_a=op_a, op_b=op_b)
+    info = tg.tg_config_info(cid)
+    r, c = sample_positions(M, N, info["block_m"], info["block_n"], 3000, 21)
+    cref = oracle.gemm_entries(As, Bs, r, c, K, M if op_a else K, K if op_b else N,
+                               op_a=op_a, op_b=op_b)
+    rep = parity.check(out[r, c], cref, K, "f16", integer, what="T-large")
+    assert not np.any(np.isnan(parity.gpu_values(out, "f16")))
+    log("T-large ops=%d%d integer=%s config=%s %s" % (op_a, op_b, integer, info["name"], rep))
+
+
+def test_torch_wrapper_takes_transposed_views():
+    M, N, K = 192, 320, 256
+    A, B = gen.operands(M, N, K, "uniform", 97)
+    a = torch.from_numpy(np.ascontiguousarray(A.T).view(np.float16)).cuda().t()   # (M, K) view
+    b = torch.from_numpy(np.ascontiguousarray(B.T).view(np.float16)).cuda().t()   # (K, N) view
+    assert a.stride(0) == 1 and b.stride(0) == 1
+    c = tg.gemm(a, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    parity.check(c.cpu().numpy(), oracle.gemm_ref(A, B, M, N, K), K, "f32", False, what="T-view")

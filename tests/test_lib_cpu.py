@@ -120,3 +120,35 @@ def test_dispatch_picks_a_supporting_config(M, N, K, lda, ldb, fused, direct):
     assert 0 <= cid < tg.tg_num_configs()
     assert tg.tg_config_supports(cid, PA, PB, bias, PC, M, N, K, lda, ldb, N, F16) == 1
     assert bool(tg.tg_config_info(cid)["direct_lds"]) == direct
+
+
+def test_gemm_ex_validation_without_gpu():
+    T, Nop = tg.TG_OP_T, tg.TG_OP_N
+    ex = lambda oa, ob, M, N, K, lda, ldb, ldc, A=PA: tg.tg_gemm_ex(
+        oa, ob, A, PB, None, PC, M, N, K, lda, ldb, ldc, F32, 0)
+    assert ex(2, Nop, 8, 8, 8, 8, 8, 8) == tg.TG_ERROR_INVALID_VALUE
+    assert ex(Nop, -1, 8, 8, 8, 8, 8, 8) == tg.TG_ERROR_INVALID_VALUE
+    # stored widths: A^T is K x M (lda >= M), B^T is N x K (ldb >= K)
+    assert ex(T, Nop, 16, 8, 4, 8, 8, 8) == tg.TG_ERROR_INVALID_VALUE
+    assert ex(Nop, T, 8, 16, 32, 32, 16, 16) == tg.TG_ERROR_INVALID_VALUE
+    assert ex(T, T, 0, 16, 32, 1, 32, 16) == tg.TG_SUCCESS        # M = 0: no-op
+    assert ex(T, Nop, 8, 8, 8, 8, 8, 8, A=PA + 1) == tg.TG_ERROR_INVALID_VALUE
+
+
+def test_orientation_support_follows_the_config_table():
+    args = (PA, PB, None, PC, 1024, 1024, 1024, 1024, 1024, 1024, F32)
+    for c in tg.configs():
+        for op_a in (0, 1):
+            for op_b in (0, 1):
+                want = 1 if c["ops"] & (1 << (2 * op_a + op_b)) else 0
+                assert tg.tg_config_supports(c["id"], *args, op_a=op_a, op_b=op_b) == want
+    for op_a in (0, 1):
+        for op_b in (0, 1):
+            cid = tg.tg_select_config(*args, op_a=op_a, op_b=op_b)
+            assert tg.tg_config_supports(cid, *args, op_a=op_a, op_b=op_b) == 1
+    # direct path with A^T needs M % 8 == 0 (A's stored rows run along M)
+    direct_all = [c["id"] for c in tg.configs() if c["direct_lds"] and c["ops"] == 15][0]
+    assert tg.tg_config_supports(direct_all, PA, PB, None, PC, 1020, 1024, 1024, 1024, 1024,
+                                 1024, F32, op_a=1) == 0
+    assert tg.tg_config_supports(direct_all, PA, PB, None, PC, 1024, 1024, 1020, 1024, 1024,
+                                 1024, F32, op_a=1) == 1

@@ -224,3 +224,57 @@ def test_integer_inputs_are_exact_at_large_K():
     Ai = A.view(np.float16).astype(np.int64)
     Bi = B.view(np.float16).astype(np.int64)
     assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+
+
+# ------------------------------------------------------- transposed operands
+
+def _stored(logical, op, pad, seed):
+    """Stored array for a logical operand: itself (op 0) or its transpose
+    (op 1), by numpy, in rows padded with NaN to width + pad."""
+    st = np.ascontiguousarray(logical.T) if op else logical
+    rows, cols = st.shape
+    out = np.full((rows, cols + pad), 0x7E00, np.uint16)
+    out[:, :cols] = st
+    return out, cols + pad
+
+
+def test_transposed_operands_match_numpy_transposes():
+    M, N, K = 13, 22, 37
+    A, B = gen.operands(M, N, K, "uniform", 40)
+    bias = gen.bias_vector(N, 41)
+    for op_a, op_b, b in itertools.product((0, 1), (0, 1), (None, bias)):
+        As, lda = _stored(A, op_a, 3, 0)
+        Bs, ldb = _stored(B, op_b, 5, 0)
+        want = oracle.gemm_ref(A, B, M, N, K, bias=b)
+        got = oracle.gemm_ref(As, Bs, M, N, K, lda=lda, ldb=ldb, bias=b, op_a=op_a, op_b=op_b)
+        assert np.array_equal(got, want), (op_a, op_b)
+        r = np.array([0, M - 1, 5, 7])
+        c = np.array([0, N - 1, 11, 3])
+        ent = oracle.gemm_entries(As, Bs, r, c, K, lda, ldb, bias=b, op_a=op_a, op_b=op_b)
+        assert np.array_equal(ent, want[r, c]), (op_a, op_b)
+
+
+@pytest.mark.parametrize("M,N,K,op_a,op_b", [(5, 3, 7, 1, 0), (5, 3, 7, 0, 1), (5, 3, 7, 1, 1),
+                                             (4, 6, 2, 1, 1)])
+def test_transposed_brute_force_exact(M, N, K, op_a, op_b):
+    # stored operands drawn directly; the logical op(A), op(B) come from numpy
+    sa = (K, M) if op_a else (M, K)
+    sb = (N, K) if op_b else (K, N)
+    As = gen.to_f16_bits(gen.uniform_pm1(60 + M, sa[0] * sa[1])).reshape(sa)
+    Bs = gen.to_f16_bits(gen.uniform_pm1(61 + N, sb[0] * sb[1])).reshape(sb)
+    A = np.ascontiguousarray(As.T) if op_a else As
+    B = np.ascontiguousarray(Bs.T) if op_b else Bs
+    C = oracle.gemm_ref(As, Bs, M, N, K, op_a=op_a, op_b=op_b)
+    ex = _brute(A, B, M, N, K)
+    for i in range(M):
+        for j in range(N):
+            assert C[i, j] == float(ex[i][j]), (i, j)
+
+
+def test_transposed_rejects_short_leading_dimensions():
+    # a stored K x M operand needs lda >= M, a stored N x K one ldb >= K
+    A = np.zeros(64, np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_ref(A, A, 4, 2, 2, lda=2, ldb=2, op_a=1)
+    with pytest.raises(ValueError):
+        oracle.gemm_ref(A, A, 2, 4, 3, lda=3, ldb=2, op_b=1)

@@ -19,10 +19,15 @@ MUTANTS = {
     "bias_wrong_index": ("s = s + (double)bias[j];", "s = s + (double)bias[0];"),
     "no_relu": ("s = (s > 0.0) ? s : 0.0;", "s = s;"),
     "relu_inverted": ("s = (s > 0.0) ? s : 0.0;", "s = (s < 0.0) ? s : 0.0;"),
-    "columns_of_B_swapped": ("bt[j * K + k] = tgref_f16_decode(B[k * ldb + j]);",
-                             "bt[j * K + k] = tgref_f16_decode(B[k * ldb + (N - 1 - j)]);"),
-    "lda_ignored": ("a[i * K + k] = tgref_f16_decode(A[i * lda + k]);",
-                    "a[i * K + k] = tgref_f16_decode(A[i * K + k]);"),
+    "columns_of_B_swapped": ("bt[j * K + k] = tgref_f16_decode(elem_b(B, op_b, ldb, k, j));",
+                             "bt[j * K + k] = tgref_f16_decode(elem_b(B, op_b, ldb, k, N - 1 - j));"),
+    "lda_ignored": ("a[i * K + k] = tgref_f16_decode(elem_a(A, op_a, lda, i, k));",
+                    "a[i * K + k] = tgref_f16_decode(elem_a(A, op_a, K, i, k));"),
+    "transposed_a_not_transposed": ("return op_a ? A[k * lda + i] : A[i * lda + k];",
+                                    "return op_a ? A[i * lda + k] : A[i * lda + k];"),
+    "transposed_b_ignores_ldb": (
+        "bt[j * K + k] = tgref_f16_decode(elem_b(B, op_b, ldb, k, j));",
+        "bt[j * K + k] = tgref_f16_decode(elem_b(B, op_b, op_b ? K : ldb, k, j));"),
     "round_half_up": ("double n = rint(a / q);", "double n = floor(a / q + 0.5);"),
     "subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     "float_accumulator": ("double s = 0.0;\n    for (int64_t k = 0; k < K; k++)",
@@ -38,6 +43,8 @@ def _pin_suite():
     yield lambda: pins.test_K0_gives_zero_or_relu_bias()
     yield pins.test_padded_leading_dimensions_ignore_padding
     yield pins.test_integer_inputs_are_exact_at_large_K
+    yield pins.test_transposed_operands_match_numpy_transposes
+    yield lambda: pins.test_transposed_brute_force_exact(5, 3, 7, 1, 1)
     for M, N, K in [(7, 5, 3), (4, 4, 4)]:
         for kind in ("uniform", "normal_scaled"):
             for fused in (False, True):
@@ -59,7 +66,8 @@ def test_pins_catch_mutant(name, tmp_path):
     real = oracle.lib()
     mut = ctypes.CDLL(str(so))
     for fn in ("tgref_f16_decode", "tgref_f16_encode", "tgref_decode_array", "tgref_to_f32",
-               "tgref_to_f16", "tgref_gemm", "tgref_gemm_entries"):
+               "tgref_to_f16", "tgref_gemm", "tgref_gemm_entries", "tgref_gemm_ex",
+               "tgref_gemm_entries_ex"):
         getattr(mut, fn).argtypes = getattr(real, fn).argtypes
         getattr(mut, fn).restype = getattr(real, fn).restype
     caught = []

@@ -92,6 +92,12 @@ WORKLOADS = {
                                  c_dtype="f16", bias_seed=4),
     "ragged3001x5003x1031": dict(M=3001, N=5003, K=1031, kind="uniform", seed=5, fused=False,
                                  c_dtype="f32"),
+    # the 8192^3 problem with transposed operands (the backward products of a
+    # linear layer); the stored operand is the transpose of the same values
+    "sq8192_nt": dict(M=8192, N=8192, K=8192, kind="normal_scaled", seed=2, fused=False,
+                      c_dtype="f16", op_b=1),
+    "sq8192_tn": dict(M=8192, N=8192, K=8192, kind="normal_scaled", seed=2, fused=False,
+                      c_dtype="f16", op_a=1),
 }
 
 
@@ -120,12 +126,19 @@ def bias_vector(N, seed, integer=False):
 
 def workload(name, integer=False):
     """Inputs of a named workload; integer=True draws A, B (and the bias) from
-    {-4..4} with the same seeds, for the bit-exact check."""
+    {-4..4} with the same seeds, for the bit-exact check.  A and B are the
+    stored arrays (transposed for workloads with op_a / op_b set)."""
     w = dict(WORKLOADS[name])
     kind = "int" if integer else w["kind"]
     A, B = operands(w["M"], w["N"], w["K"], kind, w["seed"])
+    op_a, op_b = w.get("op_a", 0), w.get("op_b", 0)
+    if op_a:
+        A = np.ascontiguousarray(A.T)   # stored K x M
+    if op_b:
+        B = np.ascontiguousarray(B.T)   # stored N x K
     bias = None
     if w["fused"]:
         bias = bias_vector(w["N"], w["bias_seed"], integer=integer)
     return dict(name=name, M=w["M"], N=w["N"], K=w["K"], A=A, B=B, bias=bias,
-                c_dtype=w["c_dtype"], integer=integer)
+                c_dtype=w["c_dtype"], integer=integer, op_a=op_a, op_b=op_b,
+                lda=A.shape[1], ldb=B.shape[1])

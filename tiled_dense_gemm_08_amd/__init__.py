@@ -22,8 +22,11 @@ TG_ERROR_NOT_DEVICE_MEMORY = 2
 TG_ERROR_UNSUPPORTED = 3
 TG_ERROR_LAUNCH = 4
 
+TG_OP_N = 0
+TG_OP_T = 1
+
 # every function declared in include/tg.h
-EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_status_string", "tg_num_configs",
+EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_version")
 
@@ -38,7 +41,7 @@ class ConfigDesc(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("mfma", ctypes.c_int), ("direct_lds", ctypes.c_int),
-                ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p)]
+                ("lds_bytes", ctypes.c_int), ("ops", ctypes.c_int), ("name", ctypes.c_char_p)]
 
 
 def _load():
@@ -60,7 +63,9 @@ def _load():
     L.tg_gemm.restype = I
     L.tg_gemm_bias_relu.argtypes = [P, P, P, P] + gemm_args
     L.tg_gemm_bias_relu.restype = I
-    L.tg_gemm_with_config.argtypes = [I, P, P, P, P] + gemm_args
+    L.tg_gemm_ex.argtypes = [I, I, P, P, P, P] + gemm_args
+    L.tg_gemm_ex.restype = I
+    L.tg_gemm_with_config.argtypes = [I, I, I, P, P, P, P] + gemm_args
     L.tg_gemm_with_config.restype = I
     L.tg_status_string.argtypes = [I]
     L.tg_status_string.restype = ctypes.c_char_p
@@ -69,9 +74,9 @@ def _load():
     L.tg_config_info.argtypes = [I, ctypes.POINTER(ConfigDesc)]
     L.tg_config_info.restype = I
     shape_args = [P, P, P, P, I64, I64, I64, I64, I64, I64, I]
-    L.tg_config_supports.argtypes = [I] + shape_args
+    L.tg_config_supports.argtypes = [I, I, I] + shape_args
     L.tg_config_supports.restype = I
-    L.tg_select_config.argtypes = shape_args
+    L.tg_select_config.argtypes = [I, I] + shape_args
     L.tg_select_config.restype = I
     L.tg_version.argtypes = []
     L.tg_version.restype = ctypes.c_char_p
@@ -90,9 +95,15 @@ def tg_gemm_bias_relu(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
     return lib.tg_gemm_bias_relu(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream or None)
 
 
-def tg_gemm_with_config(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
-    return lib.tg_gemm_with_config(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
-                                   stream or None)
+def tg_gemm_ex(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0):
+    return lib.tg_gemm_ex(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                          stream or None)
+
+
+def tg_gemm_with_config(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, stream=0,
+                        op_a=TG_OP_N, op_b=TG_OP_N):
+    return lib.tg_gemm_with_config(config_id, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
+                                   c_dtype, stream or None)
 
 
 def tg_status_string(status):
@@ -111,12 +122,15 @@ def tg_config_info(config_id):
     return {f: (getattr(d, f).decode() if f == "name" else getattr(d, f)) for f, _ in d._fields_}
 
 
-def tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype):
-    return lib.tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+def tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                       op_a=TG_OP_N, op_b=TG_OP_N):
+    return lib.tg_config_supports(config_id, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
+                                  c_dtype)
 
 
-def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype):
-    return lib.tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_N,
+                     op_b=TG_OP_N):
+    return lib.tg_select_config(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
 
 
 def tg_version():
@@ -138,7 +152,7 @@ def _dtype_code(t):
 
 
 def _matrix(t, name):
-    import torch
+    """Pointer and leading dimension of a row-major 2-D tensor."""
     if t.dim() != 2:
         raise ValueError("%s must be 2-D" % name)
     if t.size(0) > 1 and t.stride(1) != 1 or t.size(1) > 1 and t.stride(1) != 1:
@@ -147,10 +161,27 @@ def _matrix(t, name):
     return t.data_ptr(), max(ld, t.size(1))
 
 
+def _operand(t, name):
+    """Pointer, leading dimension and orientation of an operand tensor: a
+    row-major tensor is used as stored (TG_OP_N); a tensor with unit row
+    stride (a transposed view of a row-major array) is passed as the stored
+    array with TG_OP_T."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.stride(1) == 1 or t.size(1) == 1:
+        p, ld = _matrix(t, name)
+        return p, ld, TG_OP_N
+    if t.stride(0) == 1 or t.size(0) == 1:
+        p, ld = _matrix(t.t(), name)
+        return p, ld, TG_OP_T
+    raise ValueError("%s must be row-major or a transposed row-major view" % name)
+
+
 def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
     """C = A.B (or max(A.B + bias, 0) when bias is given) with libtg.
 
-    a: (M, K) float16, b: (K, N) float16, both row-major on the current device;
+    a: (M, K) float16, b: (K, N) float16 on the current device, each row-major
+    or a transposed view of a row-major array (passed with TG_OP_T, no copy);
     out: optional preallocated (M, N) float16/float32 row-major tensor.
     config: None (dispatcher's choice) or a configuration id.
     """
@@ -165,8 +196,8 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
         out = torch.empty((M, N), dtype=out_dtype or torch.float16, device=a.device)
     if tuple(out.shape) != (M, N):
         raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (M, N)))
-    pa, lda = _matrix(a, "A")
-    pb, ldb = _matrix(b, "B")
+    pa, lda, op_a = _operand(a, "A")
+    pb, ldb, op_b = _operand(b, "B")
     pc, ldc = _matrix(out, "C")
     code = _dtype_code(out.dtype)
     pbias = 0
@@ -177,7 +208,9 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
     s = (stream if stream is not None else torch.cuda.current_stream(a.device)).cuda_stream
     if config is not None:
         st = tg_gemm_with_config(config, pa, pb, pbias or None, pc, M, N, K, lda, ldb, ldc,
-                                 code, s)
+                                 code, s, op_a=op_a, op_b=op_b)
+    elif op_a or op_b:
+        st = tg_gemm_ex(op_a, op_b, pa, pb, pbias or None, pc, M, N, K, lda, ldb, ldc, code, s)
     elif bias is not None:
         st = tg_gemm_bias_relu(pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s)
     else:

@@ -33,6 +33,7 @@ struct Problem {
     int64_t M, N, K, lda, ldb, ldc;
     tg_dtype c_dtype;
     bool fused;
+    int op_a, op_b;   // 1: A stored K x M / B stored N x K
 };
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -42,14 +43,22 @@ int64_t span_elems(int64_t rows, int64_t cols, int64_t ld)
     return (rows == 0 || cols == 0) ? 0 : (rows - 1) * ld + cols;
 }
 
+// Stored shape of A and B: rows x cols of the row-major arrays.
+int64_t a_rows(const Problem &p) { return p.op_a ? p.K : p.M; }
+int64_t a_cols(const Problem &p) { return p.op_a ? p.M : p.K; }
+int64_t b_rows(const Problem &p) { return p.op_b ? p.N : p.K; }
+int64_t b_cols(const Problem &p) { return p.op_b ? p.K : p.N; }
+
 // Pure argument checks (no HIP calls).
 tg_status validate(const Problem &p)
 {
     if (p.c_dtype != TG_DTYPE_F16 && p.c_dtype != TG_DTYPE_F32)
         return TG_ERROR_INVALID_VALUE;
+    if ((p.op_a != TG_OP_N && p.op_a != TG_OP_T) || (p.op_b != TG_OP_N && p.op_b != TG_OP_T))
+        return TG_ERROR_INVALID_VALUE;
     if (p.M < 0 || p.N < 0 || p.K < 0)
         return TG_ERROR_INVALID_VALUE;
-    if (p.lda < p.K || p.ldb < p.N || p.ldc < p.N)
+    if (p.lda < a_cols(p) || p.ldb < b_cols(p) || p.ldc < p.N)
         return TG_ERROR_INVALID_VALUE;
     if (p.lda < 0 || p.ldb < 0 || p.ldc < 0)
         return TG_ERROR_INVALID_VALUE;
@@ -71,22 +80,48 @@ tg_status validate(const Problem &p)
     return TG_SUCCESS;
 }
 
-// Whether a configuration's load path can serve this problem.
+// One operand as the kernels see it: k-major when its stored rows run along M
+// or N (A, or B stored N x K), mn-major when they run along K.
+struct OperandShape {
+    bool kmaj;
+    int64_t x;     // M or N
+    int64_t ld;
+    int tile;      // block_m or block_n
+};
+
+bool operand_direct_ok(const OperandShape &o, const Problem &p, int bk)
+{
+    if (o.ld % 8 || (o.kmaj ? p.K % 8 : o.x % 8))
+        return false;
+    // lane offsets of rows past the edge (x + tile rows of a k-major operand,
+    // block_k + 1 rows of an mn-major one) must stay below 2^32 so that the
+    // range check sees them
+    if (o.kmaj)
+        return 2 * (o.x + o.tile) * o.ld < (int64_t(1) << 32);
+    return 2 * (bk + 1) * o.ld < kMaxSpan;
+}
+
+bool operand_staged_ok(const OperandShape &o, int bk)
+{
+    return int64_t(o.kmaj ? o.tile : bk) * o.ld < kMaxSpan;   // in-tile offsets fit 31 bits
+}
+
+// Whether a configuration can serve this problem (orientation compiled, and
+// the alignment and size requirements of its load path).
 bool supports(const KernelConfig &c, const Problem &p)
 {
-    if (!c.direct)   // register-staged path: any alignment; in-tile offsets fit 31 bits
-        return int64_t(c.bm) * p.lda < kMaxSpan && int64_t(c.bk) * p.ldb < kMaxSpan;
+    if (!(c.ops & (1 << (2 * p.op_a + p.op_b))))
+        return false;
+    const OperandShape a{p.op_a == 0, p.M, p.lda, c.bm};
+    const OperandShape b{p.op_b == 1, p.N, p.ldb, c.bn};
+    if (!c.direct)
+        return operand_staged_ok(a, c.bk) && operand_staged_ok(b, c.bk);
     if (!aligned(p.A, 16) || !aligned(p.B, 16))
         return false;
-    if (p.lda % 8 || p.ldb % 8 || p.K % 8 || p.N % 8)
+    if (2 * span_elems(a_rows(p), a_cols(p), p.lda) >= kMaxSpan ||
+        2 * span_elems(b_rows(p), b_cols(p), p.ldb) >= kMaxSpan)
         return false;
-    if (2 * span_elems(p.M, p.K, p.lda) >= kMaxSpan || 2 * span_elems(p.K, p.N, p.ldb) >= kMaxSpan)
-        return false;
-    // lane offsets of rows past the edge (M + block_m rows of A, block_k + 1
-    // rows of B) must stay below 2^32 so that the range check sees them
-    if (2 * (p.M + c.bm) * p.lda >= (int64_t(1) << 32) || 2 * (c.bk + 1) * p.ldb >= kMaxSpan)
-        return false;
-    return true;
+    return operand_direct_ok(a, p, c.bk) && operand_direct_ok(b, p, c.bk);
 }
 
 // ---- configuration table (shape class -> config id), chosen offline ------
@@ -181,8 +216,10 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     k.tiles_m = (int)((p.M + cfg.bm - 1) / cfg.bm);
     k.tiles_n = (int)((p.N + cfg.bn - 1) / cfg.bn);
     k.group_m = 8;
-    const int64_t a_span = 2 * span_elems(p.M, p.K, p.lda);
-    const int64_t b_span = 2 * span_elems(p.K, p.N, p.ldb);
+    k.trans_a = p.op_a;
+    k.trans_b = p.op_b;
+    const int64_t a_span = 2 * span_elems(a_rows(p), a_cols(p), p.lda);
+    const int64_t b_span = 2 * span_elems(b_rows(p), b_cols(p), p.ldb);
     k.a_bytes = (uint32_t)(a_span < kMaxSpan ? a_span : 0);
     k.b_bytes = (uint32_t)(b_span < kMaxSpan ? b_span : 0);
     const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
@@ -207,7 +244,8 @@ extern "C" {
 tg_status tg_gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                   int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype, hipStream_t stream)
 {
-    return run(-1, Problem{A, B, nullptr, C, M, N, K, lda, ldb, ldc, c_dtype, false}, stream);
+    return run(-1, Problem{A, B, nullptr, C, M, N, K, lda, ldb, ldc, c_dtype, false, 0, 0},
+               stream);
 }
 
 tg_status tg_gemm_bias_relu(const void *A, const void *B, const float *bias, void *C,
@@ -216,17 +254,27 @@ tg_status tg_gemm_bias_relu(const void *A, const void *B, const float *bias, voi
 {
     if (bias == nullptr)
         return TG_ERROR_INVALID_VALUE;
-    return run(-1, Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, true}, stream);
+    return run(-1, Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, true, 0, 0}, stream);
 }
 
-tg_status tg_gemm_with_config(int config_id, const void *A, const void *B, const float *bias,
-                              void *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                              int64_t ldb, int64_t ldc, tg_dtype c_dtype, hipStream_t stream)
+tg_status tg_gemm_ex(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
+                     void *C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t ldc, tg_dtype c_dtype, hipStream_t stream)
+{
+    return run(-1,
+               Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr, op_a, op_b},
+               stream);
+}
+
+tg_status tg_gemm_with_config(int config_id, tg_op op_a, tg_op op_b, const void *A,
+                              const void *B, const float *bias, void *C, int64_t M, int64_t N,
+                              int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                              tg_dtype c_dtype, hipStream_t stream)
 {
     if (config_id < 0 || config_id >= kNumConfigs)
         return TG_ERROR_INVALID_VALUE;
     return run(config_id,
-               Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr},
+               Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr, op_a, op_b},
                stream);
 }
 
@@ -259,25 +307,28 @@ tg_status tg_config_info(int id, tg_config_desc *out)
     out->mfma = c.mfma;
     out->direct_lds = c.direct;
     out->lds_bytes = c.lds_bytes;
+    out->ops = c.ops;
     out->name = c.name;
     return TG_SUCCESS;
 }
 
-int tg_config_supports(int id, const void *A, const void *B, const float *bias, const void *C,
-                       int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                       tg_dtype c_dtype)
+int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void *B,
+                       const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype)
 {
-    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr};
+    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
+              op_a, op_b};
     if (id < 0 || id >= kNumConfigs || validate(p) != TG_SUCCESS)
         return -1;
     return supports(kConfigs[id], p) ? 1 : 0;
 }
 
-int tg_select_config(const void *A, const void *B, const float *bias, const void *C, int64_t M,
-                     int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                     tg_dtype c_dtype)
+int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
+                     const void *C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t ldc, tg_dtype c_dtype)
 {
-    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr};
+    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
+              op_a, op_b};
     if (validate(p) != TG_SUCCESS)
         return -1;
     return choose(p);

@@ -19,6 +19,7 @@ struct Params {
     int lda, ldb, ldc;
     int tiles_m, tiles_n, group_m;
     uint32_t a_bytes, b_bytes;
+    int trans_a, trans_b;   // A stored K x M / B stored N x K
     int vec_store;   // C rows allow 4-element vector stores (alignment)
     int line_store;  // C rows allow 16-byte stores: staged, full-line epilogue
     int vec_bias;    // bias allows 16-byte loads
@@ -32,6 +33,7 @@ struct KernelConfig {
     int mfma;         // MFMA block edge: 16 (16x16x32) or 32 (32x32x16)
     int direct;       // 1: direct global->LDS path, 0: register-staged path
     int lds_bytes;
+    int ops;          // bit 2*trans_a + trans_b set: that orientation is compiled
     const char *name;
 };
 

@@ -130,9 +130,17 @@ template <int MI> struct AccT;
 template <> struct AccT<16> { typedef float4v type; };
 template <> struct AccT<32> { typedef float16v type; };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_, int SCHED_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_, int SCHED_,
+          int TA_ = 0, int TB_ = 0>
 struct Cfg {
     static constexpr int SCHED = SCHED_;   // copy issue: 0 burst after the barrier, 1 spread
+    // Operand orientation: TA = 1 when A is stored K x M (the product uses its
+    // transpose), TB = 1 when B is stored N x K.  The LDS tile of an operand is
+    // k-major (rows of BK fp16, k contiguous, read with ds_read_b128) when its
+    // rows run along M or N in memory, and mn-major (BK rows, M or N
+    // contiguous, read with the transpose read) otherwise.
+    static constexpr bool TA = TA_ != 0, TB = TB_ != 0;
+    static constexpr bool A_KMAJ = !TA, B_KMAJ = TB;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WM_, WAVES_N = WN_;
     static constexpr int STAGES = STAGES_;
@@ -152,66 +160,102 @@ struct Cfg {
     static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;  // per thread per K step
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
-    static constexpr int A_ROWS_PER_LOAD = 1024 / (BK * 2);
-    static constexpr int B_ROWS_PER_LOAD = 1024 / (BN * 2);
+    // rows of the LDS tile that one copy instruction (1 KiB) fills
+    static constexpr int A_ROWS_PER_LOAD = A_KMAJ ? 1024 / (BK * 2) : 1024 / (BM * 2);
+    static constexpr int B_ROWS_PER_LOAD = B_KMAJ ? 1024 / (BK * 2) : 1024 / (BN * 2);
+    // fragment offset registers: one per k-step (k-major) or per block (mn-major)
+    static constexpr int A_NOFF = A_KMAJ ? BK / (512 / MI_) : BM / WM_ / MI_;
+    static constexpr int B_NOFF = B_KMAJ ? BK / (512 / MI_) : BN / WN_ / MI_;
     typedef typename AccT<MI>::type acc_t;
     static_assert(MI == 16 || MI == 32, "MI");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(TM % MI == 0 && TN % MI == 0, "wave tile");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "copy split");
-    static_assert(BN * 2 <= 1024 && BN % 64 == 0, "BN");
+    static_assert(BN * 2 <= 1024 && BN % 64 == 0 && BM * 2 <= 1024 && BM % 64 == 0, "BM, BN");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // ------------------------------------------------------------- fragments --
-// Per-lane LDS byte offsets of the fragment reads (stage-relative).
-//  A (MFMA second source): lane l holds row l % MI, k = 8 (l / MI) .. +7 of
-//    the k-step: one ds_read_b128.  a_off[ks] + mt * MI * BK * 2 for block mt.
-//  B (MFMA first source): lane l holds column l % MI, the same 8 k.  Two
-//    transpose reads of 4 k each: lane L = 16 G + 4 e + q reads row
-//    k = 8 (L / MI) + e (+4 for the second read, + KI per k-step) at columns
-//    16 ((L % MI) / 16) + 4 q .. +3 of the block; the hardware hands lane
-//    16 G + j the 4 rows' column j.  b_off[nt] for block nt.
-template <class C>
-__device__ __forceinline__ void fragment_offsets(int wm, int wn, int (&a_off)[C::KS],
-                                                 int (&b_off)[C::NT])
+// Per-lane LDS byte offsets of the fragment reads (stage-relative).  An MFMA
+// operand fragment gives lane l the 8 k = 8 (l / MI) .. +7 of the k-step for
+// row (A, second source) or column (B, first source) l % MI of its block.
+//  k-major tile (R rows of BK): one ds_read_b128 per block at
+//    off[ks] + block * MI * BK * 2.
+//  mn-major tile (BK rows of R): two transpose reads of 4 k each: lane
+//    L = 16 G + 4 e + q reads row k = 8 (L / MI) + e (+4 for the second read,
+//    + KI per k-step) at positions 16 ((L % MI) / 16) + 4 q .. +3 of the
+//    block; the hardware hands lane 16 G + j the 4 rows' position j.
+//    off[block] + ks * KI * R * 2.
+template <class C, int NOFF>
+__device__ __forceinline__ void kmajor_offsets(int base, int (&off)[NOFF])
 {
     const int lane = threadIdx.x & 63;
-    const int kgroup = lane / C::MI;
+    const int row = base + lane % C::MI;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ks++) {
-        const int row = wm * C::TM + lane % C::MI;
-        const int chunk = ks * (C::KI / 8) + kgroup;
-        a_off[ks] = row * C::BK * 2 + ((chunk ^ swz_a<C::BK>(row)) * 16);
+    for (int ks = 0; ks < NOFF; ks++) {
+        const int chunk = ks * (C::KI / 8) + lane / C::MI;
+        off[ks] = row * C::BK * 2 + ((chunk ^ swz_a<C::BK>(row)) * 16);
     }
+}
+
+template <class C, int R, int NOFF>
+__device__ __forceinline__ void mnmajor_offsets(int base, int (&off)[NOFF])
+{
+    const int lane = threadIdx.x & 63;
     const int i = lane & 15;
     const int e = i >> 2, q = i & 3;
-    const int k = 8 * kgroup + e;
+    const int k = 8 * (lane / C::MI) + e;
     const int sub = (lane % C::MI) >> 4;
 #pragma unroll
-    for (int nt = 0; nt < C::NT; nt++) {
-        const int col = wn * C::TN + nt * C::MI + sub * 16 + 4 * q;
-        b_off[nt] = k * C::BN * 2 + (((col >> 3) ^ swz_b<C::BN>(k)) * 16) + (col & 7) * 2;
+    for (int b = 0; b < NOFF; b++) {
+        const int col = base + b * C::MI + sub * 16 + 4 * q;
+        off[b] = k * R * 2 + (((col >> 3) ^ swz_b<R>(k)) * 16) + (col & 7) * 2;
     }
 }
 
 template <class C>
-__device__ __forceinline__ void read_frags(const char *as, const char *bs, int ks,
-                                           const int (&a_off)[C::KS], const int (&b_off)[C::NT],
-                                           half8 (&fa)[C::MT], half8 (&fb)[C::NT])
+__device__ __forceinline__ void fragment_offsets(int wm, int wn, int (&a_off)[C::A_NOFF],
+                                                 int (&b_off)[C::B_NOFF])
+{
+    if constexpr (C::A_KMAJ)
+        kmajor_offsets<C>(wm * C::TM, a_off);
+    else
+        mnmajor_offsets<C, C::BM>(wm * C::TM, a_off);
+    if constexpr (C::B_KMAJ)
+        kmajor_offsets<C>(wn * C::TN, b_off);
+    else
+        mnmajor_offsets<C, C::BN>(wn * C::TN, b_off);
+}
+
+template <class C, bool KMAJ, int R, int NOFF, int NBLK>
+__device__ __forceinline__ void read_operand(const char *tile, int ks, const int (&off)[NOFF],
+                                             half8 (&frag)[NBLK])
 {
 #pragma unroll
-    for (int nt = 0; nt < C::NT; nt++) {
-        const char *q = bs + b_off[nt] + ks * C::KI * C::BN * 2;
-        short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v *)TG_LDS(q));
-        short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * C::BN * 2));
-        fb[nt] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int b = 0; b < NBLK; b++) {
+        if constexpr (KMAJ) {
+            frag[b] = *(const half8 *)(tile + off[ks] + b * C::MI * C::BK * 2);
+        } else {
+            const char *q = tile + off[b] + ks * C::KI * R * 2;
+            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v *)TG_LDS(q));
+            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * R * 2));
+            frag[b] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
+                                                                        6, 7));
+        }
     }
-#pragma unroll
-    for (int mt = 0; mt < C::MT; mt++)
-        fa[mt] = *(const half8 *)(as + a_off[ks] + mt * C::MI * C::BK * 2);
+}
+
+// B fragments first (transpose reads in the normal orientation), then A.
+template <class C>
+__device__ __forceinline__ void read_frags(const char *as, const char *bs, int ks,
+                                           const int (&a_off)[C::A_NOFF],
+                                           const int (&b_off)[C::B_NOFF], half8 (&fa)[C::MT],
+                                           half8 (&fb)[C::NT])
+{
+    read_operand<C, C::B_KMAJ, C::BN>(bs, ks, b_off, fb);
+    read_operand<C, C::A_KMAJ, C::BM>(as, ks, a_off, fa);
 }
 
 template <class C>
@@ -434,60 +478,110 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 }
 
 // Wave w's copy instruction t of a K step fills LDS bytes [1 KiB * (w *
-// LOADS + t), +1 KiB) of the A (or B) tile: A_ROWS_PER_LOAD rows of the A tile
-// (lane -> row lane / (BK/8), physical chunk lane % (BK/8)), or
-// B_ROWS_PER_LOAD k-rows of the B tile.  The swizzle is applied on the global
-// side: each lane fetches the logical chunk that belongs at its physical slot.
+// LOADS + t), +1 KiB) of an operand's tile: ROWS_PER_LOAD rows of it.  In a
+// k-major tile lane i takes row i / (BK/8) and physical chunk i % (BK/8); in an
+// mn-major tile k-row i / (R/8) and physical chunk i % (R/8).  The swizzle is
+// applied on the global side: each lane fetches the logical chunk that belongs
+// at its physical slot.
 //
 // The K position is carried by the buffer descriptors, not by the lane
-// offsets: for K step kt the A descriptor starts at A + kt*BK with its range
-// shortened by as much, and likewise for B, so the lane offsets are constants
-// of the tile and a K step costs a few scalar instructions.  The range check
-// of the descriptor gives zeros for the rows of A past M and the rows of B
-// past K (the host guarantees that those offsets do not wrap 32 bits);
-// columns of B past N and the columns of A past K in the last K step lie
-// inside the buffer and are pushed out of range explicitly.  Steps at or past
-// nk get a zero-length descriptor: every lane reads zeros without touching
-// memory, so each K step keeps the same number of outstanding copies.
+// offsets: for K step kt a k-major operand's descriptor starts kt*BK elements
+// further along its rows, an mn-major one kt*BK rows further down, with the
+// range shortened by as much, so the lane offsets are constants of the tile
+// and a K step costs a few scalar instructions.  The range check gives zeros
+// for rows past the end of the operand (rows past M or N of a k-major tile,
+// rows past K of an mn-major one; the host guarantees those offsets do not
+// wrap 32 bits); the columns past K of a k-major tile in the last K step and
+// the columns past M or N of an mn-major tile lie inside the buffer and are
+// pushed out of range explicitly.  Steps at or past nk get a zero-length
+// descriptor: every lane reads zeros without touching memory, so each K step
+// keeps the same number of outstanding copies.
+template <class C, bool KMAJ, int R, int NLOADS>
+struct OperandCopy {
+    static constexpr int RPL = KMAJ ? 1024 / (C::BK * 2) : 1024 / (R * 2);
+    uint32_t lane_off;   // k-major: byte offset of this lane's chunk in instruction 0
+    int kc8;             // k-major: logical k offset of this lane's chunk in the tile
+    int row, phys;       // mn-major: k-row within an instruction; physical chunk
+
+    __device__ __forceinline__ void init(int x0, int ld)
+    {
+        const int lane = threadIdx.x & 63;
+        if constexpr (KMAJ) {
+            const int r = lane / (C::BK / 8);
+            // the swizzle depends on row % RPL only (8 or 16 rows)
+            kc8 = ((lane % (C::BK / 8)) ^ swz_a<C::BK>(r)) * 8;
+            lane_off = (uint32_t)(((int64_t)(x0 + r) * ld + kc8) * 2);
+        } else {
+            row = lane / (R / 8);
+            phys = lane % (R / 8);
+        }
+    }
+
+    // Lane offset of copy instruction t (x0: tile origin along M or N; X: M or N).
+    __device__ __forceinline__ uint32_t off(int t, int x0, int X, int ld) const
+    {
+        const int inst = (threadIdx.x >> 6) * NLOADS + t;
+        if constexpr (KMAJ) {
+            return lane_off + (uint32_t)(inst * RPL) * (uint32_t)ld * 2u;
+        } else {
+            const int k = inst * RPL + row;
+            const int col = x0 + (phys ^ swz_b<R>(k)) * 8;
+            return col < X ? ((uint32_t)k * (uint32_t)ld + (uint32_t)col) * 2u : kOOB;
+        }
+    }
+
+    // Descriptor of K step kt (zero-length past the end).
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const _Float16 *ptr, int ld,
+                                                                 uint32_t bytes, int kt, int nk)
+    {
+        const int k0 = kt * C::BK;
+        const int64_t step = KMAJ ? (int64_t)k0 : (int64_t)k0 * ld;   // elements
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(ptr + step), 0, kt < nk ? (int)(bytes - (uint32_t)step * 2u) : 0,
+            kRsrcWord3);
+    }
+
+    // K tail of a k-major tile: this lane's chunk lies past K.
+    __device__ __forceinline__ bool dead(int kt, int nk, int K) const
+    {
+        if constexpr (KMAJ)
+            return (kt == nk - 1) && (kc8 >= K - kt * C::BK);
+        else
+            return false;
+    }
+};
+
 template <class C>
 struct DirectLoader {
+    using ACopy = OperandCopy<C, C::A_KMAJ, C::BM, C::A_LOADS>;
+    using BCopy = OperandCopy<C, C::B_KMAJ, C::BN, C::B_LOADS>;
     // Per-instruction lane offsets are kept in registers when there are few
     // of them; otherwise they are rebuilt at issue from lane constants.
     static constexpr bool KEEP = C::LOADS <= 8;
     uint32_t voff[KEEP ? C::LOADS : 1];
-    uint32_t a_lane;   // A: byte offset of this lane's chunk in instruction 0
-    int a_kc8;         // A: logical k offset of this lane's chunk in the tile
-    int b_row, b_phys; // B: k-row within an instruction; physical chunk
+    ACopy a;
+    BCopy b;
     uint32_t lds0;     // LDS byte address of the workgroup's buffer
 
-    __device__ __forceinline__ uint32_t a_off(const Params &p, int t) const
+    __device__ __forceinline__ uint32_t a_off(const Params &p, int t, int m0) const
     {
-        const int inst = (threadIdx.x >> 6) * C::A_LOADS + t;
-        return a_lane + (uint32_t)(inst * C::A_ROWS_PER_LOAD) * (uint32_t)p.lda * 2u;
+        return a.off(t, m0, p.M, p.lda);
     }
 
     __device__ __forceinline__ uint32_t b_off(const Params &p, int t, int n0) const
     {
-        const int inst = (threadIdx.x >> 6) * C::B_LOADS + t;
-        const int k = inst * C::B_ROWS_PER_LOAD + b_row;
-        const int col = n0 + (b_phys ^ swz_b<C::BN>(k)) * 8;
-        return col < p.N ? ((uint32_t)k * (uint32_t)p.ldb + (uint32_t)col) * 2u : kOOB;
+        return b.off(t, n0, p.N, p.ldb);
     }
 
     __device__ __forceinline__ void init(const Params &p, const char *smem, int m0, int n0)
     {
-        const int lane = threadIdx.x & 63;
-        const int a_row = lane / (C::BK / 8);
-        // the A swizzle depends on row % A_ROWS_PER_LOAD only (8 or 16 rows)
-        a_kc8 = ((lane % (C::BK / 8)) ^ swz_a<C::BK>(a_row)) * 8;
-        a_lane = (uint32_t)(((int64_t)(m0 + a_row) * p.lda + a_kc8) * 2);
-        b_row = lane / (C::BN / 8);
-        b_phys = lane % (C::BN / 8);
+        a.init(m0, p.lda);
+        b.init(n0, p.ldb);
         lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
         if constexpr (KEEP) {
 #pragma unroll
             for (int t = 0; t < C::A_LOADS; t++)
-                voff[t] = a_off(p, t);
+                voff[t] = a_off(p, t, m0);
 #pragma unroll
             for (int t = 0; t < C::B_LOADS; t++)
                 voff[C::A_LOADS + t] = b_off(p, t, n0);
@@ -497,39 +591,30 @@ struct DirectLoader {
     // Issue copy instruction T (A copies first, then B) of K step kt into
     // LDS stage S.
     template <int S, int T>
-    __device__ __forceinline__ void issue_one(const Params &p, int kt, int nk, int n0)
+    __device__ __forceinline__ void issue_one(const Params &p, int kt, int nk, int m0, int n0)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool valid = kt < nk;
-        const int k0 = kt * C::BK;
         if constexpr (T < C::A_LOADS) {
-            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.A + k0), 0, valid ? (int)(p.a_bytes - (uint32_t)k0 * 2u) : 0,
-                kRsrcWord3);
-            // K tail: this lane's A chunk lies past K (inside the row's padding
-            // or the next row), so it is pushed out of range
-            const bool a_dead = (kt == nk - 1) && (a_kc8 >= p.K - k0);
-            const uint32_t o = KEEP ? voff[T] : a_off(p, T);
-            dma16(ra, a_dead ? kOOB : o,
+            const __amdgpu_buffer_rsrc_t ra = ACopy::rsrc(p.A, p.lda, p.a_bytes, kt, nk);
+            const uint32_t o = KEEP ? voff[T] : a_off(p, T, m0);
+            dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o,
                   lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024);
         } else {
             constexpr int t = T - C::A_LOADS;
-            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.B + (int64_t)k0 * p.ldb), 0,
-                valid ? (int)(p.b_bytes - (uint32_t)k0 * (uint32_t)p.ldb * 2u) : 0, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rb = BCopy::rsrc(p.B, p.ldb, p.b_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : b_off(p, t, n0);
-            dma16(rb, o,
+            dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o,
                   lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024);
         }
     }
 
     // Copy instructions [T0, T1) of K step kt into LDS stage S.
     template <int S, int T0 = 0, int T1 = C::LOADS>
-    __device__ __forceinline__ void issue(const Params &p, int kt, int nk, int n0)
+    __device__ __forceinline__ void issue(const Params &p, int kt, int nk, int m0, int n0)
     {
         if constexpr (T0 < T1) {
-            issue_one<S, T0>(p, kt, nk, n0);
-            issue<S, T0 + 1, T1>(p, kt, nk, n0);
+            issue_one<S, T0>(p, kt, nk, m0, n0);
+            issue<S, T0 + 1, T1>(p, kt, nk, m0, n0);
         }
     }
 };
@@ -564,7 +649,7 @@ __device__ __forceinline__ void sched_interleave_reads()
 
 template <class C>
 struct PipeState {
-    int a_off[C::KS], b_off[C::NT];
+    int a_off[C::A_NOFF], b_off[C::B_NOFF];
     half8 fa[2][C::MT], fb[2][C::NT];
     typename C::acc_t acc[C::MT][C::NT];
 };
@@ -602,30 +687,30 @@ struct Spread {
 // OFF (window W refills stage (W + STAGES) % STAGES with K step kt0+W+STAGES).
 template <class C, int W, int OFF, int T = 0>
 __device__ __forceinline__ void window_copies(const Params &p, DirectLoader<C> &ld, int kt0, int nk,
-                                              int n0)
+                                              int m0, int n0)
 {
     if constexpr (T < C::LOADS) {
         if constexpr (Spread<C>::pos(T) == OFF) {
             __builtin_amdgcn_sched_barrier(0);
-            ld.template issue_one<(W + C::STAGES) % C::STAGES, T>(p, kt0 + W + C::STAGES, nk, n0);
+            ld.template issue_one<(W + C::STAGES) % C::STAGES, T>(p, kt0 + W + C::STAGES, nk, m0, n0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        window_copies<C, W, OFF, T + 1>(p, ld, kt0, nk, n0);
+        window_copies<C, W, OFF, T + 1>(p, ld, kt0, nk, m0, n0);
     }
 }
 
 // MFMAs [I, HI) of the k-step; MFMA I sits at position OFF of window W.
 template <class C, int W, int OFF, int I, int HI>
 __device__ __forceinline__ void mfma_window(const Params &p, DirectLoader<C> &ld, int kt0, int nk,
-                                            int n0, const half8 (&fa)[C::MT],
+                                            int m0, int n0, const half8 (&fa)[C::MT],
                                             const half8 (&fb)[C::NT],
                                             typename C::acc_t (&acc)[C::MT][C::NT])
 {
     if constexpr (I < HI) {
         constexpr int mt = I / C::NT, nt = I % C::NT;
         acc[mt][nt] = mfma<C>(fb[nt], fa[mt], acc[mt][nt]);
-        window_copies<C, W, OFF>(p, ld, kt0, nk, n0);
-        mfma_window<C, W, OFF + 1, I + 1, HI>(p, ld, kt0, nk, n0, fa, fb, acc);
+        window_copies<C, W, OFF>(p, ld, kt0, nk, m0, n0);
+        mfma_window<C, W, OFF + 1, I + 1, HI>(p, ld, kt0, nk, m0, n0, fa, fb, acc);
     }
 }
 
@@ -633,7 +718,7 @@ __device__ __forceinline__ void mfma_window(const Params &p, DirectLoader<C> &ld
 // K loop (no barrier, reads or copies after its last k-step).
 template <class C, int U, bool FINAL>
 __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld, const char *smem,
-                                           int kt0, int nk, int n0, PipeState<C> &st)
+                                           int kt0, int nk, int m0, int n0, PipeState<C> &st)
 {
     constexpr int S = U / C::KS, ks = U % C::KS, P = U % 2;
     constexpr int NMF = C::MT * C::NT;
@@ -648,16 +733,16 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
             if constexpr (ks + 1 < C::KS)
                 read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off,
                               st.b_off, st.fa[1 - P], st.fb[1 - P]);
-            mfma_window<C, S - 1, OFF, 0, NMF>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+            mfma_window<C, S - 1, OFF, 0, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
         } else {
             constexpr int SN = (S + 1) % C::STAGES;
-            mfma_window<C, S - 1, OFF, 0, H>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+            mfma_window<C, S - 1, OFF, 0, H>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
             lds_barrier();                               // everyone's did; stage S is free
             read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
                           st.fa[1 - P], st.fb[1 - P]);
-            mfma_window<C, S, 0, H, NMF>(p, ld, kt0, nk, n0, st.fa[P], st.fb[P], st.acc);
+            mfma_window<C, S, 0, H, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
         }
     } else if constexpr (ks + 1 < C::KS) {
         // next k-step of the same K step: prefetch its fragments
@@ -672,7 +757,7 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
         lds_barrier();                               // everyone's did; stage S is free
         read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
                       st.fa[1 - P], st.fb[1 - P]);
-        ld.template issue<S>(p, kt0 + S + C::STAGES, nk, n0);
+        ld.template issue<S>(p, kt0 + S + C::STAGES, nk, m0, n0);
         mfma_range<C, H, NMF>(st.fa[P], st.fb[P], st.acc);
         sched_interleave_reads<NRD, R>();
     } else {
@@ -696,11 +781,11 @@ constexpr int prologue_after_step0()
 
 template <class C, bool FINAL, int U = 0>
 __device__ __forceinline__ void pipe_body(const Params &p, DirectLoader<C> &ld, const char *smem,
-                                          int kt0, int nk, int n0, PipeState<C> &st)
+                                          int kt0, int nk, int m0, int n0, PipeState<C> &st)
 {
     if constexpr (U < C::STAGES * C::KS) {
-        pipe_kstep<C, U, FINAL>(p, ld, smem, kt0, nk, n0, st);
-        pipe_body<C, FINAL, U + 1>(p, ld, smem, kt0, nk, n0, st);
+        pipe_kstep<C, U, FINAL>(p, ld, smem, kt0, nk, m0, n0, st);
+        pipe_body<C, FINAL, U + 1>(p, ld, smem, kt0, nk, m0, n0, st);
     }
 }
 
@@ -732,17 +817,17 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
             // window position precedes the loop (the rest come from window -1
             // of the first loop body)
             [&]<int... S>(std::integer_sequence<int, S...>) {
-                (ld.template issue<S>(p, S, nk, n0), ...);
+                (ld.template issue<S>(p, S, nk, m0, n0), ...);
             }(std::make_integer_sequence<int, C::STAGES - 1>{});
             [&]<int... T>(std::integer_sequence<int, T...>) {
                 ((Spread<C>::pos(T) < Spread<C>::H
-                      ? ld.template issue_one<C::STAGES - 1, T>(p, C::STAGES - 1, nk, n0)
+                      ? ld.template issue_one<C::STAGES - 1, T>(p, C::STAGES - 1, nk, m0, n0)
                       : void()),
                  ...);
             }(std::make_integer_sequence<int, C::LOADS>{});
         } else {
             [&]<int... S>(std::integer_sequence<int, S...>) {
-                (ld.template issue<S>(p, S, nk, n0), ...);
+                (ld.template issue<S>(p, S, nk, m0, n0), ...);
             }(std::make_integer_sequence<int, C::STAGES>{});
         }
         wait_vmcnt<prologue_after_step0<C>()>();   // step 0 landed
@@ -752,8 +837,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
         const int nsteps = (nk + C::STAGES - 1) / C::STAGES * C::STAGES;
         int kt = 0;
         for (; kt + C::STAGES < nsteps; kt += C::STAGES)
-            pipe_body<C, false>(p, ld, smem, kt, nk, n0, st);
-        pipe_body<C, true>(p, ld, smem, kt, nk, n0, st);
+            pipe_body<C, false>(p, ld, smem, kt, nk, m0, n0, st);
+        pipe_body<C, true>(p, ld, smem, kt, nk, m0, n0, st);
         // drain the dummy copies (they write zeros into LDS) and let every
         // wave finish its fragment reads before LDS is reused for the epilogue
         wait_vmcnt<0>();
@@ -769,39 +854,73 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 // chunks that cross the K or N edge are read element by element.  Same LDS
 // layout and fragment reads as the direct path, two LDS stages.
 // ============================================================================
+// One operand's share of a K step, register-staged.  Chunk t of this thread
+// sits at the same LDS position as the direct copies would put it; offsets
+// are in elements from the tile corner (x0, k0) of a k-major operand or
+// (k0, x0) of an mn-major one, where x runs along M (A) or N (B).
+template <class C, bool KMAJ, int R, int NLOADS>
+struct OperandStage {
+    static constexpr int RPL = KMAJ ? 1024 / (C::BK * 2) : 1024 / (R * 2);
+
+    // row (along x, k-major) or k-row (mn-major) of chunk t, and its
+    // logical column (k, k-major; x, mn-major)
+    __device__ __forceinline__ static int row(int t)
+    {
+        const int lane = threadIdx.x & 63;
+        return ((threadIdx.x >> 6) * NLOADS + t) * RPL + lane / (KMAJ ? C::BK / 8 : R / 8);
+    }
+    __device__ __forceinline__ static int col(int t)
+    {
+        const int lane = threadIdx.x & 63;
+        if constexpr (KMAJ)
+            return ((lane % (C::BK / 8)) ^ swz_a<C::BK>(row(t))) * 8;
+        else
+            return ((lane % (R / 8)) ^ swz_b<R>(row(t))) * 8;
+    }
+    __device__ __forceinline__ static uint32_t off(int t, int ld)
+    {
+        return (uint32_t)(row(t) * ld + col(t));
+    }
+
+    // Load chunk t: zeros past x = X (rows of a k-major tile, columns of an
+    // mn-major one) and past K.
+    __device__ __forceinline__ static half8 load(const _Float16 *ptr, int ld, uint32_t o, int t,
+                                                 int x0, int X, int k0, int K)
+    {
+        half8 v = {};
+        const int rvalid = KMAJ ? X - x0 : K - k0;   // rows of the tile inside the matrix
+        const int cleft = (KMAJ ? K - k0 : X - x0) - col(t);   // valid elements of the chunk
+        const _Float16 *corner = KMAJ ? ptr + (int64_t)x0 * ld + k0 : ptr + (int64_t)k0 * ld + x0;
+        if (row(t) < rvalid && cleft > 0) {
+            const _Float16 *src = corner + o;
+            if (cleft >= 8) {
+                __builtin_memcpy(&v, src, 16);   // 16-byte load, any 2-byte alignment
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    v[e] = e < cleft ? src[e] : (_Float16)0.f;
+            }
+        }
+        return v;
+    }
+};
+
 template <class C>
 struct StagedLoader {
-    half8 r[C::LOADS];     // one K step of this thread's chunks: A first, then B
+    using AS = OperandStage<C, C::A_KMAJ, C::BM, C::A_LOADS>;
+    using BS = OperandStage<C, C::B_KMAJ, C::BN, C::B_LOADS>;
+    half8 r[C::LOADS];       // one K step of this thread's chunks: A first, then B
     uint32_t off[C::LOADS];  // element offset of each chunk from the tile corner
-                           // (host: bm * lda and bk * ldb stay below 2^31)
-
-    __device__ __forceinline__ static int a_row(int t)
-    {
-        return ((threadIdx.x >> 6) * C::A_LOADS + t) * C::A_ROWS_PER_LOAD +
-               (threadIdx.x & 63) / (C::BK / 8);
-    }
-    __device__ __forceinline__ static int a_kc(int t)
-    {
-        return (((threadIdx.x & 63) % (C::BK / 8)) ^ swz_a<C::BK>(a_row(t))) * 8;
-    }
-    __device__ __forceinline__ static int b_k(int t)
-    {
-        return ((threadIdx.x >> 6) * C::B_LOADS + t) * C::B_ROWS_PER_LOAD +
-               (threadIdx.x & 63) / (C::BN / 8);
-    }
-    __device__ __forceinline__ static int b_col(int t)
-    {
-        return (((threadIdx.x & 63) % (C::BN / 8)) ^ swz_b<C::BN>(b_k(t))) * 8;
-    }
+                             // (host: in-tile offsets stay below 2^31)
 
     __device__ __forceinline__ void init(const Params &p)
     {
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++)
-            off[t] = (uint32_t)(a_row(t) * p.lda + a_kc(t));
+            off[t] = AS::off(t, p.lda);
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++)
-            off[C::A_LOADS + t] = (uint32_t)(b_k(t) * p.ldb + b_col(t));
+            off[C::A_LOADS + t] = BS::off(t, p.ldb);
     }
 
     // Load K step kt into registers; zeros past M, N and K (so steps past the
@@ -809,47 +928,23 @@ struct StagedLoader {
     __device__ __forceinline__ void load(const Params &p, int m0, int n0, int kt)
     {
         const int k0 = kt * C::BK;
-        const _Float16 *a0 = p.A + (int64_t)m0 * p.lda + k0;
-        const _Float16 *b0 = p.B + (int64_t)k0 * p.ldb + n0;
         if (m0 + C::BM <= p.M && n0 + C::BN <= p.N && k0 + C::BK <= p.K) {
             // interior: every chunk is whole
+            const _Float16 *a0 = C::A_KMAJ ? p.A + (int64_t)m0 * p.lda + k0
+                                           : p.A + (int64_t)k0 * p.lda + m0;
+            const _Float16 *b0 = C::B_KMAJ ? p.B + (int64_t)n0 * p.ldb + k0
+                                           : p.B + (int64_t)k0 * p.ldb + n0;
 #pragma unroll
             for (int t = 0; t < C::LOADS; t++)
                 __builtin_memcpy(&r[t], (t < C::A_LOADS ? a0 : b0) + off[t], 16);
             return;
         }
 #pragma unroll
-        for (int t = 0; t < C::A_LOADS; t++) {
-            const int kleft = p.K - k0 - a_kc(t);   // valid elements of the chunk
-            half8 v = {};
-            if (m0 + a_row(t) < p.M && kleft > 0) {
-                const _Float16 *src = a0 + off[t];
-                if (kleft >= 8) {
-                    __builtin_memcpy(&v, src, 16);
-                } else {
+        for (int t = 0; t < C::A_LOADS; t++)
+            r[t] = AS::load(p.A, p.lda, off[t], t, m0, p.M, k0, p.K);
 #pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        v[e] = e < kleft ? src[e] : (_Float16)0.f;
-                }
-            }
-            r[t] = v;
-        }
-#pragma unroll
-        for (int t = 0; t < C::B_LOADS; t++) {
-            const int nleft = p.N - n0 - b_col(t);
-            half8 v = {};
-            if (k0 + b_k(t) < p.K && nleft > 0) {
-                const _Float16 *src = b0 + off[C::A_LOADS + t];
-                if (nleft >= 8) {
-                    __builtin_memcpy(&v, src, 16);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        v[e] = e < nleft ? src[e] : (_Float16)0.f;
-                }
-            }
-            r[C::A_LOADS + t] = v;
-        }
+        for (int t = 0; t < C::B_LOADS; t++)
+            r[C::A_LOADS + t] = BS::load(p.B, p.ldb, off[C::A_LOADS + t], t, n0, p.N, k0, p.K);
     }
 
     // Registers -> LDS stage S, in the layout the direct copies produce.
@@ -959,8 +1054,11 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
 }
 
 // ------------------------------------------------------------ instances --
+template <class C, int TA, int TB>
+using WithOps = Cfg<C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N, C::STAGES, C::MI, C::SCHED, TA, TB>;
+
 template <class C, int KIND>
-hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
+hipError_t launch_ops(const Params &p, bool f16_out, bool bias, hipStream_t s)
 {
     const dim3 grid(p.tiles_m * p.tiles_n), block(C::THREADS);
 #define TG_GO(KERNEL, OUT, B)                                                        \
@@ -978,6 +1076,22 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 #undef TG_GO
 }
 
+// OPS: bit (1 << (2 TA + TB)) set for each operand orientation instantiated.
+template <class C, int KIND, int OPS>
+hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
+{
+    const int op = 2 * p.trans_a + p.trans_b;
+    if constexpr ((OPS & 1) != 0)
+        if (op == 0) return launch_ops<WithOps<C, 0, 0>, KIND>(p, f16_out, bias, s);
+    if constexpr ((OPS & 2) != 0)
+        if (op == 1) return launch_ops<WithOps<C, 0, 1>, KIND>(p, f16_out, bias, s);
+    if constexpr ((OPS & 4) != 0)
+        if (op == 2) return launch_ops<WithOps<C, 1, 0>, KIND>(p, f16_out, bias, s);
+    if constexpr ((OPS & 8) != 0)
+        if (op == 3) return launch_ops<WithOps<C, 1, 1>, KIND>(p, f16_out, bias, s);
+    return hipErrorInvalidValue;
+}
+
 // The library is built from TG_SHARDS compilations of this file (so they
 // can run in parallel); compilation TG_SHARD instantiates the configurations
 // whose id is TG_SHARD modulo TG_SHARDS and publishes their launchers in its
@@ -990,11 +1104,11 @@ hipError_t launch_cfg(const Params &p, bool f16_out, bool bias, hipStream_t s)
 #endif
 static_assert(TG_SHARDS >= 1 && TG_SHARDS <= kMaxShards && TG_SHARD < TG_SHARDS, "shards");
 
-template <int ID, class CFG, int KIND>
+template <int ID, class CFG, int KIND, int OPS>
 LaunchFn shard_launch()
 {
     if constexpr (ID % TG_SHARDS == TG_SHARD)
-        return &launch_cfg<CFG, KIND>;
+        return &launch_cfg<CFG, KIND, OPS>;
     else
         return nullptr;
 }
@@ -1011,24 +1125,24 @@ TG_SHARD_DECL(0) TG_SHARD_DECL(1) TG_SHARD_DECL(2) TG_SHARD_DECL(3)
 TG_SHARD_DECL(4) TG_SHARD_DECL(5) TG_SHARD_DECL(6) TG_SHARD_DECL(7)
 #undef TG_SHARD_DECL
 
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
-    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND>(),
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
+    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND, OPS>(),
 const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
 #include "tg_config_list.inc"
 };
 #undef TG_CONFIG_ROW
 #else
 // device pass: instantiate the kernels of this shard
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
-    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND>();
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
+    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND, OPS>();
 #include "tg_config_list.inc"
 #undef TG_CONFIG_ROW
 #endif
 
 #if TG_SHARD == 0 && !defined(__HIP_DEVICE_COMPILE__)
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH)                          \
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
-     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>::LDS_BYTES,                                     \
+     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>::LDS_BYTES, OPS,                                \
      (KIND == 2 ? "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI    \
                       "_c" #SCH                                                      \
                 : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI)},

@@ -31,6 +31,8 @@ import tg_inputs as gen  # noqa: E402
 # (= 2516.6 TFLOP/s; AMD's published figure rounds it to 2.5 PFLOP/s).
 PEAK_CUS, PEAK_GHZ, FLOP_PER_CLK_CU = 256, 2.4, 4096
 PEAK_TFLOPS = PEAK_CUS * PEAK_GHZ * FLOP_PER_CLK_CU / 1e3
+# dense int8 MFMA: twice the fp16 rate (AMD's published 5.0 POPS)
+PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 
 # Memory-side traffic of the dominant kernel per launch, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
@@ -107,9 +109,13 @@ def main():
     A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
     B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
     bias = torch.from_numpy(w["bias"]).to(dev) if fused else None
-    tdt = torch.float16 if c_dtype == "f16" else torch.float32
+    is_i8 = c_dtype == "i32"
+    if is_i8:
+        A = torch.from_numpy(w["A"]).to(dev)
+        B = torch.from_numpy(w["B"]).to(dev)
+    tdt = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[c_dtype]
     C = torch.empty((M, N), dtype=tdt, device=dev)
-    code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
+    code = {"f16": tg.TG_DTYPE_F16, "f32": tg.TG_DTYPE_F32, "i32": tg.TG_DTYPE_I32}[c_dtype]
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
     pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
@@ -128,20 +134,25 @@ def main():
             raise RuntimeError(tg.tg_status_string(st))
 
     # ---- parity gate on sampled outputs
-    C.fill_(float("nan"))
+    C.fill_(2 ** 31 - 1 if is_i8 else float("nan"))
     step()
     torch.cuda.synchronize()
     rng = np.random.default_rng(123)
     r = rng.integers(0, M, a.samples)
     c = rng.integers(0, N, a.samples)
     out = C.cpu().numpy()
-    vals = out[r, c].astype(np.float64)
-    cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, lda, ldb, bias=w["bias"], op_a=op_a,
-                               op_b=op_b)
-    tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
-                                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
-                               if c_dtype == "f16" else 0.0)
-    ok = bool(np.all(np.abs(vals - cref) <= tol)) and not np.isnan(out).any()
+    if is_i8:
+        cref = oracle.gemm_i8_entries(w["A"], w["B"], r, c, K, lda, ldb, op_a=op_a, op_b=op_b)
+        ok = bool(np.array_equal(out[r, c].astype(np.int64), cref)) and \
+            not np.any(out == 2 ** 31 - 1)
+    else:
+        vals = out[r, c].astype(np.float64)
+        cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, lda, ldb, bias=w["bias"],
+                                   op_a=op_a, op_b=op_b)
+        tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
+                                            2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
+                                   if c_dtype == "f16" else 0.0)
+        ok = bool(np.all(np.abs(vals - cref) <= tol)) and not np.isnan(out).any()
     if not ok:
         print(json.dumps({"error": "parity gate failed", "workload": a.workload,
                           "config": info["name"]}))
@@ -174,22 +185,30 @@ def main():
         rows = 8
         while True:
             t = time.perf_counter()
-            oracle.gemm_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K, lda=lda,
-                            ldb=ldb, bias=w["bias"], nthreads=threads, op_a=op_a, op_b=op_b)
+            if is_i8:
+                oracle.gemm_i8_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K,
+                                   lda=lda, ldb=ldb, nthreads=threads, op_a=op_a, op_b=op_b)
+            else:
+                oracle.gemm_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K, lda=lda,
+                                ldb=ldb, bias=w["bias"], nthreads=threads, op_a=op_a, op_b=op_b)
             dt = time.perf_counter() - t
             if dt >= 0.8 * a.cpu_seconds or rows >= M:
                 break
             rows = min(M, max(rows + 1, int(rows * a.cpu_seconds / max(dt, 1e-3))))
-        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6),
+               "unit": "TOPS" if is_i8 else "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": "first %d of %d rows of C (%dx%dx%d fp64 dot products), %.1f s"
-                         % (rows, M, rows, N, K, dt)}
+               "sample": "first %d of %d rows of C (%dx%dx%d %s dot products), %.1f s"
+                         % (rows, M, rows, N, K, "int64" if is_i8 else "fp64", dt)}
 
     traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest()))
+    peak = PEAK_TOPS_INT8 if is_i8 else PEAK_TFLOPS
+    unit = "TOPS" if is_i8 else "TFLOP/s"
     line = {
-        "metric": "GEMM TFLOP/s and % of MI355X fp16 MFMA peak at 8192^3; fused bias+ReLU",
+        "metric": ("int8 GEMM TOPS and % of MI355X int8 MFMA peak" if is_i8 else
+                   "GEMM TFLOP/s and % of MI355X fp16 MFMA peak at 8192^3; fused bias+ReLU"),
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
@@ -197,15 +216,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "i8" if is_i8 else "f16",
         "data": "synthetic",
         "config": {"workload": a.workload, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
                    "fused_bias_relu": fused, "op_a": "T" if op_a else "N",
                    "op_b": "T" if op_b else "N", "kernel": info["name"],
-                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+                   "pct_of_peak": round(100.0 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},
+                     "peak": round(peak, 1), "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

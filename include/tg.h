@@ -54,7 +54,10 @@
 extern "C" {
 #endif
 
-typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2 } tg_dtype;
+/* Output type.  TG_DTYPE_I32 selects the int8 product: A and B then hold
+ * int8 values and C = op(A).op(B) is accumulated and stored in int32 (exact:
+ * K is limited to 131072 so that no partial sum leaves int32). */
+typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2, TG_DTYPE_I32 = 3 } tg_dtype;
 
 /* Operand orientation for tg_gemm_ex: TG_OP_N uses the stored matrix as is,
  * TG_OP_T uses its transpose. */
@@ -92,7 +95,11 @@ tg_status tg_gemm_bias_relu(const void *A, const void *B, const float *bias, voi
  *                    B[j*ldb + k]), ldb >= K.
  * C is M x N row-major with ldc >= N.  Same ownership, validation and errors
  * as tg_gemm; an op outside {TG_OP_N, TG_OP_T} is TG_ERROR_INVALID_VALUE.
- * tg_gemm(...) equals tg_gemm_ex(TG_OP_N, TG_OP_N, A, B, NULL, C, ...). */
+ * tg_gemm(...) equals tg_gemm_ex(TG_OP_N, TG_OP_N, A, B, NULL, C, ...).
+ * c_dtype == TG_DTYPE_I32: int8 A and B, int32 C (the quantized variant the
+ * pwwt.cn article names as a next step, section 5.3; exact integer
+ * arithmetic); bias must be NULL (TG_ERROR_INVALID_VALUE otherwise) and
+ * K > 131071 is TG_ERROR_UNSUPPORTED. */
 tg_status tg_gemm_ex(tg_op op_a, tg_op op_b, const void *A, const void *B,
                      const float *bias, void *C,
                      int64_t M, int64_t N, int64_t K,
@@ -121,6 +128,7 @@ typedef struct {
                                         with per-element bounds (any alignment) */
     int lds_bytes;                   /* LDS per workgroup */
     int ops;                         /* orientations compiled: bit (1 << (2*op_a + op_b)) */
+    int elem_bytes;                  /* operand element: 2 fp16, 1 int8 (int32 C) */
     const char *name;                /* static string */
 } tg_config_desc;
 

@@ -43,6 +43,10 @@ def lib():
         L.tgref_gemm_ex.restype = I
         L.tgref_gemm_entries_ex.argtypes = [I, I, P, P, P, P, P, I64, P, I64, I64, I64]
         L.tgref_gemm_entries_ex.restype = I
+        L.tgref_gemm_i8_ex.argtypes = [I, I, P, P, P, I64, I64, I64, I64, I64, I64, I]
+        L.tgref_gemm_i8_ex.restype = I
+        L.tgref_gemm_i8_entries_ex.argtypes = [I, I, P, P, P, P, I64, P, I64, I64, I64]
+        L.tgref_gemm_i8_entries_ex.restype = I
         _lib = L
     return _lib
 
@@ -130,6 +134,37 @@ def gemm_entries(A, B, rows, cols, K, lda, ldb, bias=None, op_a=0, op_b=0):
                                      _ptr(cols), rows.size, _ptr(out), K, lda, ldb)
     if rc != 0:
         raise ValueError("tgref_gemm_entries_ex rejected its arguments")
+    return out
+
+
+def _i8(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.int8, a.dtype
+    return a.reshape(-1)
+
+
+def gemm_i8_ref(A, B, M, N, K, lda=None, ldb=None, nthreads=None, op_a=0, op_b=0):
+    """Exact int64 C (M x N) of op(A).op(B) for int8 operands (stored as for
+    gemm_ref: M x K or, with op_a, K x M; K x N or, with op_b, N x K)."""
+    lda = (M if op_a else K) if lda is None else lda
+    ldb = (K if op_b else N) if ldb is None else ldb
+    C = np.zeros((M, N), np.int64)
+    rc = lib().tgref_gemm_i8_ex(op_a, op_b, _ptr(_i8(A)), _ptr(_i8(B)), _ptr(C), M, N, K, lda,
+                                ldb, N, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("tgref_gemm_i8_ex rejected its arguments")
+    return C
+
+
+def gemm_i8_entries(A, B, rows, cols, K, lda, ldb, op_a=0, op_b=0):
+    """Exact int64 values of op(A).op(B) at the listed (row, col) positions."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(rows.shape, np.int64)
+    rc = lib().tgref_gemm_i8_entries_ex(op_a, op_b, _ptr(_i8(A)), _ptr(_i8(B)), _ptr(rows),
+                                        _ptr(cols), rows.size, _ptr(out), K, lda, ldb)
+    if rc != 0:
+        raise ValueError("tgref_gemm_i8_entries_ex rejected its arguments")
     return out
 
 

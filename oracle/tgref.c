@@ -254,3 +254,87 @@ int tgref_gemm_entries(const uint16_t *A, const uint16_t *B, const float *bias,
 {
     return tgref_gemm_entries_ex(0, 0, A, B, bias, rows, cols, count, out, K, lda, ldb);
 }
+
+/* ---- int8 operands, exact integer product (the quantized variant of the
+ * pwwt.cn article, section 5.3).  Each output is the exact sum
+ *   C[i][j] = sum_{k<K} op(A)[i][k] * op(B)[k][j]
+ * of int8 products in int64 (no rounding, no overflow for K < 2^47). */
+
+static void *gemm_i8_worker(void *p);
+
+typedef struct {
+    const int8_t *A, *B;
+    int op_a, op_b;
+    int64_t *C;
+    int64_t N, K, lda, ldb, ldc;
+    int64_t row_begin, row_end;
+} gemm_i8_job;
+
+static int64_t dot_i8(const int8_t *A, const int8_t *B, int op_a, int op_b, int64_t lda,
+                      int64_t ldb, int64_t K, int64_t i, int64_t j)
+{
+    int64_t s = 0;
+    for (int64_t k = 0; k < K; k++) {
+        const int64_t a = op_a ? A[k * lda + i] : A[i * lda + k];
+        const int64_t b = op_b ? B[j * ldb + k] : B[k * ldb + j];
+        s += a * b;
+    }
+    return s;
+}
+
+static void *gemm_i8_worker(void *p)
+{
+    gemm_i8_job *jb = (gemm_i8_job *)p;
+    for (int64_t i = jb->row_begin; i < jb->row_end; i++)
+        for (int64_t j = 0; j < jb->N; j++)
+            jb->C[i * jb->ldc + j] =
+                dot_i8(jb->A, jb->B, jb->op_a, jb->op_b, jb->lda, jb->ldb, jb->K, i, j);
+    return NULL;
+}
+
+/* All M x N entries of op(A).op(B) for int8 A, B into int64 C (leading
+ * dimension ldc).  Returns 0, or -1 on bad arguments. */
+int tgref_gemm_i8_ex(int op_a, int op_b, const int8_t *A, const int8_t *B, int64_t *C,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                     int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || ldc < N || (op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return -1;
+    if (lda < (op_a ? M : K) || ldb < (op_b ? K : N))
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > M)
+        nthreads = (int)M;
+    pthread_t th[64];
+    gemm_i8_job jobs[64];
+    if (nthreads > 64)
+        nthreads = 64;
+    int started[64] = {0};
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t] = (gemm_i8_job){A, B, op_a, op_b, C, N, K, lda, ldb, ldc,
+                                M * t / nthreads, M * (t + 1) / nthreads};
+        if (pthread_create(&th[t], NULL, gemm_i8_worker, &jobs[t]) == 0)
+            started[t] = 1;
+        else
+            gemm_i8_worker(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; t++)
+        if (started[t])
+            pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* Selected entries (rows[t], cols[t]) of the int8 product. */
+int tgref_gemm_i8_entries_ex(int op_a, int op_b, const int8_t *A, const int8_t *B,
+                             const int64_t *rows, const int64_t *cols, int64_t count,
+                             int64_t *out, int64_t K, int64_t lda, int64_t ldb)
+{
+    if (K < 0 || (op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1))
+        return -1;
+    for (int64_t t = 0; t < count; t++)
+        out[t] = dot_i8(A, B, op_a, op_b, lda, ldb, K, rows[t], cols[t]);
+    return 0;
+}

@@ -58,7 +58,7 @@ def gemm_rc(*, A=PA, B=PB, C=PC, M=64, N=64, K=64, lda=None, ldb=None, ldc=None,
     dict(M=-1), dict(N=-1), dict(K=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63),
     dict(A=0), dict(B=0), dict(C=0),
-    dict(dt=0), dict(dt=3),
+    dict(dt=0), dict(dt=4),
     dict(A=PA + 1), dict(B=PB + 1), dict(C=PC + 2),
 ])
 def test_invalid_arguments_rejected_without_gpu(kw):
@@ -140,15 +140,35 @@ def test_orientation_support_follows_the_config_table():
     for c in tg.configs():
         for op_a in (0, 1):
             for op_b in (0, 1):
-                want = 1 if c["ops"] & (1 << (2 * op_a + op_b)) else 0
+                want = 1 if c["ops"] & (1 << (2 * op_a + op_b)) and c["elem_bytes"] == 2 else 0
                 assert tg.tg_config_supports(c["id"], *args, op_a=op_a, op_b=op_b) == want
     for op_a in (0, 1):
         for op_b in (0, 1):
             cid = tg.tg_select_config(*args, op_a=op_a, op_b=op_b)
             assert tg.tg_config_supports(cid, *args, op_a=op_a, op_b=op_b) == 1
     # direct path with A^T needs M % 8 == 0 (A's stored rows run along M)
-    direct_all = [c["id"] for c in tg.configs() if c["direct_lds"] and c["ops"] == 15][0]
+    direct_all = [c["id"] for c in tg.configs()
+                  if c["direct_lds"] and c["ops"] == 15 and c["elem_bytes"] == 2][0]
     assert tg.tg_config_supports(direct_all, PA, PB, None, PC, 1020, 1024, 1024, 1024, 1024,
                                  1024, F32, op_a=1) == 0
     assert tg.tg_config_supports(direct_all, PA, PB, None, PC, 1024, 1024, 1020, 1024, 1024,
                                  1024, F32, op_a=1) == 1
+
+
+def test_int8_validation_without_gpu():
+    I32 = tg.TG_DTYPE_I32
+    ex = lambda bias, K, C=PC, A=PA: tg.tg_gemm_ex(tg.TG_OP_N, tg.TG_OP_N, A, PB, bias, C,
+                                                    64, 64, K, K, 64, 64, I32, 0)
+    assert ex(PBIAS, 64) == tg.TG_ERROR_INVALID_VALUE          # no bias with int32 C
+    assert ex(None, 131072) == tg.TG_ERROR_UNSUPPORTED          # partial sums could leave int32
+    assert ex(None, 64, C=PC + 2) == tg.TG_ERROR_INVALID_VALUE  # int32 C needs 4-byte alignment
+    args = (PA + 1, PB + 3, None, PC, 1024, 1024, 1024, 1024, 1024, 1024, I32)
+    cid = tg.tg_select_config(*args)
+    info = tg.tg_config_info(cid)
+    assert info["elem_bytes"] == 1 and not info["direct_lds"]  # odd bases: general path
+    cid = tg.tg_select_config(PA, PB, None, PC, 8192, 8192, 8192, 8192, 8192, 8192, I32)
+    assert tg.tg_config_info(cid)["elem_bytes"] == 1 and tg.tg_config_info(cid)["direct_lds"]
+    # fp16 configurations never serve int8 and vice versa
+    for c in tg.configs():
+        sup = tg.tg_config_supports(c["id"], PA, PB, None, PC, 512, 512, 512, 512, 512, 512, I32)
+        assert sup == (1 if c["elem_bytes"] == 1 else 0)

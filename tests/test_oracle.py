@@ -278,3 +278,62 @@ def test_transposed_rejects_short_leading_dimensions():
         oracle.gemm_ref(A, A, 4, 2, 2, lda=2, ldb=2, op_a=1)
     with pytest.raises(ValueError):
         oracle.gemm_ref(A, A, 2, 4, 3, lda=3, ldb=2, op_b=1)
+
+
+# ------------------------------------------------------------ int8 operands
+
+def _stored_i8(logical, op):
+    return np.ascontiguousarray(logical.T) if op else logical
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 4, 4), (7, 5, 3), (3, 7, 5)])
+def test_int8_brute_force_exact(M, N, K):
+    A, B = gen.operands_i8(M, N, K, 70 + M)
+    for op_a, op_b in itertools.product((0, 1), (0, 1)):
+        C = oracle.gemm_i8_ref(_stored_i8(A, op_a), _stored_i8(B, op_b), M, N, K, op_a=op_a,
+                               op_b=op_b)
+        for i in range(M):
+            for j in range(N):
+                want = sum(int(A[i, k]) * int(B[k, j]) for k in range(K))
+                assert int(C[i, j]) == want, (op_a, op_b, i, j)
+
+
+def test_int8_matches_numpy_int64_matmul_all_orientations():
+    M, N, K = 67, 45, 300
+    A, B = gen.operands_i8(M, N, K, 71)
+    want = A.astype(np.int64) @ B.astype(np.int64)
+    for op_a, op_b in itertools.product((0, 1), (0, 1)):
+        As, Bs = _stored_i8(A, op_a), _stored_i8(B, op_b)
+        got = oracle.gemm_i8_ref(As, Bs, M, N, K, op_a=op_a, op_b=op_b)
+        assert np.array_equal(got, want), (op_a, op_b)
+        r, c = np.array([0, M - 1, 31]), np.array([N - 1, 0, 17])
+        ent = oracle.gemm_i8_entries(As, Bs, r, c, K, As.shape[1], Bs.shape[1], op_a=op_a,
+                                     op_b=op_b)
+        assert np.array_equal(ent, want[r, c])
+
+
+def test_int8_extremes_and_padding():
+    # -128 * -128 summed K times is the largest magnitude; K = 131071 stays
+    # below 2^31 (the int32 bound the library enforces)
+    K = 131071
+    A = np.full((1, K), -128, np.int8)
+    B = np.full((K, 2), -128, np.int8)
+    B[:, 1] = 127
+    C = oracle.gemm_i8_ref(A, B, 1, 2, K)
+    assert C[0, 0] == 16384 * K and C[0, 0] < 2 ** 31
+    assert C[0, 1] == -16256 * K
+    # padded rows are ignored
+    M, N, K = 5, 6, 9
+    A, B = gen.operands_i8(M, N, K, 72)
+    Ap = np.full((M, K + 7), 99, np.int8)
+    Ap[:, :K] = A
+    Bp = np.full((K, N + 3), -99, np.int8)
+    Bp[:, :N] = B
+    assert np.array_equal(oracle.gemm_i8_ref(Ap, Bp, M, N, K, lda=K + 7, ldb=N + 3),
+                          oracle.gemm_i8_ref(A, B, M, N, K))
+
+
+def test_int8_generator_range():
+    v = gen.ints_i8(3, 100000)
+    assert v.dtype == np.int8 and v.min() == -128 and v.max() == 127
+    assert abs(float(v.mean()) + 0.5) < 1.0

@@ -98,6 +98,10 @@ WORKLOADS = {
                       c_dtype="f16", op_b=1),
     "sq8192_tn": dict(M=8192, N=8192, K=8192, kind="normal_scaled", seed=2, fused=False,
                       c_dtype="f16", op_a=1),
+    # int8 operands uniform over [-128, 127], exact int32 C
+    "sq8192_i8": dict(M=8192, N=8192, K=8192, kind="i8", seed=6, fused=False, c_dtype="i32"),
+    "sq8192_i8_nt": dict(M=8192, N=8192, K=8192, kind="i8", seed=6, fused=False,
+                         c_dtype="i32", op_b=1),
 }
 
 
@@ -118,6 +122,18 @@ def operands(M, N, K, kind, seed):
     return A, B
 
 
+def ints_i8(seed, n, start=0):
+    """int8 values uniform over [-128, 127]: floor(256 u) - 128."""
+    return (np.floor(256.0 * uniform01(seed, n, start)) - 128.0).astype(np.int8)
+
+
+def operands_i8(M, N, K, seed):
+    """int8 A (M x K) then B (K x N) from one stream."""
+    A = ints_i8(seed, M * K, 0).reshape(M, K)
+    B = ints_i8(seed, K * N, M * K).reshape(K, N)
+    return A, B
+
+
 def bias_vector(N, seed, integer=False):
     if integer:
         return ints_pm4(seed, N).astype(np.float32)
@@ -130,7 +146,10 @@ def workload(name, integer=False):
     stored arrays (transposed for workloads with op_a / op_b set)."""
     w = dict(WORKLOADS[name])
     kind = "int" if integer else w["kind"]
-    A, B = operands(w["M"], w["N"], w["K"], kind, w["seed"])
+    if w["kind"] == "i8":
+        A, B = operands_i8(w["M"], w["N"], w["K"], w["seed"])
+    else:
+        A, B = operands(w["M"], w["N"], w["K"], kind, w["seed"])
     op_a, op_b = w.get("op_a", 0), w.get("op_b", 0)
     if op_a:
         A = np.ascontiguousarray(A.T)   # stored K x M

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libtg.so")
 
 TG_DTYPE_F16 = 1
 TG_DTYPE_F32 = 2
+TG_DTYPE_I32 = 3   # int8 operands, int32 C
 
 TG_SUCCESS = 0
 TG_ERROR_INVALID_VALUE = 1
@@ -41,7 +42,8 @@ class ConfigDesc(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("mfma", ctypes.c_int), ("direct_lds", ctypes.c_int),
-                ("lds_bytes", ctypes.c_int), ("ops", ctypes.c_int), ("name", ctypes.c_char_p)]
+                ("lds_bytes", ctypes.c_int), ("ops", ctypes.c_int), ("elem_bytes", ctypes.c_int),
+                ("name", ctypes.c_char_p)]
 
 
 def _load():

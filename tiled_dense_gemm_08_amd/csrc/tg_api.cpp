@@ -36,6 +36,13 @@ struct Problem {
     int op_a, op_b;   // 1: A stored K x M / B stored N x K
 };
 
+// Operand element size: int8 operands exactly when C is int32.
+int elem_size(const Problem &p) { return p.c_dtype == TG_DTYPE_I32 ? 1 : 2; }
+
+// Largest K for which every int32 partial sum of int8 products is exact:
+// |a*b| <= 128*128 = 2^14, and (2^17 - 1) * 2^14 < 2^31.
+constexpr int64_t kMaxKInt8 = (int64_t(1) << 17) - 1;
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int64_t span_elems(int64_t rows, int64_t cols, int64_t ld)
@@ -52,8 +59,10 @@ int64_t b_cols(const Problem &p) { return p.op_b ? p.K : p.N; }
 // Pure argument checks (no HIP calls).
 tg_status validate(const Problem &p)
 {
-    if (p.c_dtype != TG_DTYPE_F16 && p.c_dtype != TG_DTYPE_F32)
+    if (p.c_dtype != TG_DTYPE_F16 && p.c_dtype != TG_DTYPE_F32 && p.c_dtype != TG_DTYPE_I32)
         return TG_ERROR_INVALID_VALUE;
+    if (p.c_dtype == TG_DTYPE_I32 && p.fused)
+        return TG_ERROR_INVALID_VALUE;   // no bias + ReLU epilogue for int32 C
     if ((p.op_a != TG_OP_N && p.op_a != TG_OP_T) || (p.op_b != TG_OP_N && p.op_b != TG_OP_T))
         return TG_ERROR_INVALID_VALUE;
     if (p.M < 0 || p.N < 0 || p.K < 0)
@@ -71,11 +80,14 @@ tg_status validate(const Problem &p)
     if (p.K > 0 && (p.A == nullptr || p.B == nullptr))
         return TG_ERROR_INVALID_VALUE;
     const uintptr_t c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
-    if (!aligned(p.A, 2) || !aligned(p.B, 2) || !aligned(p.C, c_elem) ||
+    const uintptr_t es = elem_size(p);
+    if (!aligned(p.A, es) || !aligned(p.B, es) || !aligned(p.C, c_elem) ||
         (p.bias && !aligned(p.bias, 4)))
         return TG_ERROR_INVALID_VALUE;
     if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim || p.lda > kMaxDim ||
         p.ldb > kMaxDim || p.ldc > kMaxDim)
+        return TG_ERROR_UNSUPPORTED;
+    if (p.c_dtype == TG_DTYPE_I32 && p.K > kMaxKInt8)
         return TG_ERROR_UNSUPPORTED;
     return TG_SUCCESS;
 }
@@ -91,14 +103,16 @@ struct OperandShape {
 
 bool operand_direct_ok(const OperandShape &o, const Problem &p, int bk)
 {
-    if (o.ld % 8 || (o.kmaj ? p.K % 8 : o.x % 8))
+    // every 16-byte chunk entirely inside or entirely outside the operand
+    const int64_t es = elem_size(p);
+    if ((o.ld * es) % 16 || (o.kmaj ? (p.K * es) % 16 : (o.x * es) % 16))
         return false;
     // lane offsets of rows past the edge (x + tile rows of a k-major operand,
     // block_k + 1 rows of an mn-major one) must stay below 2^32 so that the
     // range check sees them
     if (o.kmaj)
-        return 2 * (o.x + o.tile) * o.ld < (int64_t(1) << 32);
-    return 2 * (bk + 1) * o.ld < kMaxSpan;
+        return es * (o.x + o.tile) * o.ld < (int64_t(1) << 32);
+    return es * (bk + 1) * o.ld < kMaxSpan;
 }
 
 bool operand_staged_ok(const OperandShape &o, int bk)
@@ -110,7 +124,7 @@ bool operand_staged_ok(const OperandShape &o, int bk)
 // the alignment and size requirements of its load path).
 bool supports(const KernelConfig &c, const Problem &p)
 {
-    if (!(c.ops & (1 << (2 * p.op_a + p.op_b))))
+    if (!(c.ops & (1 << (2 * p.op_a + p.op_b))) || c.es != elem_size(p))
         return false;
     const OperandShape a{p.op_a == 0, p.M, p.lda, c.bm};
     const OperandShape b{p.op_b == 1, p.N, p.ldb, c.bn};
@@ -118,8 +132,8 @@ bool supports(const KernelConfig &c, const Problem &p)
         return operand_staged_ok(a, c.bk) && operand_staged_ok(b, c.bk);
     if (!aligned(p.A, 16) || !aligned(p.B, 16))
         return false;
-    if (2 * span_elems(a_rows(p), a_cols(p), p.lda) >= kMaxSpan ||
-        2 * span_elems(b_rows(p), b_cols(p), p.ldb) >= kMaxSpan)
+    if (elem_size(p) * span_elems(a_rows(p), a_cols(p), p.lda) >= kMaxSpan ||
+        elem_size(p) * span_elems(b_rows(p), b_cols(p), p.ldb) >= kMaxSpan)
         return false;
     return operand_direct_ok(a, p, c.bk) && operand_direct_ok(b, p, c.bk);
 }
@@ -129,6 +143,12 @@ bool supports(const KernelConfig &c, const Problem &p)
 
 int choose(const Problem &p)
 {
+    if (elem_size(p) == 1) {
+        const int id = dispatch_int8(p.M, p.N, p.K);
+        if (supports(kConfigs[id], p))
+            return id;
+        return dispatch_int8_fallback(p.M, p.N, p.K);
+    }
     const int id = dispatch_table_lookup(p.M, p.N, p.K, p.fused);
     if (id >= 0 && id < kNumConfigs && supports(kConfigs[id], p))
         return id;
@@ -218,8 +238,8 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     k.group_m = 8;
     k.trans_a = p.op_a;
     k.trans_b = p.op_b;
-    const int64_t a_span = 2 * span_elems(a_rows(p), a_cols(p), p.lda);
-    const int64_t b_span = 2 * span_elems(b_rows(p), b_cols(p), p.ldb);
+    const int64_t a_span = elem_size(p) * span_elems(a_rows(p), a_cols(p), p.lda);
+    const int64_t b_span = elem_size(p) * span_elems(b_rows(p), b_cols(p), p.ldb);
     k.a_bytes = (uint32_t)(a_span < kMaxSpan ? a_span : 0);
     k.b_bytes = (uint32_t)(b_span < kMaxSpan ? b_span : 0);
     const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
@@ -308,6 +328,7 @@ tg_status tg_config_info(int id, tg_config_desc *out)
     out->direct_lds = c.direct;
     out->lds_bytes = c.lds_bytes;
     out->ops = c.ops;
+    out->elem_bytes = c.es;
     out->name = c.name;
     return TG_SUCCESS;
 }
@@ -334,6 +355,6 @@ int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const
     return choose(p);
 }
 
-const char *tg_version(void) { return "tg 0.1.0 (gfx950)"; }
+const char *tg_version(void) { return "tg 0.2.0 (gfx950)"; }
 
 }  // extern "C"

@@ -11,8 +11,8 @@ namespace tg {
 // Kernel arguments.  Sizes are validated by the host to fit 32-bit ints; the
 // byte spans a_bytes / b_bytes are the buffer-descriptor ranges of A and B.
 struct Params {
-    const _Float16 *A;
-    const _Float16 *B;
+    const void *A;   // fp16 or int8 elements (the configuration's element size)
+    const void *B;
     const float *bias;
     void *C;
     int M, N, K;
@@ -34,6 +34,7 @@ struct KernelConfig {
     int direct;       // 1: direct global->LDS path, 0: register-staged path
     int lds_bytes;
     int ops;          // bit 2*trans_a + trans_b set: that orientation is compiled
+    int es;           // operand element size: 2 fp16, 1 int8
     const char *name;
 };
 

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "tg_kernels.h"
@@ -44,6 +45,9 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
 
 #define TG_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -80,10 +84,11 @@ __device__ __forceinline__ void wait_vmcnt()
 // full ds_read_b128 rate on gfx950 (measured: about 200 B/clk/CU, against
 // about 60 without a swizzle).  64-byte rows (BK = 32) use a 2-bit analogue.
 // Both are unchanged by row += 16, so one per-lane offset serves every block.
-template <int BK>
+template <int ROWB>
 __device__ __forceinline__ int swz_a(int row)
 {
-    if constexpr (BK == 64)
+    static_assert(ROWB == 128 || ROWB == 64, "k-major row bytes");
+    if constexpr (ROWB == 128)
         return row & 7;
     else
         return (row >> 1) & 3;
@@ -102,6 +107,26 @@ __device__ __forceinline__ int swz_b(int k)
         return 2 * (k & 3) + 8 * ((k >> 3) & 1);
     else
         return 2 * (k & 3);
+}
+
+// Same for 1-byte elements (R bytes per row): the 8-bit transpose read has,
+// per 16-lane group, 8 rows (k % 8 = 0..7) of 16 bytes; XOR by k % 8 puts them
+// on 8 distinct 16-byte slots.  Unchanged by k += 8.
+template <int R>
+__device__ __forceinline__ int swz_b8(int k)
+{
+    constexpr int CHUNKS = R / 16;
+    return k & (CHUNKS >= 8 ? 7 : CHUNKS - 1);
+}
+
+// The swizzle of an mn-major tile of R elements of ES bytes per row.
+template <int ES, int R>
+__device__ __forceinline__ int swz_mn(int k)
+{
+    if constexpr (ES == 2)
+        return swz_b<R>(k);
+    else
+        return swz_b8<R>(k);
 }
 
 // ------------------------------------------------------------- tile order --
@@ -126,13 +151,20 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_
 }
 
 // ---------------------------------------------------------------- configs --
-template <int MI> struct AccT;
-template <> struct AccT<16> { typedef float4v type; };
-template <> struct AccT<32> { typedef float16v type; };
+template <int MI, int ES> struct AccT;
+template <> struct AccT<16, 2> { typedef float4v type; };
+template <> struct AccT<32, 2> { typedef float16v type; };
+template <> struct AccT<16, 1> { typedef int4v type; };
+template <> struct AccT<32, 1> { typedef int16v type; };
 
+// ES: operand element size: 2 (fp16 operands, fp32 accumulation) or 1 (int8
+// operands, int32 accumulation).  BK counts elements; a k-major tile row is
+// BK * ES bytes (64 or 128), and every copy, swizzle and fragment read works
+// on 16-byte chunks, so both element sizes share them.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_, int SCHED_,
-          int TA_ = 0, int TB_ = 0>
+          int TA_ = 0, int TB_ = 0, int ES_ = 2>
 struct Cfg {
+    static constexpr int ES = ES_;
     static constexpr int SCHED = SCHED_;   // copy issue: 0 burst after the barrier, 1 spread
     // Operand orientation: TA = 1 when A is stored K x M (the product uses its
     // transpose), TB = 1 when B is stored N x K.  The LDS tile of an operand is
@@ -145,15 +177,16 @@ struct Cfg {
     static constexpr int WAVES_M = WM_, WAVES_N = WN_;
     static constexpr int STAGES = STAGES_;
     static constexpr int MI = MI_;                         // MFMA block edge
-    static constexpr int KI = 512 / MI;                    // k per MFMA: 32 or 16
-    static constexpr int ACC = MI * MI / 64;               // fp32 per lane per block
+    static constexpr int KI = 1024 / MI / ES;              // k per MFMA: 32x32: 16 (fp16), 32 (int8)
+    static constexpr int ACC = MI * MI / 64;               // accumulators per lane per block
     static constexpr int WAVES = WM_ * WN_;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int TM = BM / WM_, TN = BN / WN_;     // wave tile
     static constexpr int MT = TM / MI, NT = TN / MI;       // MFMA blocks per wave
     static constexpr int KS = BK / KI;                     // MFMA k-steps per K step
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int A_BYTES = BM * BK * ES;
+    static constexpr int B_BYTES = BK * BN * ES;
+    static constexpr int KROWB = BK * ES;                  // bytes of a k-major tile row
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // global->LDS copy: each wave instruction moves 1 KiB (64 lanes x 16 B)
@@ -161,17 +194,18 @@ struct Cfg {
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     // rows of the LDS tile that one copy instruction (1 KiB) fills
-    static constexpr int A_ROWS_PER_LOAD = A_KMAJ ? 1024 / (BK * 2) : 1024 / (BM * 2);
-    static constexpr int B_ROWS_PER_LOAD = B_KMAJ ? 1024 / (BK * 2) : 1024 / (BN * 2);
+    static constexpr int A_ROWS_PER_LOAD = A_KMAJ ? 1024 / KROWB : 1024 / (BM * ES);
+    static constexpr int B_ROWS_PER_LOAD = B_KMAJ ? 1024 / KROWB : 1024 / (BN * ES);
     // fragment offset registers: one per k-step (k-major) or per block (mn-major)
-    static constexpr int A_NOFF = A_KMAJ ? BK / (512 / MI_) : BM / WM_ / MI_;
-    static constexpr int B_NOFF = B_KMAJ ? BK / (512 / MI_) : BN / WN_ / MI_;
-    typedef typename AccT<MI>::type acc_t;
+    static constexpr int A_NOFF = A_KMAJ ? BK / KI : BM / WM_ / MI_;
+    static constexpr int B_NOFF = B_KMAJ ? BK / KI : BN / WN_ / MI_;
+    typedef typename AccT<MI, ES>::type acc_t;
     static_assert(MI == 16 || MI == 32, "MI");
-    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(ES == 1 || ES == 2, "element size");
+    static_assert(KROWB == 64 || KROWB == 128, "BK");
     static_assert(TM % MI == 0 && TN % MI == 0, "wave tile");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "copy split");
-    static_assert(BN * 2 <= 1024 && BN % 64 == 0 && BM * 2 <= 1024 && BM % 64 == 0, "BM, BN");
+    static_assert(BN * ES <= 1024 && BN % 64 == 0 && BM * ES <= 1024 && BM % 64 == 0, "BM, BN");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -180,12 +214,16 @@ struct Cfg {
 // operand fragment gives lane l the 8 k = 8 (l / MI) .. +7 of the k-step for
 // row (A, second source) or column (B, first source) l % MI of its block.
 //  k-major tile (R rows of BK): one ds_read_b128 per block at
-//    off[ks] + block * MI * BK * 2.
-//  mn-major tile (BK rows of R): two transpose reads of 4 k each: lane
+//    off[ks] + block * MI * BK * ES.
+//  mn-major tile (BK rows of R), fp16: two transpose reads of 4 k each: lane
 //    L = 16 G + 4 e + q reads row k = 8 (L / MI) + e (+4 for the second read,
 //    + KI per k-step) at positions 16 ((L % MI) / 16) + 4 q .. +3 of the
 //    block; the hardware hands lane 16 G + j the 4 rows' position j.
-//    off[block] + ks * KI * R * 2.
+//  mn-major tile, int8: two 8-bit transpose reads of 8 k each: lane
+//    L = 16 G + 2 e + h reads row k = 16 (L / MI) + e (+8 for the second read)
+//    at positions 16 ((L % MI) / 16) + 8 h .. +7; lane 16 G + j receives the 8
+//    rows' position j (measured on gfx950 with an in-bounds probe).
+//    off[block] + ks * KI * R * ES.
 template <class C, int NOFF>
 __device__ __forceinline__ void kmajor_offsets(int base, int (&off)[NOFF])
 {
@@ -193,8 +231,8 @@ __device__ __forceinline__ void kmajor_offsets(int base, int (&off)[NOFF])
     const int row = base + lane % C::MI;
 #pragma unroll
     for (int ks = 0; ks < NOFF; ks++) {
-        const int chunk = ks * (C::KI / 8) + lane / C::MI;
-        off[ks] = row * C::BK * 2 + ((chunk ^ swz_a<C::BK>(row)) * 16);
+        const int chunk = ks * (C::KI * C::ES / 16) + lane / C::MI;
+        off[ks] = row * C::KROWB + ((chunk ^ swz_a<C::KROWB>(row)) * 16);
     }
 }
 
@@ -203,13 +241,23 @@ __device__ __forceinline__ void mnmajor_offsets(int base, int (&off)[NOFF])
 {
     const int lane = threadIdx.x & 63;
     const int i = lane & 15;
-    const int e = i >> 2, q = i & 3;
-    const int k = 8 * (lane / C::MI) + e;
     const int sub = (lane % C::MI) >> 4;
+    if constexpr (C::ES == 2) {
+        const int e = i >> 2, q = i & 3;
+        const int k = 8 * (lane / C::MI) + e;
 #pragma unroll
-    for (int b = 0; b < NOFF; b++) {
-        const int col = base + b * C::MI + sub * 16 + 4 * q;
-        off[b] = k * R * 2 + (((col >> 3) ^ swz_b<R>(k)) * 16) + (col & 7) * 2;
+        for (int b = 0; b < NOFF; b++) {
+            const int col = base + b * C::MI + sub * 16 + 4 * q;
+            off[b] = k * R * 2 + (((col >> 3) ^ swz_b<R>(k)) * 16) + (col & 7) * 2;
+        }
+    } else {
+        const int e = i >> 1, h = i & 1;
+        const int k = 16 * (lane / C::MI) + e;
+#pragma unroll
+        for (int b = 0; b < NOFF; b++) {
+            const int col = base + b * C::MI + sub * 16 + 8 * h;
+            off[b] = k * R + (((col >> 4) ^ swz_b8<R>(k)) * 16) + (col & 15);
+        }
     }
 }
 
@@ -234,8 +282,8 @@ __device__ __forceinline__ void read_operand(const char *tile, int ks, const int
 #pragma unroll
     for (int b = 0; b < NBLK; b++) {
         if constexpr (KMAJ) {
-            frag[b] = *(const half8 *)(tile + off[ks] + b * C::MI * C::BK * 2);
-        } else {
+            frag[b] = *(const half8 *)(tile + off[ks] + b * C::MI * C::KROWB);
+        } else if constexpr (C::ES == 2) {
             const char *q = tile + off[b] + ks * C::KI * R * 2;
             short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) short4v *)TG_LDS(q));
@@ -243,6 +291,13 @@ __device__ __forceinline__ void read_operand(const char *tile, int ks, const int
                 (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * R * 2));
             frag[b] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
                                                                         6, 7));
+        } else {
+            const char *q = tile + off[b] + ks * C::KI * R;
+            int2v lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) int2v *)TG_LDS(q));
+            int2v hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) int2v *)TG_LDS(q + 8 * R));
+            frag[b] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
         }
     }
 }
@@ -258,13 +313,21 @@ __device__ __forceinline__ void read_frags(const char *as, const char *bs, int k
     read_operand<C, C::A_KMAJ, C::BM>(as, ks, a_off, fa);
 }
 
+// half8 is the 16-byte fragment container for both element sizes.
 template <class C>
 __device__ __forceinline__ typename C::acc_t mfma(half8 b, half8 a, typename C::acc_t c)
 {
-    if constexpr (C::MI == 16)
+    if constexpr (C::ES == 1) {
+        const int4v bi = __builtin_bit_cast(int4v, b), ai = __builtin_bit_cast(int4v, a);
+        if constexpr (C::MI == 16)
+            return __builtin_amdgcn_mfma_i32_16x16x64_i8(bi, ai, c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(bi, ai, c, 0, 0, 0);
+    } else if constexpr (C::MI == 16) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
-    else
+    } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    }
 }
 
 template <class C, int LO, int HI>
@@ -303,19 +366,37 @@ __device__ __forceinline__ float4v load_bias4(const Params &p, int col)
     return bv;
 }
 
+// 4 accumulator values of one run: fp32 (fp16 operands) or int32 (int8).
+template <class C>
+using val4_t = typename std::conditional<C::ES == 1, int4v, float4v>::type;
+
 template <class C, bool BIAS>
-__device__ __forceinline__ float4v epi_value(const typename C::acc_t &a, int run, float4v bv)
+__device__ __forceinline__ val4_t<C> epi_value(const typename C::acc_t &a, int run, float4v bv)
 {
-    float4v v;
+    val4_t<C> v;
 #pragma unroll
     for (int r = 0; r < 4; r++)
         v[r] = a[4 * run + r];
     if constexpr (BIAS) {
+        static_assert(C::ES == 2, "bias + ReLU is an fp32 epilogue");
 #pragma unroll
         for (int r = 0; r < 4; r++)
             v[r] = fmaxf(v[r] + bv[r], 0.f);
     }
     return v;
+}
+
+// Store 4 consecutive outputs: fp32 and int32 as 16 bytes, fp16 converted
+// (round to nearest even) as 8 bytes.
+template <typename OutT, typename V>
+__device__ __forceinline__ void store4(char *dst, V v)
+{
+    if constexpr (sizeof(OutT) == 4) {
+        *(V *)dst = v;
+    } else {
+        half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        *(half4 *)dst = h;
+    }
 }
 
 // Direct epilogue: each lane stores its 4-column runs straight to C.  Used when
@@ -340,15 +421,10 @@ __device__ __forceinline__ void epilogue_direct(const Params &p, int m_base, int
                 const int row = m_base + mt * C::MI + lane % C::MI;
                 if (row >= p.M)
                     continue;
-                const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
+                const val4_t<C> v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
                 OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
                 if (vec_ok && col + 3 < p.N) {
-                    if constexpr (sizeof(OutT) == 4) {
-                        *(float4v *)dst = v;
-                    } else {
-                        half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(half4 *)dst = h;
-                    }
+                    store4<OutT>((char *)dst, v);
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; r++)
@@ -406,14 +482,8 @@ __device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_
                 for (int i = 0; i < MT_PASS; i++) {
                     const int mt = pass * MT_PASS + i;
                     const int row = i * C::MI + lane % C::MI;
-                    const float4v v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
-                    char *dst = region + row * ROWB + run_col<C>(nt, run) * ES;
-                    if constexpr (ES == 4) {
-                        *(float4v *)dst = v;
-                    } else {
-                        half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(half4 *)dst = h;
-                    }
+                    const val4_t<C> v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
+                    store4<OutT>(region + row * ROWB + run_col<C>(nt, run) * ES, v);
                 }
         }
         // LDS -> C, 16 bytes per lane, consecutive lanes along a row.  A wave's
@@ -498,54 +568,56 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // keeps the same number of outstanding copies.
 template <class C, bool KMAJ, int R, int NLOADS>
 struct OperandCopy {
-    static constexpr int RPL = KMAJ ? 1024 / (C::BK * 2) : 1024 / (R * 2);
+    static constexpr int ES = C::ES;
+    static constexpr int RCH = KMAJ ? C::KROWB / 16 : R * ES / 16;   // 16-byte chunks per row
+    static constexpr int RPL = 64 / RCH;                             // rows per instruction
     uint32_t lane_off;   // k-major: byte offset of this lane's chunk in instruction 0
-    int kc8;             // k-major: logical k offset of this lane's chunk in the tile
+    int kc;              // k-major: logical k (elements) of this lane's chunk in the tile
     int row, phys;       // mn-major: k-row within an instruction; physical chunk
 
     __device__ __forceinline__ void init(int x0, int ld)
     {
         const int lane = threadIdx.x & 63;
         if constexpr (KMAJ) {
-            const int r = lane / (C::BK / 8);
+            const int r = lane / RCH;
             // the swizzle depends on row % RPL only (8 or 16 rows)
-            kc8 = ((lane % (C::BK / 8)) ^ swz_a<C::BK>(r)) * 8;
-            lane_off = (uint32_t)(((int64_t)(x0 + r) * ld + kc8) * 2);
+            kc = ((lane % RCH) ^ swz_a<C::KROWB>(r)) * (16 / ES);
+            lane_off = (uint32_t)(((int64_t)(x0 + r) * ld + kc) * ES);
         } else {
-            row = lane / (R / 8);
-            phys = lane % (R / 8);
+            row = lane / RCH;
+            phys = lane % RCH;
         }
     }
 
-    // Lane offset of copy instruction t (x0: tile origin along M or N; X: M or N).
+    // Lane byte offset of copy instruction t (x0: tile origin along M or N;
+    // X: M or N).
     __device__ __forceinline__ uint32_t off(int t, int x0, int X, int ld) const
     {
         const int inst = (threadIdx.x >> 6) * NLOADS + t;
         if constexpr (KMAJ) {
-            return lane_off + (uint32_t)(inst * RPL) * (uint32_t)ld * 2u;
+            return lane_off + (uint32_t)(inst * RPL) * (uint32_t)ld * (uint32_t)ES;
         } else {
             const int k = inst * RPL + row;
-            const int col = x0 + (phys ^ swz_b<R>(k)) * 8;
-            return col < X ? ((uint32_t)k * (uint32_t)ld + (uint32_t)col) * 2u : kOOB;
+            const int col = x0 + (phys ^ swz_mn<ES, R>(k)) * (16 / ES);
+            return col < X ? ((uint32_t)k * (uint32_t)ld + (uint32_t)col) * (uint32_t)ES : kOOB;
         }
     }
 
     // Descriptor of K step kt (zero-length past the end).
-    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const _Float16 *ptr, int ld,
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const char *ptr, int ld,
                                                                  uint32_t bytes, int kt, int nk)
     {
         const int k0 = kt * C::BK;
-        const int64_t step = KMAJ ? (int64_t)k0 : (int64_t)k0 * ld;   // elements
+        const int64_t step = (KMAJ ? (int64_t)k0 : (int64_t)k0 * ld) * ES;   // bytes
         return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(ptr + step), 0, kt < nk ? (int)(bytes - (uint32_t)step * 2u) : 0,
-            kRsrcWord3);
+            (void *)(ptr + step), 0, kt < nk ? (int)(bytes - (uint32_t)step) : 0, kRsrcWord3);
     }
 
     // K tail of a k-major tile: this lane's chunk lies past K.
     __device__ __forceinline__ bool dead(int kt, int nk, int K) const
     {
         if constexpr (KMAJ)
-            return (kt == nk - 1) && (kc8 >= K - kt * C::BK);
+            return (kt == nk - 1) && (kc >= K - kt * C::BK);
         else
             return false;
     }
@@ -595,13 +667,13 @@ struct DirectLoader {
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         if constexpr (T < C::A_LOADS) {
-            const __amdgpu_buffer_rsrc_t ra = ACopy::rsrc(p.A, p.lda, p.a_bytes, kt, nk);
+            const __amdgpu_buffer_rsrc_t ra = ACopy::rsrc((const char *)p.A, p.lda, p.a_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : a_off(p, T, m0);
             dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o,
                   lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024);
         } else {
             constexpr int t = T - C::A_LOADS;
-            const __amdgpu_buffer_rsrc_t rb = BCopy::rsrc(p.B, p.ldb, p.b_bytes, kt, nk);
+            const __amdgpu_buffer_rsrc_t rb = BCopy::rsrc((const char *)p.B, p.ldb, p.b_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : b_off(p, t, n0);
             dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o,
                   lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024);
@@ -860,22 +932,25 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 // (k0, x0) of an mn-major one, where x runs along M (A) or N (B).
 template <class C, bool KMAJ, int R, int NLOADS>
 struct OperandStage {
-    static constexpr int RPL = KMAJ ? 1024 / (C::BK * 2) : 1024 / (R * 2);
+    static constexpr int ES = C::ES;
+    static constexpr int CE = 16 / ES;                               // elements per chunk
+    static constexpr int RCH = KMAJ ? C::KROWB / 16 : R * ES / 16;   // chunks per row
+    static constexpr int RPL = 64 / RCH;
 
     // row (along x, k-major) or k-row (mn-major) of chunk t, and its
-    // logical column (k, k-major; x, mn-major)
+    // logical column in elements (k, k-major; x, mn-major)
     __device__ __forceinline__ static int row(int t)
     {
         const int lane = threadIdx.x & 63;
-        return ((threadIdx.x >> 6) * NLOADS + t) * RPL + lane / (KMAJ ? C::BK / 8 : R / 8);
+        return ((threadIdx.x >> 6) * NLOADS + t) * RPL + lane / RCH;
     }
     __device__ __forceinline__ static int col(int t)
     {
         const int lane = threadIdx.x & 63;
         if constexpr (KMAJ)
-            return ((lane % (C::BK / 8)) ^ swz_a<C::BK>(row(t))) * 8;
+            return ((lane % RCH) ^ swz_a<C::KROWB>(row(t))) * CE;
         else
-            return ((lane % (R / 8)) ^ swz_b<R>(row(t))) * 8;
+            return ((lane % RCH) ^ swz_mn<ES, R>(row(t))) * CE;
     }
     __device__ __forceinline__ static uint32_t off(int t, int ld)
     {
@@ -884,21 +959,23 @@ struct OperandStage {
 
     // Load chunk t: zeros past x = X (rows of a k-major tile, columns of an
     // mn-major one) and past K.
-    __device__ __forceinline__ static half8 load(const _Float16 *ptr, int ld, uint32_t o, int t,
+    __device__ __forceinline__ static half8 load(const char *ptr, int ld, uint32_t o, int t,
                                                  int x0, int X, int k0, int K)
     {
         half8 v = {};
         const int rvalid = KMAJ ? X - x0 : K - k0;   // rows of the tile inside the matrix
         const int cleft = (KMAJ ? K - k0 : X - x0) - col(t);   // valid elements of the chunk
-        const _Float16 *corner = KMAJ ? ptr + (int64_t)x0 * ld + k0 : ptr + (int64_t)k0 * ld + x0;
+        const int64_t corner = KMAJ ? (int64_t)x0 * ld + k0 : (int64_t)k0 * ld + x0;
         if (row(t) < rvalid && cleft > 0) {
-            const _Float16 *src = corner + o;
-            if (cleft >= 8) {
-                __builtin_memcpy(&v, src, 16);   // 16-byte load, any 2-byte alignment
+            const char *src = ptr + (corner + o) * ES;
+            if (cleft >= CE) {
+                __builtin_memcpy(&v, src, 16);   // 16-byte load, any element alignment
             } else {
+                char *d = (char *)&v;
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    v[e] = e < cleft ? src[e] : (_Float16)0.f;
+                for (int e = 0; e < CE; e++)
+                    if (e < cleft)
+                        __builtin_memcpy(d + e * ES, src + e * ES, ES);
             }
         }
         return v;
@@ -930,21 +1007,22 @@ struct StagedLoader {
         const int k0 = kt * C::BK;
         if (m0 + C::BM <= p.M && n0 + C::BN <= p.N && k0 + C::BK <= p.K) {
             // interior: every chunk is whole
-            const _Float16 *a0 = C::A_KMAJ ? p.A + (int64_t)m0 * p.lda + k0
-                                           : p.A + (int64_t)k0 * p.lda + m0;
-            const _Float16 *b0 = C::B_KMAJ ? p.B + (int64_t)n0 * p.ldb + k0
-                                           : p.B + (int64_t)k0 * p.ldb + n0;
+            const char *a0 = (const char *)p.A + (C::A_KMAJ ? (int64_t)m0 * p.lda + k0
+                                                            : (int64_t)k0 * p.lda + m0) * C::ES;
+            const char *b0 = (const char *)p.B + (C::B_KMAJ ? (int64_t)n0 * p.ldb + k0
+                                                            : (int64_t)k0 * p.ldb + n0) * C::ES;
 #pragma unroll
             for (int t = 0; t < C::LOADS; t++)
-                __builtin_memcpy(&r[t], (t < C::A_LOADS ? a0 : b0) + off[t], 16);
+                __builtin_memcpy(&r[t], (t < C::A_LOADS ? a0 : b0) + (int64_t)off[t] * C::ES, 16);
             return;
         }
 #pragma unroll
         for (int t = 0; t < C::A_LOADS; t++)
-            r[t] = AS::load(p.A, p.lda, off[t], t, m0, p.M, k0, p.K);
+            r[t] = AS::load((const char *)p.A, p.lda, off[t], t, m0, p.M, k0, p.K);
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++)
-            r[C::A_LOADS + t] = BS::load(p.B, p.ldb, off[C::A_LOADS + t], t, n0, p.N, k0, p.K);
+            r[C::A_LOADS + t] = BS::load((const char *)p.B, p.ldb, off[C::A_LOADS + t], t, n0,
+                                         p.N, k0, p.K);
     }
 
     // Registers -> LDS stage S, in the layout the direct copies produce.
@@ -1055,7 +1133,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
 
 // ------------------------------------------------------------ instances --
 template <class C, int TA, int TB>
-using WithOps = Cfg<C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N, C::STAGES, C::MI, C::SCHED, TA, TB>;
+using WithOps = Cfg<C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N, C::STAGES, C::MI, C::SCHED, TA, TB,
+                    C::ES>;
 
 template <class C, int KIND>
 hipError_t launch_ops(const Params &p, bool f16_out, bool bias, hipStream_t s)
@@ -1066,7 +1145,14 @@ hipError_t launch_ops(const Params &p, bool f16_out, bool bias, hipStream_t s)
         hipLaunchKernelGGL((KERNEL<C, OUT, B>), grid, block, 0, s, p);               \
         return hipGetLastError();                                                    \
     } while (0)
-    if constexpr (KIND == 2) {
+    if constexpr (C::ES == 1) {   // int8 operands: int32 C, no bias
+        if (f16_out || bias)
+            return hipErrorInvalidValue;
+        if constexpr (KIND == 2)
+            TG_GO(gemm_pipe, int32_t, false);
+        else
+            TG_GO(gemm_staged, int32_t, false);
+    } else if constexpr (KIND == 2) {
         if (f16_out) { if (bias) TG_GO(gemm_pipe, _Float16, true); else TG_GO(gemm_pipe, _Float16, false); }
         else { if (bias) TG_GO(gemm_pipe, float, true); else TG_GO(gemm_pipe, float, false); }
     } else {
@@ -1125,27 +1211,30 @@ TG_SHARD_DECL(0) TG_SHARD_DECL(1) TG_SHARD_DECL(2) TG_SHARD_DECL(3)
 TG_SHARD_DECL(4) TG_SHARD_DECL(5) TG_SHARD_DECL(6) TG_SHARD_DECL(7)
 #undef TG_SHARD_DECL
 
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
-    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND, OPS>(),
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
+    shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>, KIND, OPS>(),
 const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
 #include "tg_config_list.inc"
 };
 #undef TG_CONFIG_ROW
 #else
 // device pass: instantiate the kernels of this shard
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
-    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>, KIND, OPS>();
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
+    template LaunchFn shard_launch<ID, Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>, KIND, OPS>();
 #include "tg_config_list.inc"
 #undef TG_CONFIG_ROW
 #endif
 
 #if TG_SHARD == 0 && !defined(__HIP_DEVICE_COMPILE__)
-#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS)                          \
+#define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
-     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH>::LDS_BYTES, OPS,                                \
-     (KIND == 2 ? "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI    \
-                      "_c" #SCH                                                      \
-                : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI)},
+     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>::LDS_BYTES, OPS, ES,                   \
+     (KIND == 2 ? (ES == 1 ? "i8_pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI \
+                             "_c" #SCH                                                     \
+                           : "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI   \
+                             "_c" #SCH)                                                    \
+                : (ES == 1 ? "i8_staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI   \
+                           : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI))},
 
 const KernelConfig kConfigs[] = {
 #include "tg_config_list.inc"

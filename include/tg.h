@@ -68,7 +68,8 @@ typedef enum {
     TG_ERROR_INVALID_VALUE = 1,
     TG_ERROR_NOT_DEVICE_MEMORY = 2,
     TG_ERROR_UNSUPPORTED = 3,
-    TG_ERROR_LAUNCH = 4
+    TG_ERROR_LAUNCH = 4,
+    TG_ERROR_FILE = 5            /* tg_tuning_load: the file cannot be opened or read */
 } tg_status;
 
 /* C = A.B (overwrites C; no alpha/beta scaling).  A, B: fp16; C: c_dtype. */
@@ -112,9 +113,17 @@ const char *tg_status_string(tg_status s);
 /* ---- tuning and test entry points ---------------------------------------
  * The kernel configurations (block tile, K step, pipeline stages, waves per
  * workgroup, load path) compiled into the library.  The dispatcher above
- * picks one per call from a static table chosen offline by an on-device sweep
- * (lqnn.cn walkthrough, sections 2.3 and 5.3: search block sizes and stages on
- * the real device, record the best per shape, read the record at run time). */
+ * picks one per call (lqnn.cn walkthrough, sections 2.3 and 5.3: search block
+ * sizes and stages on the real device, record the best per shape, read the
+ * record at run time), trying in order
+ *   1. the run-time tuning cache below (exact shape, orientation, C dtype and
+ *      fused flag),
+ *   2. a compiled table of exact shapes,
+ *   3. a compiled shape-class grid: the nearest grid point in log2 distance
+ *      along M, N and K, whose configurations are ranked by on-device timing,
+ *   4. the register-staged kernels, which take any alignment,
+ * and at each step uses the configuration only if it can run the problem
+ * (tg_config_supports). */
 
 typedef struct {
     int id;
@@ -159,6 +168,47 @@ tg_status tg_gemm_with_config(int config_id, tg_op op_a, tg_op op_b, const void 
                               int64_t M, int64_t N, int64_t K,
                               int64_t lda, int64_t ldb, int64_t ldc,
                               tg_dtype c_dtype, hipStream_t stream);
+
+/* ---- run-time tuning cache ------------------------------------------------
+ * Exact-shape records written by the on-device sweep (the sweep's --tune
+ * mode) and read, never written, by the library: the offline-tune /
+ * online-lookup scheme of the lqnn.cn walkthrough, section 5.3.  File format
+ * (text): the first line is exactly "tg-tuning 1"; blank lines and lines
+ * starting with '#' are ignored; every other line is one record of ten
+ * whitespace-separated fields
+ *     M N K op_a op_b c_dtype fused config name tflops
+ * with op_a, op_b in {N, T}, c_dtype in {f16, f32, i32}, fused in {0, 1}
+ * (i32 only with 0), config a configuration id, name that configuration's
+ * name (tg_config_desc.name) and tflops the measured rate (informational).
+ * A record whose id names another kernel than `name` in this library, or a
+ * kernel that cannot serve its orientation or C dtype, is stale: it is
+ * skipped and counted.  A later record for the same key replaces an earlier
+ * one.  At dispatch a cached configuration that cannot run the actual
+ * pointers or leading dimensions (alignment) is passed over.
+ *
+ * If the environment variable TG_TUNING_FILE names a file, it is loaded once,
+ * before the first call that reads or changes the cache; if it does not
+ * load, the cache starts empty and one line on stderr says why.
+ *
+ * The cache is process-wide and safe to use from several threads: a load
+ * builds a new table and replaces the old one whole, so each GEMM call sees
+ * either of them.  The tables are host memory. */
+
+/* Replace the cache with the records of the file at `path`.  On success
+ * *loaded receives the number of distinct keys now cached and *skipped the
+ * number of stale records.  On failure the cache is unchanged and
+ * *error_line receives the 1-based line that could not be parsed (0 for an
+ * I/O error).  Any of the three out pointers may be NULL.
+ * Errors: TG_ERROR_INVALID_VALUE (NULL path; missing or wrong first line;
+ * a malformed record or an over-long line; more than 2^20 records),
+ * TG_ERROR_FILE (cannot open or read). */
+tg_status tg_tuning_load(const char *path, int *loaded, int *skipped, int *error_line);
+
+/* Empty the cache (the compiled tables still apply).  Always TG_SUCCESS. */
+tg_status tg_tuning_clear(void);
+
+/* Number of keys in the cache. */
+int tg_tuning_count(void);
 
 /* Library version string (static). */
 const char *tg_version(void);

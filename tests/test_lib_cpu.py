@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
 
 
 def test_status_strings_and_version():
-    for s in range(5):
+    for s in range(6):
         assert tg.tg_status_string(s).startswith("TG_")
     assert "gfx950" in tg.tg_version()
 

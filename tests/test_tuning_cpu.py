@@ -1,0 +1,376 @@
+"""Run-time tuning cache and shape-class dispatch of libtg.so, on the CPU.
+
+The cache is host logic (file parsing, key lookup, the atomic swap) and the
+dispatcher reports its choice through tg_select_config without touching a
+device, so every rule here is checked with fake, well-aligned addresses.
+"""
+import os
+import re
+import subprocess
+import sys
+import threading
+
+import pytest
+
+import tiled_dense_gemm_08_amd as tg
+from tiled_dense_gemm_08_amd import sweep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PA, PB, PC, PBIAS = 0x100000, 0x200000, 0x300000, 0x400000
+F16, F32, I32 = tg.TG_DTYPE_F16, tg.TG_DTYPE_F32, tg.TG_DTYPE_I32
+MAGIC = "tg-tuning 1"
+
+
+@pytest.fixture(autouse=True)
+def empty_cache():
+    tg.tg_tuning_clear()
+    yield
+    tg.tg_tuning_clear()
+
+
+def name(cid):
+    return tg.tg_config_info(cid)["name"]
+
+
+def ids(pred):
+    return [c["id"] for c in tg.configs() if pred(c)]
+
+
+def select(M, N, K, op_a=0, op_b=0, dtype=F16, bias=None, pa=PA, pb=PB):
+    lda = M if op_a else K
+    ldb = K if op_b else N
+    return tg.tg_select_config(pa, pb, bias, PC, M, N, K, lda, ldb, N, dtype, op_a=op_a,
+                               op_b=op_b)
+
+
+def write(tmp_path, body, fname="t.tgtune"):
+    p = tmp_path / fname
+    p.write_text(body)
+    return str(p)
+
+
+def f16_direct_all_ops():
+    return ids(lambda c: c["direct_lds"] and c["elem_bytes"] == 2 and c["ops"] == 15)
+
+
+# ------------------------------------------------------------ records --
+def test_record_overrides_dispatch_for_its_key_only(tmp_path):
+    M, N, K = 3072, 2048, 1536
+    default = select(M, N, K)
+    alt = next(c for c in f16_direct_all_ops() if c != default)
+    path = write(tmp_path, "%s\n# comment\n\n%d %d %d N N f16 0 %d %s 123.4\n"
+                 % (MAGIC, M, N, K, alt, name(alt)))
+    assert tg.load_tuning(path) == (1, 0)
+    assert tg.tg_tuning_count() == 1
+    assert select(M, N, K) == alt
+    # every other field of the key must match
+    assert select(M, N, K + 8) == default or select(M, N, K + 8) != alt
+    assert select(M, N, K, dtype=F32) != alt or default == alt
+    assert select(M, N, K, bias=PBIAS) != alt or default == alt
+    assert select(M, N, K, op_b=1) != alt or select(M, N, K, op_b=1) == default
+    tg.tg_tuning_clear()
+    assert tg.tg_tuning_count() == 0
+    assert select(M, N, K) == default
+
+
+def test_every_key_field_is_distinguished(tmp_path):
+    M, N, K = 1536, 1536, 1536
+    cands = f16_direct_all_ops()
+    assert len(cands) >= 3
+    # pick for each key a config different from what the dispatcher would
+    # choose without a record, so that a hit is visible
+    keys = [dict(op_a=0, op_b=0, dtype=F16, bias=None, tag="N N f16 0"),
+            dict(op_a=1, op_b=0, dtype=F16, bias=None, tag="T N f16 0"),
+            dict(op_a=0, op_b=1, dtype=F16, bias=None, tag="N T f16 0"),
+            dict(op_a=1, op_b=1, dtype=F16, bias=None, tag="T T f16 0"),
+            dict(op_a=0, op_b=0, dtype=F32, bias=None, tag="N N f32 0"),
+            dict(op_a=0, op_b=0, dtype=F16, bias=PBIAS, tag="N N f16 1")]
+    lines, want = [MAGIC], []
+    for i, k in enumerate(keys):
+        tag = k.pop("tag")
+        default = select(M, N, K, **k)
+        pick = [c for c in cands if c != default][i % (len(cands) - 1)]
+        lines.append("%d %d %d %s %d %s 1.0" % (M, N, K, tag, pick, name(pick)))
+        want.append((k, pick))
+    assert tg.load_tuning(write(tmp_path, "\n".join(lines) + "\n")) == (len(keys), 0)
+    for k, pick in want:
+        assert select(M, N, K, **k) == pick, k
+
+
+def test_int8_records(tmp_path):
+    i8 = ids(lambda c: c["direct_lds"] and c["elem_bytes"] == 1)
+    default = select(4096, 4096, 4096, dtype=I32)
+    alt = next(c for c in i8 if c != default)
+    path = write(tmp_path, "%s\n4096 4096 4096 N N i32 0 %d %s 2000\n" % (MAGIC, alt, name(alt)))
+    assert tg.load_tuning(path) == (1, 0)
+    assert select(4096, 4096, 4096, dtype=I32) == alt
+    assert select(4096, 4096, 4096, dtype=F16) != alt
+
+
+def test_later_record_wins(tmp_path):
+    a, b = f16_direct_all_ops()[:2]
+    path = write(tmp_path, "%s\n2048 2048 2048 N N f16 0 %d %s 1\n2048 2048 2048 N N f16 0 %d %s 2\n"
+                 % (MAGIC, a, name(a), b, name(b)))
+    assert tg.load_tuning(path) == (1, 0)
+    assert select(2048, 2048, 2048) == b
+
+
+def test_stale_records_are_skipped(tmp_path):
+    nn_only = ids(lambda c: c["direct_lds"] and c["elem_bytes"] == 2 and c["ops"] == 1)
+    i8 = ids(lambda c: c["elem_bytes"] == 1)
+    good = f16_direct_all_ops()[0]
+    body = [MAGIC,
+            "1000 1000 1000 N N f16 0 %d not_this_kernel 1" % good,              # name mismatch
+            "1000 1000 1000 N N f16 0 %d %s 1" % (tg.tg_num_configs(), name(good)),  # no such id
+            "1000 1000 1000 T N f16 0 %d %s 1" % (nn_only[0], name(nn_only[0])),  # orientation
+            "1000 1000 1000 N N f16 0 %d %s 1" % (i8[0], name(i8[0])),            # element type
+            "1000 1000 1000 N N i32 0 %d %s 1" % (good, name(good)),              # element type
+            "2000 1000 1000 N N f16 0 %d %s 1" % (good, name(good))]
+    assert tg.load_tuning(write(tmp_path, "\n".join(body) + "\n")) == (1, 5)
+    assert select(2000, 1000, 1000) == good
+
+
+def test_cached_config_that_cannot_run_the_pointers_is_passed_over(tmp_path):
+    d = f16_direct_all_ops()[0]
+    path = write(tmp_path, "%s\n1024 1024 1024 N N f16 0 %d %s 1\n" % (MAGIC, d, name(d)))
+    tg.load_tuning(path)
+    assert select(1024, 1024, 1024) == d
+    # A offset by one element: direct loads cannot take it
+    cid = select(1024, 1024, 1024, pa=PA + 2)
+    assert cid != d and not tg.tg_config_info(cid)["direct_lds"]
+
+
+# ------------------------------------------------------------- errors --
+GOOD = "2048 2048 2048 N N f16 0 {id} {name} 1.5"
+
+
+@pytest.mark.parametrize("body,line", [
+    ("", 1),
+    ("tg-tuning 2\n", 1),
+    ("# tg-tuning 1\n", 1),
+    (MAGIC + "\n2048 2048 N N f16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n# c\n" + GOOD + " extra\n", 3),
+    (MAGIC + "\n-1 2048 2048 N N f16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2x N N f16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 X N f16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N n f16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N bf16 0 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N f16 2 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N i32 1 {id} {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N f16 0 -3 {name} 1\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N f16 0 {id} {name} fast\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N f16 0 {id} {name} nan\n", 2),
+    (MAGIC + "\n2048 2048 2048 N N f16 0 {id} {name} -1\n", 2),
+    (MAGIC + "\n" + GOOD + "\n" + "9" * 2000 + "\n", 3),
+    (MAGIC + "\n99999999999 2048 2048 N N f16 0 {id} {name} 1\n", 2),
+])
+def test_malformed_file_is_rejected_and_cache_kept(tmp_path, body, line):
+    d = f16_direct_all_ops()[0]
+    keep = write(tmp_path, "%s\n1104 1112 1120 N N f16 0 %d %s 1\n" % (MAGIC, d, name(d)), "k")
+    assert tg.load_tuning(keep) == (1, 0)
+    bad = write(tmp_path, body.format(id=d, name=name(d)))
+    st, loaded, skipped, err = tg.tg_tuning_load(bad)
+    assert st == tg.TG_ERROR_INVALID_VALUE
+    assert err == line and loaded == 0 and skipped == 0
+    assert tg.tg_tuning_count() == 1 and select(1104, 1112, 1120) == d
+    with pytest.raises(tg.TgError, match="line %d" % line):
+        tg.load_tuning(bad)
+
+
+def test_missing_file_and_null_path(tmp_path):
+    st, loaded, skipped, err = tg.tg_tuning_load(str(tmp_path / "none"))
+    assert (st, loaded, skipped, err) == (tg.TG_ERROR_FILE, 0, 0, 0)
+    assert tg.tg_tuning_load(None)[0] == tg.TG_ERROR_INVALID_VALUE
+    st, loaded, skipped, err = tg.tg_tuning_load(str(tmp_path))   # a directory
+    assert st in (tg.TG_ERROR_FILE, tg.TG_ERROR_INVALID_VALUE)
+    assert "TG_ERROR_FILE" in tg.tg_status_string(tg.TG_ERROR_FILE)
+
+
+def test_sweep_writer_and_library_reader_agree(tmp_path):
+    a, b = f16_direct_all_ops()[:2]
+    i8 = ids(lambda c: c["direct_lds"] and c["elem_bytes"] == 1)[0]
+    recs = {(3000, 1000, 512, 0, 1, "f16", 1): (a, name(a), 812.25),
+            (512, 3000, 1000, 1, 0, "f32", 0): (b, name(b), 99.0),
+            (4096, 4096, 256, 0, 0, "i32", 0): (i8, name(i8), 1500.0)}
+    path = str(tmp_path / "w.tgtune")
+    sweep.write_cache(path, recs)
+    assert sweep.read_cache(path) == recs
+    assert tg.load_tuning(path) == (3, 0)
+    assert select(3000, 1000, 512, op_b=1, bias=PBIAS) == a
+    assert select(512, 3000, 1000, op_a=1, dtype=F32) == b
+    assert select(4096, 4096, 256, dtype=I32) == i8
+
+
+def test_environment_variable_loads_once(tmp_path):
+    d = f16_direct_all_ops()[1]
+    good = write(tmp_path, "%s\n1232 1240 1248 N N f16 0 %d %s 1\n" % (MAGIC, d, name(d)), "g")
+    bad = write(tmp_path, MAGIC + "\nnot a record\n", "b")
+    code = ("import tiled_dense_gemm_08_amd as tg; P=0x100000; "
+            "print(tg.tg_tuning_count(), tg.tg_select_config(P,P,None,P,1232,1240,1248,1248,"
+            "1240,1240,1))")
+    env = dict(os.environ, TG_TUNING_FILE=good)
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["1", str(d)]
+    env["TG_TUNING_FILE"] = bad
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "0"
+    assert "TG_TUNING_FILE" in out.stderr and "line 2" in out.stderr
+
+
+def test_concurrent_loads_and_lookups(tmp_path):
+    a, b = f16_direct_all_ops()[:2]
+    pa = write(tmp_path, "%s\n2560 2560 2560 N N f16 0 %d %s 1\n" % (MAGIC, a, name(a)), "a")
+    pb = write(tmp_path, "%s\n2560 2560 2560 N N f16 0 %d %s 1\n" % (MAGIC, b, name(b)), "b")
+    default = select(2560, 2560, 2560)
+    allowed = {a, b, default}
+    seen, errors = set(), []
+    stop = threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            c = select(2560, 2560, 2560)
+            seen.add(c)
+            if c not in allowed:
+                errors.append(c)
+
+    def writer():
+        for i in range(300):
+            if i % 3 == 2:
+                tg.tg_tuning_clear()
+            elif tg.tg_tuning_load(pa if i % 2 else pb)[0] != tg.TG_SUCCESS:
+                errors.append("load")
+        stop.set()
+
+    ts = [threading.Thread(target=reader) for _ in range(4)] + [threading.Thread(target=writer)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert not errors
+    assert seen <= allowed
+
+
+# ------------------------------------------------------- cost model --
+from tiled_dense_gemm_08_amd import costmodel  # noqa: E402
+
+TIMINGS = os.path.join(ROOT, "tiled_dense_gemm_08_amd", "tuning")
+CONFIGS = {c["id"]: c for c in tg.configs()}
+
+
+def exact_shapes():
+    text = open(os.path.join(ROOT, "tiled_dense_gemm_08_amd", "csrc",
+                             "tg_dispatch_table.inc")).read()
+    return {tuple(int(x) for x in m) for m in
+            re.findall(r"\{(\d+), (\d+), (\d+), 0, \d+\}", text)}
+
+
+def aligned_operands(M, N, K, op_a=0, op_b=0, es=2):
+    """Packed operands at the fake aligned addresses: 16-byte rows?"""
+    a_ld, b_ld = (M if op_a else K), (K if op_b else N)
+    a_x, b_x = (K if not op_a else M), (K if op_b else N)
+    return all((v * es) % 16 == 0 for v in (a_ld, b_ld, a_x, b_x))
+
+
+def model_choice(rows, M, N, K, cands, pad):
+    def t(c):
+        f = costmodel.row_for(rows, c, pad)
+        return (costmodel.predict(f, CONFIGS[c]["block_m"], CONFIGS[c]["block_n"], M, N, K), c)
+    return min(cands, key=t)
+
+
+def test_model_rows_are_valid():
+    rows = costmodel.read_model()
+    assert rows
+    for (c, pad), (per_cu, Ks, full, mn) in rows.items():
+        info = CONFIGS[c]
+        assert 1 <= per_cu <= 8
+        assert per_cu * info["lds_bytes"] <= 160 * 1024
+        assert Ks == sorted(set(Ks)) and Ks[0] > 0
+        assert all(v > 0 for v in full + mn)
+        # a round costs more with more K
+        assert full == sorted(full) and mn == sorted(mn), c
+        # only the register-staged kernels run on padded operands
+        assert not (pad and info["direct_lds"])
+    for c in CONFIGS.values():
+        assert (c["id"], False) in rows or (c["id"], True) in rows, c["name"]
+        if not c["direct_lds"]:
+            assert (c["id"], True) in rows, c["name"]
+
+
+def test_rounds_formula():
+    # whole rounds cost t_full each; a partial round interpolates to t_min
+    assert costmodel.rounds(512, 256) == (2.0, 0.0)
+    a, b = costmodel.rounds(320, 256)
+    assert a == pytest.approx(1.25) and b == pytest.approx(0.75)
+    a, b = costmodel.rounds(1, 256)
+    assert a == pytest.approx(1 / 256) and b == pytest.approx(255 / 256)
+    assert costmodel.n_tiles(257, 255, 256, 128) == 4
+
+
+def test_fit_recovers_known_parameters():
+    rng = __import__("random").Random(5)
+    occ, Ks, full, mn = 2, [256, 1024, 4096], [10.0, 30.0, 100.0], [4.0, 9.0, 40.0]
+    samples = []
+    for K, tf, tm in zip(Ks, full, mn):
+        for _ in range(60):
+            M, N = rng.choice(range(64, 9000, 64)), rng.choice(range(64, 9000, 64))
+            a, b = costmodel.rounds(costmodel.n_tiles(M, N, 128, 128), 256 * occ)
+            samples.append((M, N, K, a * tf + b * tm))
+    got = costmodel.fit_config(samples, 128, 128, 64 * 1024)
+    assert got[0] == occ and got[1] == Ks
+    assert got[2] == pytest.approx(full, rel=1e-6)
+    assert got[3] == pytest.approx(mn, rel=1e-6)
+    assert got[4] < 1e-9
+    # workgroups per CU never exceed what LDS holds
+    assert costmodel.fit_config(samples, 128, 128, 100 * 1024)[0] == 1
+
+
+@pytest.mark.parametrize("M,N,K", [(3072, 3072, 3072), (96, 8192, 8192), (7000, 3504, 2504),
+                                   (2816, 2816, 512), (640, 640, 8192), (12288, 12288, 1024),
+                                   (4100, 4100, 4100), (256, 256, 100000), (1, 1, 1),
+                                   (65536, 64, 64), (5000, 704, 3000), (3001, 5003, 1031)])
+def test_dispatch_evaluates_the_compiled_model(M, N, K):
+    rows = costmodel.read_model()
+    assert (M, N, K) not in exact_shapes()
+    for dtype, es in ((F16, 2), (I32, 1)):
+        pad = not aligned_operands(M, N, K, es=es)
+        cands = sorted({c for c, _ in rows if CONFIGS[c]["elem_bytes"] == es and
+                        tg.tg_config_supports(c, PA, PB, None, PC, M, N, K, K, N, N, dtype) == 1})
+        assert cands
+        assert select(M, N, K, dtype=dtype) == model_choice(rows, M, N, K, cands, pad)
+
+
+def test_transposed_problems_choose_among_kernels_that_compile_the_orientation():
+    rows = costmodel.read_model()
+    for op_a, op_b in ((1, 0), (0, 1), (1, 1)):
+        for M, N, K in ((3072, 3072, 3072), (640, 640, 8192), (8192, 512, 1024), (1000, 1000, 64)):
+            cid = select(M, N, K, op_a=op_a, op_b=op_b)
+            assert CONFIGS[cid]["ops"] >> (2 * op_a + op_b) & 1
+            pad = not aligned_operands(M, N, K, op_a, op_b)
+            lda, ldb = (M if op_a else K), (K if op_b else N)
+            cands = sorted({c for c, _ in rows if tg.tg_config_supports(
+                c, PA, PB, None, PC, M, N, K, lda, ldb, N, F16, op_a=op_a, op_b=op_b) == 1})
+            assert cid == model_choice(rows, M, N, K, cands, pad)
+
+
+@pytest.mark.parametrize("fname,mean_limit,worst_limit", [
+    ("grid_aligned.csv.gz", 1.02, 1.5),
+    ("grid_padded.csv.gz", 1.02, 1.5),
+    ("random_seed1.csv.gz", 1.02, 1.3),
+    ("random_seed2.csv.gz", 1.03, 1.4),
+    ("named_shapes.csv.gz", 1.03, 1.3),
+])
+def test_model_choice_is_close_to_the_measured_best(fname, mean_limit, worst_limit):
+    """On the recorded on-device timings, the kernel the compiled model picks
+    is on average within a few percent of the fastest one measured."""
+    rows = costmodel.read_model()
+    data = costmodel.read_timings(os.path.join(TIMINGS, fname))
+    r = costmodel.regret(data, rows, CONFIGS)
+    assert len(r) >= 10
+    v = [x[1] for x in r.values()]
+    assert sum(v) / len(v) <= mean_limit
+    assert max(v) <= worst_limit

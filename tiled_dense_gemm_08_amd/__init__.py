@@ -22,6 +22,7 @@ TG_ERROR_INVALID_VALUE = 1
 TG_ERROR_NOT_DEVICE_MEMORY = 2
 TG_ERROR_UNSUPPORTED = 3
 TG_ERROR_LAUNCH = 4
+TG_ERROR_FILE = 5
 
 TG_OP_N = 0
 TG_OP_T = 1
@@ -29,7 +30,8 @@ TG_OP_T = 1
 # every function declared in include/tg.h
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
-            "tg_gemm_with_config", "tg_version")
+            "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
+            "tg_version")
 
 
 class TgError(RuntimeError):
@@ -80,6 +82,13 @@ def _load():
     L.tg_config_supports.restype = I
     L.tg_select_config.argtypes = [I, I] + shape_args
     L.tg_select_config.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    L.tg_tuning_load.argtypes = [ctypes.c_char_p, IP, IP, IP]
+    L.tg_tuning_load.restype = I
+    L.tg_tuning_clear.argtypes = []
+    L.tg_tuning_clear.restype = I
+    L.tg_tuning_count.argtypes = []
+    L.tg_tuning_count.restype = I
     L.tg_version.argtypes = []
     L.tg_version.restype = ctypes.c_char_p
     return L
@@ -135,8 +144,33 @@ def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_
     return lib.tg_select_config(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
 
 
+def tg_tuning_load(path):
+    """Returns (status, loaded, skipped, error_line)."""
+    loaded, skipped, line = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+    st = lib.tg_tuning_load(None if path is None else os.fsencode(path), ctypes.byref(loaded),
+                            ctypes.byref(skipped), ctypes.byref(line))
+    return st, loaded.value, skipped.value, line.value
+
+
+def tg_tuning_clear():
+    return lib.tg_tuning_clear()
+
+
+def tg_tuning_count():
+    return lib.tg_tuning_count()
+
+
 def tg_version():
     return lib.tg_version().decode()
+
+
+def load_tuning(path):
+    """Load a tuning cache file (written by `sweep --tune`); raises TgError
+    naming the offending line.  Returns (loaded, skipped)."""
+    st, loaded, skipped, line = tg_tuning_load(path)
+    if st != TG_SUCCESS:
+        raise TgError(st, "tg_tuning_load(%s) line %d" % (path, line))
+    return loaded, skipped
 
 
 def configs():

@@ -10,8 +10,15 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <errno.h>
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <atomic>
+#include <memory>
 #include <mutex>
+#include <unordered_map>
 
 #include "tg.h"
 #include "tg_kernels.h"
@@ -25,6 +32,7 @@ using tg::Params;
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr int64_t kMaxSpan = int64_t(1) << 31;   // bytes a buffer descriptor may cover
+constexpr const char *kTuneMagic = "tg-tuning 1";  // first line of a tuning cache file
 
 struct Problem {
     const void *A, *B;
@@ -101,12 +109,19 @@ struct OperandShape {
     int tile;      // block_m or block_n
 };
 
+// Every 16-byte chunk of the operand's rows lies entirely inside or entirely
+// outside the operand (given a 16-byte-aligned base).
+bool chunks_aligned(const OperandShape &o, const Problem &p)
+{
+    const int64_t es = elem_size(p);
+    return (o.ld * es) % 16 == 0 && (o.kmaj ? (p.K * es) % 16 : (o.x * es) % 16) == 0;
+}
+
 bool operand_direct_ok(const OperandShape &o, const Problem &p, int bk)
 {
-    // every 16-byte chunk entirely inside or entirely outside the operand
-    const int64_t es = elem_size(p);
-    if ((o.ld * es) % 16 || (o.kmaj ? (p.K * es) % 16 : (o.x * es) % 16))
+    if (!chunks_aligned(o, p))
         return false;
+    const int64_t es = elem_size(p);
     // lane offsets of rows past the edge (x + tile rows of a k-major operand,
     // block_k + 1 rows of an mn-major one) must stay below 2^32 so that the
     // range check sees them
@@ -138,21 +153,324 @@ bool supports(const KernelConfig &c, const Problem &p)
     return operand_direct_ok(a, p, c.bk) && operand_direct_ok(b, p, c.bk);
 }
 
-// ---- configuration table (shape class -> config id), chosen offline ------
+// ---- dispatch ---------------------------------------------------------------
+// A problem is served, in this order, by: the run-time tuning cache (exact
+// shape records written by the sweep and loaded with tg_tuning_load or
+// TG_TUNING_FILE), the compiled exact-shape table, the least predicted time of
+// the compiled cost model (fitted offline to on-device timings on a grid of
+// shapes), and finally the register-staged fallback, which runs any alignment.
+// Each step is taken only if its configuration can run the problem.
 #include "tg_dispatch_table.inc"
+#include "tg_cost_model.inc"
+
+constexpr int kModelCUs = 256;   // compute units of an MI355X
+
+// Fitted time at K: piecewise linear through the grid values, the end
+// stretches extended, and never below a tenth of the smallest grid value.
+double model_interp(const int64_t *k, const double *v, int64_t K)
+{
+    int i = 0;
+    while (i + 2 < kModelNK && K > k[i + 1])
+        i++;
+    const double t = v[i] + (v[i + 1] - v[i]) * (double)(K - k[i]) / (double)(k[i + 1] - k[i]);
+    double lo = v[0];
+    for (int j = 1; j < kModelNK; j++)
+        lo = v[j] < lo ? v[j] : lo;
+    return t > 0.1 * lo ? t : 0.1 * lo;
+}
+
+// Predicted time of configuration c: tiles = ceil(M/BM) * ceil(N/BN)
+// workgroups take R = tiles / slots rounds on the chip's CUs; each full round
+// costs t_full(K), and a partial round filling a fraction f of the slots
+// costs t_min(K) + f * (t_full(K) - t_min(K)).
+double model_time(const ModelRow &r, const KernelConfig &c, const Problem &p)
+{
+    const double tiles = (double)((p.M + c.bm - 1) / c.bm) * (double)((p.N + c.bn - 1) / c.bn);
+    const double R = tiles / (double)(kModelCUs * r.per_cu);
+    const double fl = floor(R), f = R - fl;
+    double a = fl, b = 0.0;
+    if (f > 1e-12) {
+        a = fl + f;
+        b = 1.0 - f;
+    }
+    return a * model_interp(r.k, r.t_full, p.K) + b * model_interp(r.k, r.t_min, p.K);
+}
+
+// Whether the operands have the 16-byte layout the direct loads need; the
+// register-staged kernels run at a different speed on such operands, and the
+// model has a row for each case.
+bool operands_aligned(const Problem &p)
+{
+    return aligned(p.A, 16) && aligned(p.B, 16) &&
+           chunks_aligned(OperandShape{p.op_a == 0, p.M, p.lda, 0}, p) &&
+           chunks_aligned(OperandShape{p.op_b == 1, p.N, p.ldb, 0}, p);
+}
+
+bool has_model_row(int id, int padded)
+{
+    for (const ModelRow &r : kModel)
+        if (r.id == id && r.padded == padded)
+            return true;
+    return false;
+}
+
+// The modelled configuration with the least predicted time that can run the
+// problem (ties: the lower id), or -1.  A configuration's row for the
+// problem's operand layout is used, or its only row.
+int model_lookup(const Problem &p)
+{
+    const int pad = operands_aligned(p) ? 0 : 1;
+    int best = -1;
+    double best_t = 0.0;
+    for (const ModelRow &r : kModel) {
+        if (r.id < 0 || r.id >= kNumConfigs || !supports(kConfigs[r.id], p))
+            continue;
+        if (r.padded != pad && has_model_row(r.id, pad))
+            continue;
+        const double t = model_time(r, kConfigs[r.id], p);
+        if (best < 0 || t < best_t || (t == best_t && r.id < best)) {
+            best = r.id;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+// ---- run-time tuning cache ----------------------------------------------------
+// Exact-shape records, read-only once loaded: a load builds a new table and
+// swaps it in whole, so concurrent calls see either the old or the new one.
+struct TuneKey {
+    int64_t M, N, K;
+    int op_a, op_b, c_dtype, fused;
+    bool operator==(const TuneKey &o) const
+    {
+        return M == o.M && N == o.N && K == o.K && op_a == o.op_a && op_b == o.op_b &&
+               c_dtype == o.c_dtype && fused == o.fused;
+    }
+};
+
+struct TuneKeyHash {
+    size_t operator()(const TuneKey &k) const
+    {
+        uint64_t h = 0x9e3779b97f4a7c15ull;
+        for (uint64_t v : {(uint64_t)k.M, (uint64_t)k.N, (uint64_t)k.K,
+                           (uint64_t)(k.op_a | k.op_b << 1 | k.fused << 2 | k.c_dtype << 3)}) {
+            h ^= v + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+        }
+        return (size_t)h;
+    }
+};
+
+using TuneTable = std::unordered_map<TuneKey, int, TuneKeyHash>;
+
+constexpr int kMaxTuneRecords = 1 << 20;
+constexpr size_t kMaxTuneLine = 1024;
+
+std::mutex g_tune_mu;
+std::shared_ptr<const TuneTable> g_tune;   // guarded by g_tune_mu; null = empty
+std::atomic<bool> g_tune_any{false};
+std::once_flag g_tune_env_once;
+
+TuneKey tune_key(const Problem &p)
+{
+    return TuneKey{p.M, p.N, p.K, p.op_a, p.op_b, (int)p.c_dtype, p.fused ? 1 : 0};
+}
+
+bool parse_int(const char *s, int64_t lo, int64_t hi, int64_t *out)
+{
+    char *end = nullptr;
+    errno = 0;
+    const long long v = strtoll(s, &end, 10);
+    if (errno || end == s || *end != '\0' || v < lo || v > hi)
+        return false;
+    *out = v;
+    return true;
+}
+
+// One record line: M N K op_a op_b c_dtype fused config name tflops.
+// Returns 1 for a record, 0 for a stale record (the configuration id names
+// another kernel in this build, or one that cannot serve the record's
+// orientation or element type), -1 for a malformed line.
+int parse_record(char *line, TuneKey *key, int *id)
+{
+    char *tok[11];
+    int n = 0;
+    for (char *save = nullptr, *t = strtok_r(line, " \t", &save); t != nullptr;
+         t = strtok_r(nullptr, " \t", &save)) {
+        if (n == 11)
+            return -1;
+        tok[n++] = t;
+    }
+    if (n != 10)
+        return -1;
+    int64_t M, N, K, fused, cid;
+    if (!parse_int(tok[0], 0, kMaxDim, &M) || !parse_int(tok[1], 0, kMaxDim, &N) ||
+        !parse_int(tok[2], 0, kMaxDim, &K) || !parse_int(tok[6], 0, 1, &fused) ||
+        !parse_int(tok[7], 0, kMaxDim, &cid))
+        return -1;
+    int ops[2];
+    for (int i = 0; i < 2; i++) {
+        if (strcmp(tok[3 + i], "N") == 0)
+            ops[i] = TG_OP_N;
+        else if (strcmp(tok[3 + i], "T") == 0)
+            ops[i] = TG_OP_T;
+        else
+            return -1;
+    }
+    tg_dtype dt;
+    if (strcmp(tok[5], "f16") == 0)
+        dt = TG_DTYPE_F16;
+    else if (strcmp(tok[5], "f32") == 0)
+        dt = TG_DTYPE_F32;
+    else if (strcmp(tok[5], "i32") == 0)
+        dt = TG_DTYPE_I32;
+    else
+        return -1;
+    if (dt == TG_DTYPE_I32 && fused)
+        return -1;
+    char *end = nullptr;
+    const double tflops = strtod(tok[9], &end);
+    if (end == tok[9] || *end != '\0' || !(tflops >= 0.0) || tflops > 1e9)
+        return -1;
+    *key = TuneKey{M, N, K, ops[0], ops[1], (int)dt, (int)fused};
+    *id = (int)cid;
+    if (cid >= kNumConfigs)
+        return 0;
+    const KernelConfig &c = kConfigs[cid];
+    const int es = dt == TG_DTYPE_I32 ? 1 : 2;
+    if (strcmp(c.name, tok[8]) != 0 || !(c.ops & (1 << (2 * ops[0] + ops[1]))) || c.es != es)
+        return 0;
+    return 1;
+}
+
+void strip_eol(char *s)
+{
+    size_t n = strlen(s);
+    while (n > 0 && (s[n - 1] == '\n' || s[n - 1] == '\r' || s[n - 1] == ' ' || s[n - 1] == '\t'))
+        s[--n] = '\0';
+}
+
+tg_status read_tuning_file(const char *path, TuneTable *table, int *loaded, int *skipped,
+                           int *error_line)
+{
+    if (loaded)
+        *loaded = 0;
+    if (skipped)
+        *skipped = 0;
+    if (error_line)
+        *error_line = 0;
+    FILE *f = fopen(path, "r");
+    if (f == nullptr)
+        return TG_ERROR_FILE;
+    char buf[kMaxTuneLine + 2];
+    int line_no = 0, n_ok = 0, n_stale = 0;
+    tg_status st = TG_SUCCESS;
+    while (fgets(buf, sizeof(buf), f) != nullptr) {
+        line_no++;
+        if (strlen(buf) > kMaxTuneLine) {   // line longer than any record
+            st = TG_ERROR_INVALID_VALUE;
+            break;
+        }
+        strip_eol(buf);
+        if (line_no == 1) {
+            if (strcmp(buf, kTuneMagic) != 0) {
+                st = TG_ERROR_INVALID_VALUE;
+                break;
+            }
+            continue;
+        }
+        const char *q = buf;
+        while (*q == ' ' || *q == '\t')
+            q++;
+        if (*q == '\0' || *q == '#')
+            continue;
+        TuneKey key;
+        int id = -1;
+        const int r = parse_record(buf, &key, &id);
+        if (r < 0 || n_ok + n_stale >= kMaxTuneRecords) {
+            st = TG_ERROR_INVALID_VALUE;
+            break;
+        }
+        if (r == 0) {
+            n_stale++;
+            continue;
+        }
+        (*table)[key] = id;   // a later record for the same key wins
+        n_ok++;   // counts toward the record limit
+    }
+    if (st == TG_SUCCESS && ferror(f))
+        st = TG_ERROR_FILE;
+    if (st == TG_SUCCESS && line_no == 0)
+        st = TG_ERROR_INVALID_VALUE;   // empty file: no magic line
+    fclose(f);
+    if (error_line)
+        *error_line = st == TG_ERROR_INVALID_VALUE ? (line_no == 0 ? 1 : line_no) : 0;
+    if (st == TG_SUCCESS && loaded)
+        *loaded = (int)table->size();
+    if (st == TG_SUCCESS && skipped)
+        *skipped = n_stale;
+    return st;
+}
+
+void publish(std::shared_ptr<const TuneTable> t)
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune = std::move(t);
+    g_tune_any.store(g_tune != nullptr && !g_tune->empty(), std::memory_order_release);
+}
+
+// TG_TUNING_FILE: loaded once, before the first call that reads or changes
+// the cache.  A file that does not load leaves the cache empty and is
+// reported once on stderr (a GEMM call has no status for it).
+void load_env_cache()
+{
+    const char *path = getenv("TG_TUNING_FILE");
+    if (path == nullptr || *path == '\0')
+        return;
+    auto t = std::make_shared<TuneTable>();
+    int line = 0;
+    const tg_status st = read_tuning_file(path, t.get(), nullptr, nullptr, &line);
+    if (st != TG_SUCCESS) {
+        fprintf(stderr, "libtg: TG_TUNING_FILE=%s not loaded (%s, line %d)\n", path,
+                tg_status_string(st), line);
+        return;
+    }
+    publish(std::move(t));
+}
+
+void ensure_env_cache() { std::call_once(g_tune_env_once, load_env_cache); }
+
+int tuned_lookup(const Problem &p)
+{
+    ensure_env_cache();
+    if (!g_tune_any.load(std::memory_order_acquire))
+        return -1;
+    std::shared_ptr<const TuneTable> t;
+    {
+        std::lock_guard<std::mutex> lk(g_tune_mu);
+        t = g_tune;
+    }
+    if (!t)
+        return -1;
+    const auto it = t->find(tune_key(p));
+    return it == t->end() ? -1 : it->second;
+}
 
 int choose(const Problem &p)
 {
-    if (elem_size(p) == 1) {
-        const int id = dispatch_int8(p.M, p.N, p.K);
-        if (supports(kConfigs[id], p))
-            return id;
-        return dispatch_int8_fallback(p.M, p.N, p.K);
+    const int tuned = tuned_lookup(p);
+    if (tuned >= 0 && supports(kConfigs[tuned], p))
+        return tuned;
+    if (elem_size(p) == 2) {
+        const int exact = dispatch_exact(p.M, p.N, p.K, p.fused);
+        if (exact >= 0 && supports(kConfigs[exact], p))
+            return exact;
     }
-    const int id = dispatch_table_lookup(p.M, p.N, p.K, p.fused);
-    if (id >= 0 && id < kNumConfigs && supports(kConfigs[id], p))
-        return id;
-    return dispatch_fallback(p.M, p.N, p.K);
+    const int modelled = model_lookup(p);
+    if (modelled >= 0)
+        return modelled;
+    return elem_size(p) == 1 ? dispatch_int8_fallback(p.M, p.N, p.K)
+                             : dispatch_fallback(p.M, p.N, p.K);
 }
 
 // ---- device checks (HIP calls) -------------------------------------------
@@ -306,6 +624,7 @@ const char *tg_status_string(tg_status s)
     case TG_ERROR_NOT_DEVICE_MEMORY: return "TG_ERROR_NOT_DEVICE_MEMORY: pointer is not device memory of the current device";
     case TG_ERROR_UNSUPPORTED: return "TG_ERROR_UNSUPPORTED: device or problem not supported";
     case TG_ERROR_LAUNCH: return "TG_ERROR_LAUNCH: kernel launch failed";
+    case TG_ERROR_FILE: return "TG_ERROR_FILE: file cannot be opened or read";
     }
     return "unknown tg_status";
 }
@@ -355,6 +674,35 @@ int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const
     return choose(p);
 }
 
-const char *tg_version(void) { return "tg 0.2.0 (gfx950)"; }
+tg_status tg_tuning_load(const char *path, int *loaded, int *skipped, int *error_line)
+{
+    ensure_env_cache();
+    if (path == nullptr) {
+        if (error_line)
+            *error_line = 0;
+        return TG_ERROR_INVALID_VALUE;
+    }
+    auto t = std::make_shared<TuneTable>();
+    const tg_status st = read_tuning_file(path, t.get(), loaded, skipped, error_line);
+    if (st == TG_SUCCESS)
+        publish(std::move(t));
+    return st;
+}
+
+tg_status tg_tuning_clear(void)
+{
+    ensure_env_cache();
+    publish(nullptr);
+    return TG_SUCCESS;
+}
+
+int tg_tuning_count(void)
+{
+    ensure_env_cache();
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    return g_tune ? (int)g_tune->size() : 0;
+}
+
+const char *tg_version(void) { return "tg 0.3.0 (gfx950)"; }
 
 }  // extern "C"

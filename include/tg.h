@@ -47,6 +47,7 @@
 #ifndef TG_H
 #define TG_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -106,6 +107,54 @@ tg_status tg_gemm_ex(tg_op op_a, tg_op op_b, const void *A, const void *B,
                      int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc,
                      tg_dtype c_dtype, hipStream_t stream);
+
+/* ---- split-K: K cut into slices, with a caller-owned workspace ------------
+ * For problems with few output tiles and a long K (M*N small next to the
+ * 256 CUs, K large), one workgroup per output tile leaves most of the chip
+ * idle.  These calls cut K into `splits` slices of k_split elements (K/splits
+ * rounded up to the kernel's K step; fewer slices when K is short), run every
+ * slice's product as its own set of workgroups, each writing an fp32 (int32
+ * for int8 operands) partial product of C to the workspace, and then sum the
+ * partials in slice order, add the bias, apply ReLU and convert to C's type
+ * in a second kernel on the same stream.  The order is fixed, so a result is
+ * reproducible; it may differ from the unsliced call's by fp32 rounding (for
+ * integer inputs and int8 operands it is exact and equal).  The product is
+ * the one defined at the top of this file; only the grouping of the K sum
+ * changes.
+ *
+ * workspace: device memory of the current device, 16-byte aligned, not
+ * overlapping A, B, C or bias, of at least tg_splitk_workspace_bytes(M, N,
+ * slices) bytes for the slice count used; owned by the caller, who must keep
+ * it alive and not reuse it until the stream has passed the call.  Calls
+ * that share a workspace must be ordered (same stream, or synchronised). */
+
+/* Workspace bytes for `splits` slices: splits * M * N * 4 (0 if splits <= 1
+ * or M, N <= 0; 0 also for splits > 64, which the calls reject). */
+size_t tg_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
+
+/* As tg_gemm_ex (and tg_gemm_with_config when config_id >= 0), computed in K
+ * slices.  config_id: -1 = the dispatcher's choice.  splits: 0 = chosen by
+ * the dispatcher's cost model among 1 (no slicing) and 2..32 slices whose
+ * partials fit in workspace_bytes (with a NULL workspace only 1); 1 = no
+ * slicing (then the workspace is not used); 2..64 = that many slices.
+ * Additional errors: TG_ERROR_INVALID_VALUE for splits outside 0..64, or
+ * when slicing is used and the workspace is NULL, not 16-byte aligned or too
+ * small; TG_ERROR_NOT_DEVICE_MEMORY for a workspace that is not device memory
+ * of the current device. */
+tg_status tg_gemm_splitk(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
+                         const void *B, const float *bias, void *C,
+                         int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The configuration and slice count tg_gemm_splitk(-1, 0, ...) would use
+ * with a workspace of workspace_bytes (*splits = 1: no slicing; for an empty
+ * problem *config_id = -1).  Touches no device state; returns
+ * TG_ERROR_INVALID_VALUE for invalid arguments, as the call would. */
+tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                           const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                           size_t workspace_bytes, int *config_id, int *splits);
 
 /* Static, human-readable name of a status code. */
 const char *tg_status_string(tg_status s);

@@ -1,0 +1,105 @@
+"""Split-K entry points of libtg.so on the CPU: argument and workspace
+checks happen before any device call, and the dispatcher's choice of
+configuration and slice count (tg_select_splitk) is checked against
+recorded on-device timings."""
+import os
+
+import pytest
+
+import tiled_dense_gemm_08_amd as tg
+from tiled_dense_gemm_08_amd import costmodel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TIMINGS = os.path.join(ROOT, "tiled_dense_gemm_08_amd", "tuning")
+PA, PB, PC, PBIAS, PW = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+F16, F32, I32 = tg.TG_DTYPE_F16, tg.TG_DTYPE_F32, tg.TG_DTYPE_I32
+CONFIGS = {c["id"]: c for c in tg.configs()}
+
+
+def select(M, N, K, ws_bytes, dtype=F16, op_a=0, op_b=0, bias=None):
+    lda, ldb = (M if op_a else K), (K if op_b else N)
+    return tg.tg_select_splitk(PA, PB, bias, PC, M, N, K, lda, ldb, N, dtype, ws_bytes,
+                               op_a=op_a, op_b=op_b)
+
+
+def test_workspace_bytes():
+    assert tg.tg_splitk_workspace_bytes(640, 640, 8) == 8 * 640 * 640 * 4
+    assert tg.tg_splitk_workspace_bytes(640, 640, 1) == 0
+    assert tg.tg_splitk_workspace_bytes(0, 640, 8) == 0
+    assert tg.tg_splitk_workspace_bytes(640, 640, 65) == 0
+
+
+@pytest.mark.parametrize("splits,ws,nbytes", [
+    (-1, PW, 1 << 30),            # splits out of range
+    (65, PW, 1 << 30),
+    (4, None, 0),                 # slicing without a workspace
+    (4, PW, 4 * 640 * 640 * 4 - 4),   # too small
+    (4, PW + 8, 1 << 30),         # not 16-byte aligned
+])
+def test_invalid_split_arguments_rejected_without_gpu(splits, ws, nbytes):
+    st = tg.tg_gemm_splitk(-1, splits, PA, PB, None, PC, 640, 640, 8192, 8192, 640, 640, F32,
+                           ws, nbytes)
+    assert st == tg.TG_ERROR_INVALID_VALUE
+
+
+def test_split_validation_follows_the_plain_call():
+    # the problem's own errors come first, whatever the slicing
+    assert tg.tg_gemm_splitk(-1, 4, PA, PB, None, PC, -1, 640, 8192, 8192, 640, 640, F32, PW,
+                             1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_splitk(-1, 4, PA, PB, PBIAS, PC, 64, 64, 64, 64, 64, 64, I32, PW,
+                             1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_splitk(tg.tg_num_configs(), 4, PA, PB, None, PC, 64, 64, 64, 64, 64, 64,
+                             F32, PW, 1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    # empty problems succeed without a workspace or a device
+    assert tg.tg_gemm_splitk(-1, 4, PA, PB, None, PC, 0, 640, 8192, 8192, 640, 640, F32, None,
+                             0) == tg.TG_SUCCESS
+
+
+def test_no_workspace_means_no_slicing():
+    for M, N, K in ((640, 640, 8192), (128, 128, 32768), (8192, 8192, 8192)):
+        st, cid, sp = select(M, N, K, 0)
+        assert st == tg.TG_SUCCESS and sp == 1
+        assert cid == tg.tg_select_config(PA, PB, None, PC, M, N, K, K, N, N, F16)
+
+
+def test_slicing_only_where_it_pays():
+    # few tiles, long K: sliced; the chip already full: not sliced
+    assert select(128, 128, 32768, 1 << 30)[2] > 1
+    assert select(640, 640, 8192, 1 << 30)[2] > 1
+    assert select(256, 256, 32768, 1 << 30, dtype=I32)[2] > 1
+    assert select(8192, 8192, 8192, 1 << 30)[2] == 1
+    assert select(4096, 11008, 4096, 1 << 30, bias=PBIAS)[2] == 1
+    # the workspace bounds the slice count
+    st, cid, sp = select(640, 640, 8192, tg.tg_splitk_workspace_bytes(640, 640, 2))
+    assert sp in (1, 2)
+
+
+def test_choice_is_a_kernel_that_can_run_it():
+    for op_a, op_b in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        for dtype, es in ((F16, 2), (I32, 1)):
+            st, cid, sp = select(512, 768, 20000 if es == 2 else 20016, 1 << 30, dtype, op_a, op_b)
+            assert st == tg.TG_SUCCESS and 1 <= sp <= 64
+            info = CONFIGS[cid]
+            assert info["elem_bytes"] == es and info["ops"] >> (2 * op_a + op_b) & 1
+
+
+@pytest.mark.parametrize("fname,mean_limit,worst_limit", [
+    ("split_grid.csv.gz", 1.03, 1.25),
+    ("split_random_seed3.csv.gz", 1.07, 1.45),
+])
+def test_split_choice_is_close_to_the_measured_best(fname, mean_limit, worst_limit):
+    """The configuration and slice count the library picks, looked up in the
+    recorded timings of every kernel at every slice count, against the
+    fastest of them."""
+    t, _ = costmodel.read_split_timings(os.path.join(TIMINGS, fname))
+    ratios = []
+    for (dt, layout, M, N, K), per in t.items():
+        op_a, op_b = "nt".index(layout[0]), "nt".index(layout[1])
+        dtype = {"f16": F16, "f32": F32, "i32": I32}[dt]
+        st, cid, sp = select(M, N, K, 1 << 34, dtype, op_a, op_b)
+        assert st == tg.TG_SUCCESS
+        if (cid, sp) in per:
+            ratios.append(per[(cid, sp)] / min(per.values()))
+    assert len(ratios) >= 0.9 * len(t)
+    assert sum(ratios) / len(ratios) <= mean_limit
+    assert max(ratios) <= worst_limit

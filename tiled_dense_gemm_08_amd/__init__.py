@@ -31,7 +31,7 @@ TG_OP_T = 1
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
-            "tg_version")
+            "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk", "tg_version")
 
 
 class TgError(RuntimeError):
@@ -83,6 +83,13 @@ def _load():
     L.tg_select_config.argtypes = [I, I] + shape_args
     L.tg_select_config.restype = I
     IP = ctypes.POINTER(ctypes.c_int)
+    SZ = ctypes.c_size_t
+    L.tg_splitk_workspace_bytes.argtypes = [I64, I64, I]
+    L.tg_splitk_workspace_bytes.restype = SZ
+    L.tg_gemm_splitk.argtypes = [I, I, I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P, SZ, P]
+    L.tg_gemm_splitk.restype = I
+    L.tg_select_splitk.argtypes = [I, I] + shape_args + [SZ, IP, IP]
+    L.tg_select_splitk.restype = I
     L.tg_tuning_load.argtypes = [ctypes.c_char_p, IP, IP, IP]
     L.tg_tuning_load.restype = I
     L.tg_tuning_clear.argtypes = []
@@ -142,6 +149,25 @@ def tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype
 def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_N,
                      op_b=TG_OP_N):
     return lib.tg_select_config(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+
+
+def tg_splitk_workspace_bytes(M, N, splits):
+    return lib.tg_splitk_workspace_bytes(M, N, splits)
+
+
+def tg_gemm_splitk(config_id, splits, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                   workspace, workspace_bytes, stream=0, op_a=TG_OP_N, op_b=TG_OP_N):
+    return lib.tg_gemm_splitk(config_id, splits, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
+                              c_dtype, workspace, workspace_bytes, stream or None)
+
+
+def tg_select_splitk(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, workspace_bytes,
+                     op_a=TG_OP_N, op_b=TG_OP_N):
+    """Returns (status, config_id, splits)."""
+    cid, sp = ctypes.c_int(-2), ctypes.c_int(-2)
+    st = lib.tg_select_splitk(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                              workspace_bytes, ctypes.byref(cid), ctypes.byref(sp))
+    return st, cid.value, sp.value
 
 
 def tg_tuning_load(path):
@@ -213,13 +239,17 @@ def _operand(t, name):
     raise ValueError("%s must be row-major or a transposed row-major view" % name)
 
 
-def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
+def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None, workspace=None,
+         splits=0):
     """C = A.B (or max(A.B + bias, 0) when bias is given) with libtg.
 
     a: (M, K) float16, b: (K, N) float16 on the current device, each row-major
     or a transposed view of a row-major array (passed with TG_OP_T, no copy);
     out: optional preallocated (M, N) float16/float32 row-major tensor.
     config: None (dispatcher's choice) or a configuration id.
+    workspace: optional device tensor (any dtype, contiguous) that allows the
+    K-sliced (split-K) path, tg_gemm_splitk; splits: 0 lets the dispatcher
+    choose, n >= 1 forces n slices (needs a workspace when n > 1).
     """
     import torch
     if a.dtype != torch.float16 or b.dtype != torch.float16:
@@ -242,7 +272,15 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
             raise ValueError("bias must be a contiguous float32 vector of length N")
         pbias = bias.data_ptr()
     s = (stream if stream is not None else torch.cuda.current_stream(a.device)).cuda_stream
-    if config is not None:
+    if workspace is not None or splits:
+        pw, nw = 0, 0
+        if workspace is not None:
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
+            pw, nw = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = tg_gemm_splitk(-1 if config is None else config, splits, pa, pb, pbias or None, pc,
+                            M, N, K, lda, ldb, ldc, code, pw or None, nw, s, op_a=op_a, op_b=op_b)
+    elif config is not None:
         st = tg_gemm_with_config(config, pa, pb, pbias or None, pc, M, N, K, lda, ldb, ldc,
                                  code, s, op_a=op_a, op_b=op_b)
     elif op_a or op_b:
@@ -256,5 +294,7 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None):
     return out
 
 
-def gemm_bias_relu(a, b, bias, out=None, out_dtype=None, config=None, stream=None):
-    return gemm(a, b, out=out, out_dtype=out_dtype, bias=bias, config=config, stream=stream)
+def gemm_bias_relu(a, b, bias, out=None, out_dtype=None, config=None, stream=None,
+                   workspace=None, splits=0):
+    return gemm(a, b, out=out, out_dtype=out_dtype, bias=bias, config=config, stream=stream,
+                workspace=workspace, splits=splits)

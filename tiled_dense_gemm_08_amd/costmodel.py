@@ -67,6 +67,35 @@ def write_timings(path, timings):
                 w.writerow(list(key) + [c, "%.3f" % us])
 
 
+def write_split_timings(path, rows):
+    """rows: {(dtype, layout, M, N, K): {(config, slices): us, ("auto", config,
+    slices): us}} -> CSV with a slices column; the dispatcher's own choice is
+    written with config "auto:<id>"."""
+    with _open_text(path, "w") as f:
+        w = csv.writer(f)
+        w.writerow(["dtype", "layout", "M", "N", "K", "config", "slices", "us"])
+        for key in sorted(rows):
+            for k, us in sorted(rows[key].items(), key=lambda kv: str(kv[0])):
+                if k[0] == "auto":
+                    w.writerow(list(key) + ["auto:%d" % k[1], k[2], "%.3f" % us])
+                else:
+                    w.writerow(list(key) + [k[0], k[1], "%.3f" % us])
+
+
+def read_split_timings(path):
+    """{(dtype, layout, M, N, K): {(config, slices): us}}, and the dispatcher's
+    choices {(dtype, layout, M, N, K): (config, slices, us)}."""
+    out, auto = {}, {}
+    with _open_text(path, "r") as f:
+        for r in csv.DictReader(f):
+            key = (r["dtype"], r["layout"], int(r["M"]), int(r["N"]), int(r["K"]))
+            if r["config"].startswith("auto:"):
+                auto[key] = (int(r["config"][5:]), int(r["slices"]), float(r["us"]))
+            else:
+                out.setdefault(key, {})[(int(r["config"]), int(r["slices"]))] = float(r["us"])
+    return out, auto
+
+
 def rounds(tiles, slots):
     """Coefficients of (T_full, T_min) for `tiles` workgroups on `slots`."""
     R = tiles / slots

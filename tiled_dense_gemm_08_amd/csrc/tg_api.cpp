@@ -183,17 +183,26 @@ double model_interp(const int64_t *k, const double *v, int64_t K)
 // workgroups take R = tiles / slots rounds on the chip's CUs; each full round
 // costs t_full(K), and a partial round filling a fraction f of the slots
 // costs t_min(K) + f * (t_full(K) - t_min(K)).
-double model_time(const ModelRow &r, const KernelConfig &c, const Problem &p)
+double model_rounds_time(const ModelRow &r, double workgroups, int64_t K)
 {
-    const double tiles = (double)((p.M + c.bm - 1) / c.bm) * (double)((p.N + c.bn - 1) / c.bn);
-    const double R = tiles / (double)(kModelCUs * r.per_cu);
+    const double R = workgroups / (double)(kModelCUs * r.per_cu);
     const double fl = floor(R), f = R - fl;
     double a = fl, b = 0.0;
     if (f > 1e-12) {
         a = fl + f;
         b = 1.0 - f;
     }
-    return a * model_interp(r.k, r.t_full, p.K) + b * model_interp(r.k, r.t_min, p.K);
+    return a * model_interp(r.k, r.t_full, K) + b * model_interp(r.k, r.t_min, K);
+}
+
+double n_tiles(const KernelConfig &c, const Problem &p)
+{
+    return (double)((p.M + c.bm - 1) / c.bm) * (double)((p.N + c.bn - 1) / c.bn);
+}
+
+double model_time(const ModelRow &r, const KernelConfig &c, const Problem &p)
+{
+    return model_rounds_time(r, n_tiles(c, p), p.K);
 }
 
 // Whether the operands have the 16-byte layout the direct loads need; the
@@ -214,18 +223,24 @@ bool has_model_row(int id, int padded)
     return false;
 }
 
+// The model row to use for configuration `r.id` on this problem: its row for
+// the problem's operand layout, or its only row.
+bool row_applies(const ModelRow &r, const Problem &p, int pad)
+{
+    if (r.id < 0 || r.id >= kNumConfigs || !supports(kConfigs[r.id], p))
+        return false;
+    return r.padded == pad || !has_model_row(r.id, pad);
+}
+
 // The modelled configuration with the least predicted time that can run the
-// problem (ties: the lower id), or -1.  A configuration's row for the
-// problem's operand layout is used, or its only row.
+// problem (ties: the lower id), or -1.
 int model_lookup(const Problem &p)
 {
     const int pad = operands_aligned(p) ? 0 : 1;
     int best = -1;
     double best_t = 0.0;
     for (const ModelRow &r : kModel) {
-        if (r.id < 0 || r.id >= kNumConfigs || !supports(kConfigs[r.id], p))
-            continue;
-        if (r.padded != pad && has_model_row(r.id, pad))
+        if (!row_applies(r, p, pad))
             continue;
         const double t = model_time(r, kConfigs[r.id], p);
         if (best < 0 || t < best_t || (t == best_t && r.id < best)) {
@@ -515,34 +530,13 @@ tg_status check_pointer(const void *ptr, int dev)
     return TG_SUCCESS;
 }
 
-tg_status run(int config_id, const Problem &p, hipStream_t stream)
+// Kernel arguments of configuration cfg for problem p (no K slicing).
+tg_status make_params(const KernelConfig &cfg, const Problem &p, Params *out)
 {
-    tg_status st = validate(p);
-    if (st != TG_SUCCESS)
-        return st;
-    if (config_id < -1 || config_id >= kNumConfigs)
-        return TG_ERROR_INVALID_VALUE;
-    if (p.M == 0 || p.N == 0)
-        return TG_SUCCESS;
-    const int id = config_id >= 0 ? config_id : choose(p);
-    const KernelConfig &cfg = kConfigs[id];
-    if (!supports(cfg, p))
-        return TG_ERROR_UNSUPPORTED;
-
-    int dev = 0;
-    if ((st = check_device(&dev)) != TG_SUCCESS)
-        return st;
-    const bool need_ab = p.K > 0;
-    if ((need_ab && ((st = check_pointer(p.A, dev)) != TG_SUCCESS ||
-                     (st = check_pointer(p.B, dev)) != TG_SUCCESS)) ||
-        (st = check_pointer(p.C, dev)) != TG_SUCCESS ||
-        (p.fused && (st = check_pointer(p.bias, dev)) != TG_SUCCESS))
-        return st;
-
-    Params k;
+    Params &k = *out;
     memset(&k, 0, sizeof(k));
-    k.A = static_cast<const _Float16 *>(p.A);
-    k.B = static_cast<const _Float16 *>(p.B);
+    k.A = p.A;
+    k.B = p.B;
     k.bias = p.bias;
     k.C = p.C;
     k.M = (int)p.M;
@@ -564,15 +558,225 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     k.vec_store = (p.ldc % 4 == 0) && aligned(p.C, 4 * c_elem);
     k.line_store = ((p.ldc * c_elem) % 16 == 0) && aligned(p.C, 16);
     k.vec_bias = p.fused && aligned(p.bias, 16);
+    k.splits = 1;
     if ((int64_t)k.tiles_m * k.tiles_n > kMaxDim)
         return TG_ERROR_UNSUPPORTED;
+    return TG_SUCCESS;
+}
 
+tg_status check_problem_pointers(const Problem &p, int *dev)
+{
+    tg_status st;
+    if ((st = check_device(dev)) != TG_SUCCESS)
+        return st;
+    const bool need_ab = p.K > 0;
+    if ((need_ab && ((st = check_pointer(p.A, *dev)) != TG_SUCCESS ||
+                     (st = check_pointer(p.B, *dev)) != TG_SUCCESS)) ||
+        (st = check_pointer(p.C, *dev)) != TG_SUCCESS ||
+        (p.fused && (st = check_pointer(p.bias, *dev)) != TG_SUCCESS))
+        return st;
+    return TG_SUCCESS;
+}
+
+tg_status launch_config(int id, const Params &k, bool f16_out, bool bias, hipStream_t stream)
+{
     (void)hipGetLastError();   // do not report an earlier, unrelated error
     const tg::LaunchFn launch = tg::config_launch(id);
     if (launch == nullptr)
         return TG_ERROR_UNSUPPORTED;
-    const hipError_t e = launch(k, p.c_dtype == TG_DTYPE_F16, p.fused, stream);
-    return e == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
+    return launch(k, f16_out, bias, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
+}
+
+tg_status run(int config_id, const Problem &p, hipStream_t stream)
+{
+    tg_status st = validate(p);
+    if (st != TG_SUCCESS)
+        return st;
+    if (config_id < -1 || config_id >= kNumConfigs)
+        return TG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0)
+        return TG_SUCCESS;
+    const int id = config_id >= 0 ? config_id : choose(p);
+    const KernelConfig &cfg = kConfigs[id];
+    if (!supports(cfg, p))
+        return TG_ERROR_UNSUPPORTED;
+    int dev = 0;
+    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
+        return st;
+    Params k;
+    if ((st = make_params(cfg, p, &k)) != TG_SUCCESS)
+        return st;
+    return launch_config(id, k, p.c_dtype == TG_DTYPE_F16, p.fused, stream);
+}
+
+// ---- split-K ------------------------------------------------------------------
+// K is cut into slices of k_split elements (a multiple of the configuration's
+// K step); every slice's product runs as its own row of workgroups and
+// writes an fp32 (int32) partial product to the caller's workspace; a second
+// kernel sums the partials in slice order, adds the bias, applies ReLU and
+// converts.  The order is fixed, so results are reproducible run to run.
+constexpr int kMaxSplits = 64;
+constexpr int kSplitCandidates[] = {2, 3, 4, 6, 8, 12, 16, 24, 32};
+// Cost of slicing on top of the sliced GEMM's modelled rounds: a fixed part
+// (the second launch), the bytes the reduction moves at an effective rate,
+// and a per-slice part (each slice's prologue and partial write).  Fitted to
+// on-device timings of every kernel at 2..32 slices on shapes with
+// M, N in 128..2048 and K in 2048..32768 (microseconds, bytes/us).
+constexpr double kReduceFixedUs = 4.5;
+constexpr double kReduceBytesPerUs = 4.5e6;
+constexpr double kSliceUs = 0.3;
+
+int64_t slice_k(int64_t K, int splits, int bk)
+{
+    const int64_t per = (K + splits - 1) / splits;
+    return (per + bk - 1) / bk * bk;
+}
+
+int64_t slice_count(int64_t K, int64_t k_split) { return k_split > 0 ? (K + k_split - 1) / k_split : 1; }
+
+int64_t partial_bytes(const Problem &p, int64_t slices) { return slices * p.M * p.N * 4; }
+
+double reduce_time(const Problem &p, int64_t slices)
+{
+    const double c_bytes = p.c_dtype == TG_DTYPE_F16 ? 2.0 : 4.0;
+    const double bytes = (double)slices * (double)p.M * (double)p.N * 4.0 +
+                         (double)p.M * (double)p.N * c_bytes;
+    return kReduceFixedUs + bytes / kReduceBytesPerUs + kSliceUs * (double)slices;
+}
+
+struct SplitChoice {
+    int id;
+    int64_t slices;    // 1: no K slicing
+    int64_t k_split;   // K elements per slice
+    double t;
+};
+
+// Least predicted time over the modelled configurations that can run the
+// problem and the slice counts whose partials fit in ws_bytes; `only_id` /
+// `only_splits` restrict the search (-1 / 0: free).  Returns id -1 when no
+// modelled configuration applies.
+SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int only_splits)
+{
+    const int pad = operands_aligned(p) ? 0 : 1;
+    SplitChoice best{-1, 1, p.K, 0.0};
+    for (const ModelRow &r : kModel) {
+        if ((only_id >= 0 && r.id != only_id) || !row_applies(r, p, pad))
+            continue;
+        const KernelConfig &c = kConfigs[r.id];
+        auto consider = [&](int64_t slices, int64_t kk) {
+            const double t = slices > 1
+                                 ? model_rounds_time(r, n_tiles(c, p) * (double)slices, kk) +
+                                       reduce_time(p, slices)
+                                 : model_time(r, c, p);
+            if (best.id < 0 || t < best.t ||
+                (t == best.t && (slices < best.slices || (slices == best.slices && r.id < best.id))))
+                best = SplitChoice{r.id, slices, kk, t};
+        };
+        if (only_splits <= 1)
+            consider(1, p.K);
+        if (only_splits == 1)
+            continue;
+        const int one[] = {only_splits};
+        const int *cand = only_splits > 1 ? one : kSplitCandidates;
+        const int ncand = only_splits > 1 ? 1 : (int)(sizeof(kSplitCandidates) / sizeof(int));
+        for (int i = 0; i < ncand; i++) {
+            const int64_t kk = slice_k(p.K, cand[i], c.bk);
+            const int64_t slices = slice_count(p.K, kk);
+            if (slices <= 1 || (size_t)partial_bytes(p, slices) > ws_bytes)
+                continue;
+            consider(slices, kk);
+        }
+    }
+    return best;
+}
+
+tg_status run_split(int config_id, int splits, const Problem &p, void *ws, size_t ws_bytes,
+                    hipStream_t stream, int *chosen_id, int *chosen_slices, bool launch)
+{
+    tg_status st = validate(p);
+    if (st != TG_SUCCESS)
+        return st;
+    if (config_id < -1 || config_id >= kNumConfigs || splits < 0 || splits > kMaxSplits)
+        return TG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0) {
+        if (chosen_id)
+            *chosen_id = -1;
+        if (chosen_slices)
+            *chosen_slices = 1;
+        return TG_SUCCESS;
+    }
+    if (config_id >= 0 && !supports(kConfigs[config_id], p))
+        return TG_ERROR_UNSUPPORTED;
+    int id = config_id;
+    int64_t slices = 1, k_split = p.K;
+    if (splits == 0 && p.K > 0) {
+        // the dispatcher's choice, K slicing included; exact records of the
+        // tuning cache and compiled table still decide an unsliced call
+        const SplitChoice sc = choose_split(p, ws ? ws_bytes : 0, config_id, 0);
+        if (sc.id >= 0) {
+            id = sc.id;
+            slices = sc.slices;
+            k_split = sc.k_split;
+        }
+        if (slices <= 1 && config_id < 0)
+            id = choose(p);
+    } else if (splits > 1 && p.K > 0) {
+        if (id < 0) {
+            const SplitChoice sc = choose_split(p, SIZE_MAX, -1, splits);
+            id = sc.id >= 0 ? sc.id : choose(p);
+        }
+        k_split = slice_k(p.K, splits, kConfigs[id].bk);
+        slices = slice_count(p.K, k_split);
+    }
+    if (id < 0)
+        id = choose(p);
+    if (chosen_id)
+        *chosen_id = id;
+    if (chosen_slices)
+        *chosen_slices = (int)slices;
+    if (!launch)
+        return TG_SUCCESS;
+    if (slices <= 1)
+        return run(id, p, stream);
+
+    const KernelConfig &cfg = kConfigs[id];
+    if (ws == nullptr || !aligned(ws, 16) || (size_t)partial_bytes(p, slices) > ws_bytes)
+        return TG_ERROR_INVALID_VALUE;
+    int dev = 0;
+    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS ||
+        (st = check_pointer(ws, dev)) != TG_SUCCESS)
+        return st;
+    // the slices' partial products: M x N, leading dimension N, fp32 (int32)
+    Problem part = p;
+    part.C = ws;
+    part.ldc = p.N;
+    part.bias = nullptr;
+    part.fused = false;
+    part.c_dtype = elem_size(p) == 1 ? TG_DTYPE_I32 : TG_DTYPE_F32;
+    Params k;
+    if ((st = make_params(cfg, part, &k)) != TG_SUCCESS)
+        return st;
+    k.splits = (int)slices;
+    k.k_split = (int)k_split;
+    k.c_slice_bytes = p.M * p.N * 4;
+    if ((st = launch_config(id, k, false, false, stream)) != TG_SUCCESS)
+        return st;
+    tg::ReduceParams r;
+    r.ws = ws;
+    r.slice_elems = p.M * p.N;
+    r.bias = p.fused ? p.bias : nullptr;
+    r.C = p.C;
+    r.M = (int)p.M;
+    r.N = (int)p.N;
+    r.ldc = (int)p.ldc;
+    r.splits = (int)slices;
+    r.vec_ws = p.N % 4 == 0;
+    const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
+    r.vec_c = p.ldc % 4 == 0 && aligned(p.C, 4 * c_elem);
+    const tg::OutKind kind = p.c_dtype == TG_DTYPE_F16   ? tg::kOutF16
+                             : p.c_dtype == TG_DTYPE_F32 ? tg::kOutF32
+                                                         : tg::kOutI32;
+    return tg::launch_splitk_reduce(r, kind, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
 }
 
 }  // namespace
@@ -703,6 +907,37 @@ int tg_tuning_count(void)
     return g_tune ? (int)g_tune->size() : 0;
 }
 
-const char *tg_version(void) { return "tg 0.3.0 (gfx950)"; }
+size_t tg_splitk_workspace_bytes(int64_t M, int64_t N, int splits)
+{
+    if (M <= 0 || N <= 0 || splits <= 1 || splits > kMaxSplits)
+        return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * 4;
+}
+
+tg_status tg_gemm_splitk(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
+                         const void *B, const float *bias, void *C, int64_t M, int64_t N,
+                         int64_t K, int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return run_split(config_id, splits,
+                     Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
+                             op_a, op_b},
+                     workspace, workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                           const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                           size_t workspace_bytes, int *config_id, int *splits)
+{
+    // a stand-in workspace address: the choice depends only on its size
+    void *ws = workspace_bytes ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    return run_split(-1, 0,
+                     Problem{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype,
+                             bias != nullptr, op_a, op_b},
+                     ws, workspace_bytes, nullptr, config_id, splits, false);
+}
+
+const char *tg_version(void) { return "tg 0.4.0 (gfx950)"; }
 
 }  // extern "C"

@@ -23,9 +23,32 @@ struct Params {
     int vec_store;   // C rows allow 4-element vector stores (alignment)
     int line_store;  // C rows allow 16-byte stores: staged, full-line epilogue
     int vec_bias;    // bias allows 16-byte loads
+    // K slicing (split-K), used when splits > 1: workgroup row blockIdx.y = z
+    // multiplies the K range [z k_split, min((z + 1) k_split, K)) and writes
+    // its fp32 (int32 for int8 operands) partial product, without bias, to
+    // C + z * c_slice_bytes with leading dimension ldc.
+    int splits;
+    int k_split;
+    int64_t c_slice_bytes;
 };
 
 typedef hipError_t (*LaunchFn)(const Params &p, bool f16_out, bool bias, hipStream_t s);
+
+// Sum of the K slices' partial products, in slice order, then bias + ReLU
+// and the conversion to C's type.
+enum OutKind { kOutF16 = 0, kOutF32 = 1, kOutI32 = 2 };
+
+struct ReduceParams {
+    const void *ws;        // splits slices of M x N partials (fp32, or int32 for kOutI32)
+    int64_t slice_elems;   // elements between slices
+    const float *bias;     // nullptr: plain sum
+    void *C;
+    int M, N, ldc, splits;
+    int vec_ws;            // slices allow 16-byte loads of 4 partials
+    int vec_c;             // C rows allow 4-element vector stores
+};
+
+hipError_t launch_splitk_reduce(const ReduceParams &r, OutKind out, hipStream_t s);
 
 struct KernelConfig {
     int id;

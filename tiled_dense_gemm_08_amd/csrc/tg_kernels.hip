@@ -861,9 +861,43 @@ __device__ __forceinline__ void pipe_body(const Params &p, DirectLoader<C> &ld, 
     }
 }
 
-template <class C, typename OutT, bool BIAS>
+// Arguments of K slice z = blockIdx.y (split-K): A and B start at the
+// slice's first K element, K is the slice's length, the buffer ranges end
+// where the operand ends -- for an operand whose rows run along K (mn-major),
+// after the slice's last K row, so that the copies of a partial last K step
+// read zeros instead of the next slice's rows -- and C is the slice's own
+// partial-product array.
+template <class C>
+__device__ __forceinline__ void k_slice(Params &p)
+{
+    const int z = blockIdx.y;
+    const int k0 = z * p.k_split;
+    const int kz = min(p.k_split, p.K - k0);
+    const int64_t a_off = (C::A_KMAJ ? (int64_t)k0 : (int64_t)k0 * p.lda) * C::ES;
+    const int64_t b_off = (C::B_KMAJ ? (int64_t)k0 : (int64_t)k0 * p.ldb) * C::ES;
+    p.A = (const char *)p.A + a_off;
+    p.B = (const char *)p.B + b_off;
+    if (p.a_bytes) {
+        uint32_t r = p.a_bytes - (uint32_t)a_off;
+        if constexpr (!C::A_KMAJ)
+            r = min(r, (uint32_t)(((int64_t)(kz - 1) * p.lda + p.M) * C::ES));
+        p.a_bytes = r;
+    }
+    if (p.b_bytes) {
+        uint32_t r = p.b_bytes - (uint32_t)b_off;
+        if constexpr (!C::B_KMAJ)
+            r = min(r, (uint32_t)(((int64_t)(kz - 1) * p.ldb + p.N) * C::ES));
+        p.b_bytes = r;
+    }
+    p.K = kz;
+    p.C = (char *)p.C + (int64_t)z * p.c_slice_bytes;
+}
+
+template <class C, typename OutT, bool BIAS, bool SPLIT>
 __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 {
+    if constexpr (SPLIT)
+        k_slice<C>(p);
     static_assert((C::STAGES * C::KS) % 2 == 0, "register double buffer parity per loop body");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     int tm, tn;
@@ -1086,9 +1120,11 @@ __device__ __forceinline__ void staged_body(const Params &p, StagedLoader<C> &ld
     }
 }
 
-template <class C, typename OutT, bool BIAS>
+template <class C, typename OutT, bool BIAS, bool SPLIT>
 __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
 {
+    if constexpr (SPLIT)
+        k_slice<C>(p);
     static_assert(C::STAGES == 2, "the register-staged path double-buffers LDS");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     int tm, tn;
@@ -1139,25 +1175,34 @@ using WithOps = Cfg<C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N, C::STAGES, C::M
 template <class C, int KIND>
 hipError_t launch_ops(const Params &p, bool f16_out, bool bias, hipStream_t s)
 {
-    const dim3 grid(p.tiles_m * p.tiles_n), block(C::THREADS);
-#define TG_GO(KERNEL, OUT, B)                                                        \
+    const dim3 grid(p.tiles_m * p.tiles_n, p.splits > 1 ? p.splits : 1), block(C::THREADS);
+#define TG_GO(KERNEL, OUT, B, SPLIT)                                                 \
     do {                                                                             \
-        hipLaunchKernelGGL((KERNEL<C, OUT, B>), grid, block, 0, s, p);               \
+        hipLaunchKernelGGL((KERNEL<C, OUT, B, SPLIT>), grid, block, 0, s, p);        \
         return hipGetLastError();                                                    \
     } while (0)
+    if (p.splits > 1) {   // K slices: fp32 (int32) partial products, no bias
+        if (f16_out || bias)
+            return hipErrorInvalidValue;
+        using PartT = std::conditional_t<C::ES == 1, int32_t, float>;
+        if constexpr (KIND == 2)
+            TG_GO(gemm_pipe, PartT, false, true);
+        else
+            TG_GO(gemm_staged, PartT, false, true);
+    }
     if constexpr (C::ES == 1) {   // int8 operands: int32 C, no bias
         if (f16_out || bias)
             return hipErrorInvalidValue;
         if constexpr (KIND == 2)
-            TG_GO(gemm_pipe, int32_t, false);
+            TG_GO(gemm_pipe, int32_t, false, false);
         else
-            TG_GO(gemm_staged, int32_t, false);
+            TG_GO(gemm_staged, int32_t, false, false);
     } else if constexpr (KIND == 2) {
-        if (f16_out) { if (bias) TG_GO(gemm_pipe, _Float16, true); else TG_GO(gemm_pipe, _Float16, false); }
-        else { if (bias) TG_GO(gemm_pipe, float, true); else TG_GO(gemm_pipe, float, false); }
+        if (f16_out) { if (bias) TG_GO(gemm_pipe, _Float16, true, false); else TG_GO(gemm_pipe, _Float16, false, false); }
+        else { if (bias) TG_GO(gemm_pipe, float, true, false); else TG_GO(gemm_pipe, float, false, false); }
     } else {
-        if (f16_out) { if (bias) TG_GO(gemm_staged, _Float16, true); else TG_GO(gemm_staged, _Float16, false); }
-        else { if (bias) TG_GO(gemm_staged, float, true); else TG_GO(gemm_staged, float, false); }
+        if (f16_out) { if (bias) TG_GO(gemm_staged, _Float16, true, false); else TG_GO(gemm_staged, _Float16, false, false); }
+        else { if (bias) TG_GO(gemm_staged, float, true, false); else TG_GO(gemm_staged, float, false, false); }
     }
 #undef TG_GO
 }
@@ -1198,6 +1243,98 @@ LaunchFn shard_launch()
     else
         return nullptr;
 }
+
+// ------------------------------------------------------ split-K reduction --
+// One lane per 4 consecutive columns of a row: the slices' partials are
+// summed in slice order (fp32, or int32 for int8 operands: exact), then the
+// bias is added and ReLU applied, and the result converted to C's type.
+// Memory-bound: 16-byte loads of each slice and one store of C per lane,
+// consecutive lanes on consecutive columns.
+template <typename AccT, typename OutT, bool BIAS>
+__global__ void __launch_bounds__(256) splitk_reduce(ReduceParams r)
+{
+    const int64_t per_row = (r.N + 3) / 4;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= (int64_t)r.M * per_row)
+        return;
+    const int64_t row = g / per_row;
+    const int col = (int)(g - row * per_row) * 4;
+    const AccT *src = (const AccT *)r.ws + row * r.N + col;
+    AccT v[4];
+    if (r.vec_ws && col + 3 < r.N) {
+        using V4 = std::conditional_t<std::is_same_v<AccT, int32_t>, int4v, float4v>;
+        V4 a = *(const V4 *)src;
+        for (int z = 1; z < r.splits; z++) {
+            const V4 b = *(const V4 *)(src + z * r.slice_elems);
+            a += b;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            v[j] = a[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[j] = 0;
+            if (col + j < r.N) {
+                v[j] = src[j];
+                for (int z = 1; z < r.splits; z++)
+                    v[j] += src[z * r.slice_elems + j];
+            }
+        }
+    }
+    OutT o[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if constexpr (BIAS) {
+            const float x = (float)v[j] + (col + j < r.N ? r.bias[col + j] : 0.f);
+            o[j] = (OutT)(x > 0.f ? x : 0.f);
+        } else {
+            o[j] = (OutT)v[j];
+        }
+    }
+    OutT *dst = (OutT *)r.C + row * r.ldc + col;
+    if (r.vec_c && col + 3 < r.N) {
+        if constexpr (sizeof(OutT) == 2) {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            *(h4 *)dst = h4{o[0], o[1], o[2], o[3]};
+        } else {
+            typedef OutT o4 __attribute__((ext_vector_type(4)));
+            *(o4 *)dst = o4{o[0], o[1], o[2], o[3]};
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            if (col + j < r.N)
+                dst[j] = o[j];
+    }
+}
+
+#if TG_SHARD == 0
+hipError_t launch_splitk_reduce(const ReduceParams &r, OutKind out, hipStream_t s)
+{
+    const int64_t lanes = (int64_t)r.M * ((r.N + 3) / 4);
+    if (lanes <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+    const bool b = r.bias != nullptr;
+    if (out == kOutI32) {
+        if (b)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((splitk_reduce<int32_t, int32_t, false>), grid, block, 0, s, r);
+    } else if (out == kOutF16) {
+        if (b)
+            hipLaunchKernelGGL((splitk_reduce<float, _Float16, true>), grid, block, 0, s, r);
+        else
+            hipLaunchKernelGGL((splitk_reduce<float, _Float16, false>), grid, block, 0, s, r);
+    } else {
+        if (b)
+            hipLaunchKernelGGL((splitk_reduce<float, float, true>), grid, block, 0, s, r);
+        else
+            hipLaunchKernelGGL((splitk_reduce<float, float, false>), grid, block, 0, s, r);
+    }
+    return hipGetLastError();
+}
+#endif
 
 #define TG_CAT2(a, b) a##b
 #define TG_CAT(a, b) TG_CAT2(a, b)

@@ -129,17 +129,13 @@ def supported(cid, sh, bufs):
     return tg.tg_config_supports(cid, *_args(sh, bufs), op_a=sh.op_a, op_b=sh.op_b) == 1
 
 
-def time_config(cid, sh, bufs, reps, timing="graph"):
-    """Average milliseconds per launch of configuration `cid`, or None."""
-    if not supported(cid, sh, bufs):
-        return None
-    args = _args(sh, bufs)
-
+def time_launch(launch, reps, timing="graph"):
+    """Average milliseconds per call of launch(stream) (a libtg call that
+    returns a status)."""
     def go():
-        s = torch.cuda.current_stream().cuda_stream
-        st = tg.tg_gemm_with_config(cid, *args, s, op_a=sh.op_a, op_b=sh.op_b)
+        st = launch(torch.cuda.current_stream().cuda_stream)
         if st != tg.TG_SUCCESS:
-            raise tg.TgError(st, "tg_gemm_with_config(%d, %s)" % (cid, sh))
+            raise tg.TgError(st, "timed call")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -173,6 +169,59 @@ def time_config(cid, sh, bufs, reps, timing="graph"):
         torch.cuda.synchronize()
         n = reps
     return e0.elapsed_time(e1) / n
+
+
+def time_config(cid, sh, bufs, reps, timing="graph"):
+    """Average milliseconds per launch of configuration `cid`, or None."""
+    if not supported(cid, sh, bufs):
+        return None
+    args = _args(sh, bufs)
+    return time_launch(lambda s: tg.tg_gemm_with_config(cid, *args, s, op_a=sh.op_a,
+                                                        op_b=sh.op_b), reps, timing)
+
+
+def time_split(cid, splits, sh, bufs, ws, reps, timing="graph"):
+    """Average milliseconds per tg_gemm_splitk call (cid -1 / splits 0: the
+    dispatcher's choice) with workspace tensor ws."""
+    args = _args(sh, bufs)
+    nbytes = ws.numel() * ws.element_size()
+    return time_launch(lambda s: tg.tg_gemm_splitk(cid, splits, *args, ws.data_ptr(), nbytes, s,
+                                                   op_a=sh.op_a, op_b=sh.op_b), reps, timing)
+
+
+def search_splits(sh, config_ids, split_counts, reps, timing):
+    """Time every configuration unsliced and at each slice count, and the
+    dispatcher's own choice.  Returns {(config, slices): ms} and the
+    dispatcher's (config, slices, ms)."""
+    bufs = Buffers(sh)
+    ws = torch.empty(tg.tg_splitk_workspace_bytes(sh.M, sh.N, max(split_counts)) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+    out = {}
+    for c in config_ids:
+        if not supported(c, sh, bufs):
+            continue
+        out[(c, 1)] = time_config(c, sh, bufs, reps, timing)
+        info = tg.tg_config_info(c)
+        seen = set()
+        for sp in split_counts:
+            kk = -(-(-(-sh.K // sp)) // info["block_k"]) * info["block_k"]
+            slices = -(-sh.K // kk)
+            if slices <= 1 or slices in seen:
+                continue
+            seen.add(slices)
+            out[(c, slices)] = time_split(c, sp, sh, bufs, ws, reps, timing)
+    a = _args(sh, bufs)
+    nbytes = ws.numel() * ws.element_size()
+    st, cid, sl = tg.tg_select_splitk(*a, nbytes, op_a=sh.op_a, op_b=sh.op_b)
+    auto = (cid, sl, time_split(-1, 0, sh, bufs, ws, reps, timing))
+    best = min(out, key=out.get)
+    print(json.dumps({"shape": str(sh), "auto": list(auto[:2]), "auto_ms": round(auto[2], 5),
+                      "best": list(best), "best_ms": round(out[best], 5),
+                      "unsliced_best_ms": round(min(v for k, v in out.items() if k[1] == 1), 5)}),
+          flush=True)
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return out, auto
 
 
 def _record(sh, cid, ms, stage):
@@ -276,17 +325,18 @@ def grid(dtype, config_ids, reps, timing, pad, timings, mn=GRID_MN, ks=None):
                 add_timings(timings, sh, res)
 
 
-def random_shapes(count, seed, dtypes, max_flop=4e12):
+def random_shapes(count, seed, dtypes, max_flop=4e12, mn_log2=(6, 14), k_log2=(6, 15)):
     """Seeded shapes for validating the cost model off its grid: M, N and K
-    log-uniform (M, N in [64, 16384], K in [64, 32768]), rounded to 16 so
-    that the direct loads apply, half of them with a transposed operand."""
+    log-uniform (by default M, N in [64, 16384], K in [64, 32768]), rounded
+    to 16 so that the direct loads apply, half of them with a transposed
+    operand."""
     import random
     rng = random.Random(seed)
     out = []
     while len(out) < count:
         dt = dtypes[len(out) % len(dtypes)]
-        M, N = (16 * max(4, round(2 ** rng.uniform(6, 14) / 16)) for _ in range(2))
-        K = 16 * max(4, round(2 ** rng.uniform(6, 15) / 16))
+        M, N = (16 * max(4, round(2 ** rng.uniform(*mn_log2) / 16)) for _ in range(2))
+        K = 16 * max(4, round(2 ** rng.uniform(*k_log2) / 16))
         if 2.0 * M * N * K > max_flop:
             continue
         op = rng.choice(("nn", "nn", "nn", "tn", "nt", "tt"))
@@ -316,6 +366,10 @@ def main():
     ap.add_argument("--random", type=int, metavar="COUNT",
                     help="time COUNT seeded random shapes (of --grid-dtypes)")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--random-mn", default="6:14", help="log2 range of random M and N")
+    ap.add_argument("--random-k", default="6:15", help="log2 range of random K")
+    ap.add_argument("--splits", help="also time K slicing: slice counts, e.g. 2,4,8")
+    ap.add_argument("--split-out", metavar="CSV", help="write the sliced timings to CSV")
     ap.add_argument("--out", metavar="CSV", help="write every timing to CSV")
     a = ap.parse_args()
     ids = (list(range(tg.tg_num_configs())) if a.configs == "all"
@@ -328,11 +382,25 @@ def main():
             costmodel.write_timings(a.out, timings)
         return 0
     if a.random:
+        rng_mn = tuple(float(x) for x in a.random_mn.split(":"))
+        rng_k = tuple(float(x) for x in a.random_k.split(":"))
         a.shape = a.shape + [str(sh) for sh in
-                             random_shapes(a.random, a.seed, a.grid_dtypes.split(","))]
+                             random_shapes(a.random, a.seed, a.grid_dtypes.split(","),
+                                           mn_log2=rng_mn, k_log2=rng_k)]
     if not a.shape:
         ap.error("--shape is required unless --grid or --random is given")
     shapes = [Shape.parse(s) for s in a.shape]
+    if a.splits:
+        counts = [int(x) for x in a.splits.split(",")]
+        rows = {}
+        for sh in shapes:
+            res, auto = search_splits(sh, ids, counts, a.reps, a.timing)
+            key = (sh.c_dtype, sh.layout, sh.M, sh.N, sh.K)
+            rows[key] = {k: v * 1000.0 for k, v in res.items()}
+            rows[key][("auto", auto[0], auto[1])] = auto[2] * 1000.0
+        if a.split_out:
+            costmodel.write_split_timings(a.split_out, rows)
+        return 0
     cache = read_cache(a.tune) if a.tune else None
     for sh in shapes:
         res = search(sh, ids, a.reps, a.timing, a.staged or bool(a.tune))

@@ -47,6 +47,13 @@ def lib():
         L.tgref_gemm_i8_ex.restype = I
         L.tgref_gemm_i8_entries_ex.argtypes = [I, I, P, P, P, P, I64, P, I64, I64, I64]
         L.tgref_gemm_i8_entries_ex.restype = I
+        D = ctypes.c_double
+        L.tgref_attention.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, D, I,
+                                      P, P, P, I]
+        L.tgref_attention.restype = I
+        L.tgref_attention_rows.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, D,
+                                           I, P, I64, P, P, P, I]
+        L.tgref_attention_rows.restype = I
         _lib = L
     return _lib
 
@@ -176,3 +183,52 @@ def output_typed(cref, c_dtype):
     if c_dtype == "f16":
         return encode_f16(cref)
     raise ValueError(c_dtype)
+
+
+# ------------------------------------------------------------ attention --
+def _strides(st):
+    st = np.ascontiguousarray(st, dtype=np.int64)
+    assert st.shape == (3,)
+    return st
+
+
+def attention_ref(Q, K, V, B, H, Hkv, Lq, Lk, d, q_strides, k_strides, v_strides, scale,
+                  causal=False, nthreads=None):
+    """fp64 reference of scaled dot-product attention (tgref_attention.c):
+    returns O [B, H, Lq, d], lse [B, H, Lq] and the softmax-weighted mean
+    magnitude A [B, H, Lq, d] of V (for the error bound).
+
+    Q, K, V: flat fp16 bit arrays (uint16) holding element (b, h, i, c) at
+    b*s[0] + h*s[1] + i*s[2] + c with s the given {batch, head, row} strides;
+    K and V have Hkv heads, query head h reading head h // (H // Hkv)."""
+    Q, K, V = (np.ascontiguousarray(_u16(x)).reshape(-1) for x in (Q, K, V))
+    qs, ks, vs = _strides(q_strides), _strides(k_strides), _strides(v_strides)
+    O = np.zeros((B, H, Lq, d))
+    lse = np.zeros((B, H, Lq))
+    A = np.zeros((B, H, Lq, d))
+    rc = lib().tgref_attention(_ptr(Q), _ptr(K), _ptr(V), B, H, Hkv, Lq, Lk, d, _ptr(qs),
+                               _ptr(ks), _ptr(vs), float(scale), int(bool(causal)), _ptr(O),
+                               _ptr(lse), _ptr(A), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("tgref_attention rejected its arguments (%d)" % rc)
+    return O, lse, A
+
+
+def attention_rows(Q, K, V, B, H, Hkv, Lq, Lk, d, q_strides, k_strides, v_strides, scale,
+                   causal, rows, nthreads=None):
+    """As attention_ref for the listed (b, h, i) query rows only; returns
+    O [n, d], lse [n], A [n, d]."""
+    Q, K, V = (np.ascontiguousarray(_u16(x)).reshape(-1) for x in (Q, K, V))
+    qs, ks, vs = _strides(q_strides), _strides(k_strides), _strides(v_strides)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    n = rows.shape[0]
+    O = np.zeros((n, d))
+    lse = np.zeros(n)
+    A = np.zeros((n, d))
+    rc = lib().tgref_attention_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, Hkv, Lq, Lk, d, _ptr(qs),
+                                    _ptr(ks), _ptr(vs), float(scale), int(bool(causal)),
+                                    _ptr(rows), n, _ptr(O), _ptr(lse), _ptr(A),
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("tgref_attention_rows rejected its arguments (%d)" % rc)
+    return O, lse, A

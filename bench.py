@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sq8192", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--workload", default="sq8192",
+                    choices=sorted(gen.WORKLOADS) + sorted(gen.ATTN_WORKLOADS))
     ap.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
@@ -96,6 +97,8 @@ def main():
         return 2
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
+    if a.workload in gen.ATTN_WORKLOADS:
+        return bench_attention(a)
     import torch
 
     import oracle
@@ -225,6 +228,129 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def attention_flop(w, rows=None):
+    """2 d FLOP per score and 2 d per weighted V row, over the visible
+    (query, key) pairs of every head (of the listed query rows)."""
+    i = np.arange(w["Lq"]) if rows is None else np.asarray(rows)
+    vis = np.clip(i + (w["Lk"] - w["Lq"]) + 1, 0, w["Lk"]) if w["causal"] else \
+        np.full(len(i), w["Lk"])
+    heads = w["B"] * w["H"] if rows is None else 1
+    return 4.0 * w["d"] * float(vis.sum()) * heads, vis
+
+
+def bench_attention(a):
+    """Fused attention forward: one step is one tg_attention_fwd call over the
+    whole workload."""
+    import torch
+
+    import oracle
+    import tiled_dense_gemm_08_amd as tg
+
+    w = gen.attention_workload(a.workload)
+    B, H, Hkv, Lq, Lk, d, causal = (w[k] for k in ("B", "H", "Hkv", "Lq", "Lk", "d", "causal"))
+    scale = 1.0 / np.sqrt(d)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(w[k].view(np.int16)).to(dev) for k in ("Q", "K", "V"))
+    to = torch.empty(B * H * Lq * d, dtype=torch.int16, device=dev)
+    tl = torch.empty(B * H * Lq, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+
+    def step():
+        st = tg.tg_attention_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr(),
+                                 tl.data_ptr(), B, H, Hkv, Lq, Lk, d, w["qs"], w["ks"], w["vs"],
+                                 w["os"], scale, causal, s)
+        if st != tg.TG_SUCCESS:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    # ---- parity gate on sampled query rows (the tolerance of the GPU tests)
+    to.fill_(0x7E00)
+    step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(123)
+    n = max(16, a.samples // 32)
+    rows = np.stack([rng.integers(0, B, n), rng.integers(0, H, n), rng.integers(0, Lq, n)], 1)
+    Or, lr, Ar = oracle.attention_rows(w["Q"], w["K"], w["V"], B, H, Hkv, Lq, Lk, d, w["qs"],
+                                       w["ks"], w["vs"], scale, causal, rows)
+    O = to.cpu().numpy().view(np.uint16).reshape(B, H, Lq, d)
+    got = O[rows[:, 0], rows[:, 1], rows[:, 2]].view(np.float16).astype(np.float64)
+    _, vis = attention_flop(w, rows[:, 2])
+    vmax = float(np.abs(w["V"].view(np.float16).astype(np.float64)).max())
+    spacing = np.where(np.abs(Or) < 2.0 ** -14, 2.0 ** -24,
+                       2.0 ** (np.floor(np.log2(np.maximum(np.abs(Or), 2.0 ** -14))) - 10))
+    tol = 2.0 ** -10 * Ar + (vis * 2.0 ** -24 * vmax)[:, None] + spacing
+    lse = tl.cpu().numpy().reshape(B, H, Lq)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    ok = bool(np.all(np.abs(got - Or) <= tol)) and \
+        bool(np.all(np.abs(lse - lr) <= 2e-5 * (1 + np.abs(lr))))
+    if not ok:
+        print(json.dumps({"error": "parity gate failed", "workload": a.workload}))
+        return 1
+
+    # ---- timing
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    flop, _ = attention_flop(w)
+    elapsed = max(wall, gpu_ms / 1e3)
+    value = flop * a.steps / elapsed / 1e12
+    achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
+
+    # ---- CPU oracle baseline: whole query rows, sampled
+    cpu = None
+    if a.cpu_seconds > 0:
+        threads = oracle.default_threads()
+        nr = 32
+        while True:
+            sel = np.stack([rng.integers(0, B, nr), rng.integers(0, H, nr),
+                            rng.integers(0, Lq, nr)], 1)
+            t = time.perf_counter()
+            oracle.attention_rows(w["Q"], w["K"], w["V"], B, H, Hkv, Lq, Lk, d, w["qs"],
+                                  w["ks"], w["vs"], scale, causal, sel, nthreads=threads)
+            dt = time.perf_counter() - t
+            if dt >= 0.8 * a.cpu_seconds or nr >= 1 << 16:
+                break
+            nr = min(1 << 16, max(nr + 1, int(nr * a.cpu_seconds / max(dt, 1e-3))))
+        f, _ = attention_flop(w, sel[:, 2])
+        cpu = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "%d random query rows (fp64 scores, softmax and weighted V sum over "
+                         "their visible keys), %.1f s" % (nr, dt)}
+
+    line = {
+        "metric": "fused attention forward TFLOP/s and % of MI355X fp16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed * 1e3 / a.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "B": B, "H": H, "Hkv": Hkv, "Lq": Lq, "Lk": Lk,
+                   "d": d, "causal": bool(causal), "kernel": "attn_fwd<%d,%s>" % (d, bool(causal)),
+                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

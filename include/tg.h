@@ -156,6 +156,38 @@ tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
                            int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
                            size_t workspace_bytes, int *config_id, int *splits);
 
+/* ---- fused attention (forward) -------------------------------------------
+ * O = softmax(scale * Q K^T [+ causal mask]) V for every batch b < B and
+ * query head h < H, computed block by block with the softmax folded in online
+ * (lqnn.cn TileLang walkthrough, section 3.2; xdnf.cn article, section 3.2):
+ *   s_ij  = scale * sum_c Q[b][h][i][c] K[b][hk][j][c]   (hk = h / (H / Hkv))
+ *   O[b][h][i][c] = sum_j softmax_j(s_ij) V[b][hk][j][c]
+ *   lse[b][h][i]  = log sum_j exp(s_ij)            (natural log)
+ * over the visible keys: j < Lk and, with causal = 1, j <= i + (Lk - Lq)
+ * (the mask aligned at the bottom right: with Lq == Lk, j <= i).  A query
+ * that sees no key gets O = 0 and lse = -inf.
+ *
+ * Q, K, V, O: fp16; scores, softmax and the weighted sum in fp32, the
+ * softmax weights rounded to fp16 for the second product.  Layout: element
+ * (b, h, i, c) of Q is Q[b * q_strides[0] + h * q_strides[1] + i *
+ * q_strides[2] + c] (strides in elements, the head dimension contiguous);
+ * K and V likewise with their Hkv heads; O like Q.  [B, H, L, d] and
+ * [B, L, H, d] are both such layouts.  lse: NULL, or fp32 [B][H][Lq] dense.
+ * O must not overlap Q, K, V or lse.  Asynchronous on `stream`.
+ *
+ * Errors: TG_ERROR_INVALID_VALUE for negative sizes or strides, H not a
+ * multiple of Hkv, NULL strides or required pointers (K, V may be NULL when
+ * Lk == 0), a non-finite scale, causal not 0 or 1, or a pointer not aligned
+ * to its element; TG_ERROR_UNSUPPORTED for d other than 64 or 128, Q, K, V
+ * or O not 16-byte aligned, a stride not a multiple of 8 elements, or a
+ * head's K or V rows spanning 2 GiB or more; TG_ERROR_NOT_DEVICE_MEMORY and
+ * TG_ERROR_LAUNCH as for the GEMM.  B == 0 or Lq == 0 is a successful no-op. */
+tg_status tg_attention_fwd(const void *Q, const void *K, const void *V, void *O, float *lse,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
+                           const int64_t *q_strides, const int64_t *k_strides,
+                           const int64_t *v_strides, const int64_t *o_strides,
+                           float scale, int causal, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char *tg_status_string(tg_status s);
 

@@ -161,3 +161,28 @@ def workload(name, integer=False):
     return dict(name=name, M=w["M"], N=w["N"], K=w["K"], A=A, B=B, bias=bias,
                 c_dtype=w["c_dtype"], integer=integer, op_a=op_a, op_b=op_b,
                 lda=A.shape[1], ldb=B.shape[1])
+
+
+# Fused-attention workloads: Q, K, V with N(0,1) values rounded to fp16, one
+# stream each (seeds seed, seed + 1, seed + 2), stored [B, H, L, d] dense.
+ATTN_WORKLOADS = {
+    "attn_b2h16l4096d128": dict(B=2, H=16, Hkv=16, Lq=4096, Lk=4096, d=128, causal=False,
+                                seed=10),
+    "attn_b2h16l4096d128_causal": dict(B=2, H=16, Hkv=16, Lq=4096, Lk=4096, d=128, causal=True,
+                                       seed=10),
+    "attn_b4h16l2048d64": dict(B=4, H=16, Hkv=16, Lq=2048, Lk=2048, d=64, causal=False,
+                               seed=13),
+}
+
+
+def attention_workload(name):
+    """fp16 bits of Q [B, H, Lq, d], K and V [B, Hkv, Lk, d] of a named
+    attention workload, with the {batch, head, row} strides."""
+    w = dict(ATTN_WORKLOADS[name])
+    B, H, Hkv, Lq, Lk, d = w["B"], w["H"], w["Hkv"], w["Lq"], w["Lk"], w["d"]
+    Q = to_f16_bits(normal(w["seed"], B * H * Lq * d))
+    K = to_f16_bits(normal(w["seed"] + 1, B * Hkv * Lk * d))
+    V = to_f16_bits(normal(w["seed"] + 2, B * Hkv * Lk * d))
+    w.update(name=name, Q=Q, K=K, V=V, qs=(H * Lq * d, Lq * d, d), ks=(Hkv * Lk * d, Lk * d, d),
+             vs=(Hkv * Lk * d, Lk * d, d), os=(H * Lq * d, Lq * d, d))
+    return w

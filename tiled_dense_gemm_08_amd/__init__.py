@@ -31,7 +31,8 @@ TG_OP_T = 1
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
-            "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk", "tg_version")
+            "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk",
+            "tg_attention_fwd", "tg_version")
 
 
 class TgError(RuntimeError):
@@ -90,6 +91,9 @@ def _load():
     L.tg_gemm_splitk.restype = I
     L.tg_select_splitk.argtypes = [I, I] + shape_args + [SZ, IP, IP]
     L.tg_select_splitk.restype = I
+    L.tg_attention_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
+                                   ctypes.c_float, I, P]
+    L.tg_attention_fwd.restype = I
     L.tg_tuning_load.argtypes = [ctypes.c_char_p, IP, IP, IP]
     L.tg_tuning_load.restype = I
     L.tg_tuning_clear.argtypes = []
@@ -168,6 +172,18 @@ def tg_select_splitk(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, workspace_b
     st = lib.tg_select_splitk(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
                               workspace_bytes, ctypes.byref(cid), ctypes.byref(sp))
     return st, cid.value, sp.value
+
+
+def _strides3(st):
+    a = (ctypes.c_int64 * 3)(*[int(x) for x in st])
+    return a
+
+
+def tg_attention_fwd(Q, K, V, O, lse, B, H, Hkv, Lq, Lk, d, q_strides, k_strides, v_strides,
+                     o_strides, scale, causal, stream=0):
+    return lib.tg_attention_fwd(Q, K, V, O, lse, B, H, Hkv, Lq, Lk, d, _strides3(q_strides),
+                                _strides3(k_strides), _strides3(v_strides),
+                                _strides3(o_strides), scale, int(causal), stream or None)
 
 
 def tg_tuning_load(path):
@@ -298,3 +314,32 @@ def gemm_bias_relu(a, b, bias, out=None, out_dtype=None, config=None, stream=Non
                    workspace=None, splits=0):
     return gemm(a, b, out=out, out_dtype=out_dtype, bias=bias, config=config, stream=stream,
                 workspace=workspace, splits=splits)
+
+
+def attention(q, k, v, causal=False, scale=None, out=None, return_lse=False, stream=None):
+    """Fused attention forward with libtg: q (B, H, Lq, d), k and v (B, Hkv, Lk, d)
+    float16 views on the current device whose last dimension is contiguous
+    (any strides otherwise, e.g. a (B, L, H, d) tensor permuted to (B, H, L, d));
+    returns out (B, H, Lq, d) float16 and, with return_lse, lse (B, H, Lq)
+    float32.  scale defaults to 1/sqrt(d)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.float16 or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("%s must be a 4-D float16 tensor with a contiguous last dim" % n)
+    B, H, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if tuple(v.shape) != (Bk, Hkv, Lk, dk) or Bk != B or dk != d:
+        raise ValueError("shapes do not match: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                                  tuple(v.shape)))
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=torch.float16, device=q.device)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = tg_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, B, H, Hkv, Lq, Lk, d,
+                          q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
+                          scale, causal, s)
+    if st != TG_SUCCESS:
+        raise TgError(st, "tg_attention_fwd")
+    return (out, lse) if return_lse else out

@@ -21,6 +21,7 @@
 #include <unordered_map>
 
 #include "tg.h"
+#include "tg_attention.h"
 #include "tg_kernels.h"
 
 namespace {
@@ -779,9 +780,100 @@ tg_status run_split(int config_id, int splits, const Problem &p, void *ws, size_
     return tg::launch_splitk_reduce(r, kind, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
 }
 
+// ---- attention ----------------------------------------------------------------
+constexpr int64_t kMaxRange = int64_t(1) << 31;
+
+tg_status attention_args(const void *Q, const void *K, const void *V, void *O, float *lse,
+                         int64_t B, int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
+                         const int64_t *qs, const int64_t *ks, const int64_t *vs,
+                         const int64_t *os, float scale, int causal, tg::AttentionArgs *a)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || H % Hkv || Lq < 0 || Lk < 0 || d < 1)
+        return TG_ERROR_INVALID_VALUE;
+    if (!qs || !ks || !vs || !os || !(scale == scale) || scale > 3.4e38f || scale < -3.4e38f ||
+        (causal != 0 && causal != 1))
+        return TG_ERROR_INVALID_VALUE;
+    for (int i = 0; i < 3; i++)
+        if (qs[i] < 0 || ks[i] < 0 || vs[i] < 0 || os[i] < 0)
+            return TG_ERROR_INVALID_VALUE;
+    if (B == 0 || Lq == 0)
+        return TG_SUCCESS;   // nothing to compute
+    if (!Q || !O || (Lk > 0 && (!K || !V)))
+        return TG_ERROR_INVALID_VALUE;
+    if (!aligned(Q, 2) || !aligned(K, 2) || !aligned(V, 2) || !aligned(O, 2) ||
+        (lse && !aligned(lse, 4)))
+        return TG_ERROR_INVALID_VALUE;
+    // what this kernel supports: head dimension 64 or 128, 16-byte rows
+    if (d != 64 && d != 128)
+        return TG_ERROR_UNSUPPORTED;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+        return TG_ERROR_UNSUPPORTED;
+    for (int i = 0; i < 3; i++)
+        if (qs[i] % 8 || ks[i] % 8 || vs[i] % 8 || os[i] % 8)
+            return TG_ERROR_UNSUPPORTED;
+    if (B > kMaxDim || H > kMaxDim || Lq > kMaxDim || Lk > kMaxDim ||
+        B * H * ((Lq + 127) / 128) > kMaxDim)
+        return TG_ERROR_UNSUPPORTED;
+    // the copies address a head's K / V rows with 32-bit offsets from the
+    // tile's first row
+    const int64_t k_bytes = Lk > 0 ? ((Lk - 1) * ks[2] + d) * 2 : 0;
+    const int64_t v_bytes = Lk > 0 ? ((Lk - 1) * vs[2] + d) * 2 : 0;
+    if (k_bytes >= kMaxRange || v_bytes >= kMaxRange || (Lk + 64) * ks[2] * 2 >= kMaxRange ||
+        (Lk + 64) * vs[2] * 2 >= kMaxRange)
+        return TG_ERROR_UNSUPPORTED;
+    memset(a, 0, sizeof(*a));
+    a->Q = Q;
+    a->K = K;
+    a->V = V;
+    a->O = O;
+    a->lse = lse;
+    a->B = (int)B;
+    a->H = (int)H;
+    a->Hkv = (int)Hkv;
+    a->Lq = (int)Lq;
+    a->Lk = (int)Lk;
+    a->d = (int)d;
+    for (int i = 0; i < 3; i++) {
+        a->qs[i] = qs[i];
+        a->ks[i] = ks[i];
+        a->vs[i] = vs[i];
+        a->os[i] = os[i];
+    }
+    a->k_bytes = (uint32_t)k_bytes;
+    a->v_bytes = (uint32_t)v_bytes;
+    a->scale = scale;
+    a->causal = causal;
+    return TG_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+tg_status tg_attention_fwd(const void *Q, const void *K, const void *V, void *O, float *lse,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
+                           const int64_t *q_strides, const int64_t *k_strides,
+                           const int64_t *v_strides, const int64_t *o_strides, float scale,
+                           int causal, hipStream_t stream)
+{
+    tg::AttentionArgs a;
+    memset(&a, 0, sizeof(a));
+    tg_status st = attention_args(Q, K, V, O, lse, B, H, Hkv, Lq, Lk, d, q_strides, k_strides,
+                                  v_strides, o_strides, scale, causal, &a);
+    if (st != TG_SUCCESS || B == 0 || Lq == 0)
+        return st;
+    int dev = 0;
+    if ((st = check_device(&dev)) != TG_SUCCESS)
+        return st;
+    if ((st = check_pointer(Q, dev)) != TG_SUCCESS || (st = check_pointer(O, dev)) != TG_SUCCESS ||
+        (Lk > 0 && ((st = check_pointer(K, dev)) != TG_SUCCESS ||
+                    (st = check_pointer(V, dev)) != TG_SUCCESS)) ||
+        (st = check_pointer(lse, dev)) != TG_SUCCESS)
+        return st;
+    (void)hipGetLastError();
+    return tg::launch_attention(a, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
+}
+
 
 tg_status tg_gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                   int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype, hipStream_t stream)

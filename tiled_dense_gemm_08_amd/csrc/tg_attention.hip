@@ -1,0 +1,375 @@
+// tg_attention.hip — fused scaled dot-product attention (forward) for gfx950.
+//
+// The block-wise form the lqnn.cn TileLang walkthrough (section 3.2) and the
+// xdnf.cn article (section 3.2) describe: K and V are loaded tile by tile
+// into LDS by the same global->LDS copies and two-stage ring as the GEMM,
+// each tile's scores are multiplied on the matrix cores, and the softmax is
+// folded in online, in registers, before the next tile:
+//     m' = max(m, max_j s_j)          alpha = exp(m - m')
+//     l' = alpha l + sum_j exp(s_j - m')
+//     O' = alpha O + sum_j exp(s_j - m') V_j
+// and at the end O / l and lse = m + log l.  Scores and the softmax are fp32,
+// the weights are rounded to fp16 for the second product, O is stored fp16.
+//
+// Work split: a workgroup of 4 waves owns 128 queries of one (batch, head);
+// each wave owns 32 of them and loops over the keys in tiles of 64.
+//
+// Both products are computed transposed so that a lane owns one query:
+//  * scores S^T = K . Q^T on v_mfma_f32_32x32x16_f16 with K from LDS (first
+//    source, rows = keys) and the wave's Q fragments in registers (second
+//    source, columns = queries): lane l holds query l % 32 and, in register
+//    r of a 32-key tile, key 8 (r / 4) + 4 (l / 32) + r % 4.  A row's maximum
+//    is the maximum over the lane's registers and lane l ^ 32.
+//  * O^T = V^T . P^T with V^T read from the LDS tile by transpose reads
+//    (first source, rows = head dimension) and P^T straight from the score
+//    registers converted to fp16 (second source): a lane's 8 weights of a
+//    16-key chunk are keys {4h .. 4h+3, 8+4h .. 11+4h} (h = l / 32), and the
+//    transpose reads fetch V's rows in that same order, so no weight moves
+//    between lanes.  The O^T accumulator again gives lane l query l % 32, so
+//    the rescale by alpha is one multiply per register.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tg_attention.h"
+
+namespace tg {
+namespace attn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+#define TGA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int BQ = 128, BKV = 64, WAVES = 4, THREADS = 64 * WAVES;
+
+template <int D>
+struct Tile {
+    static constexpr int ROWB = 2 * D;           // bytes of a K or V row
+    static constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per row
+    static constexpr int BYTES = BKV * ROWB;     // one K or V tile
+    static constexpr int STAGE = 2 * BYTES;      // K tile, then V tile
+    static constexpr int LDS = 2 * STAGE;        // two-stage ring
+    static constexpr int LOADS = BYTES / 1024 / WAVES;   // copies per wave per tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+    static constexpr int DK = D / 16;            // k-steps of the score product
+    static constexpr int DT = D / 32;            // 32-row blocks of O^T
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(BYTES % (1024 * WAVES) == 0, "copy split");
+};
+
+// K tile: 32 lanes read 32 consecutive rows at one chunk (ds_read_b128);
+// XOR by row % 8 spreads them over the banks.
+__device__ __forceinline__ int swz_k(int row) { return row & 7; }
+
+// V tile: a transpose read touches rows {4h + e} (e < 4, h < 2) at one
+// 32-byte column pair per 16-lane group; even XOR masks keep the pairs whole
+// and put the 8 rows on distinct 32-byte slots (rows of 128 bytes: 4 slots).
+template <int CHUNKS>
+__device__ __forceinline__ int swz_v(int row)
+{
+    if constexpr (CHUNKS >= 16)
+        return 2 * (row & 3) + 8 * ((row >> 2) & 1);
+    else
+        return 2 * (row & 3);
+}
+
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void wait_vmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane from buffer offset voff to LDS address m0 + 16 lane (see
+// the GEMM's copy: M0 is written only here, one wait state before the load).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
+}
+
+// Copies of one K or V tile (keys kv0 .. kv0+63 of a head whose rows are
+// rstride elements apart): wave w's instruction t fills LDS bytes
+// [1 KiB (w LOADS + t), +1 KiB) = ROWS_PER_LOAD rows; lane i takes row
+// i / CHUNKS and physical chunk i % CHUNKS, and fetches the logical chunk that
+// the tile's swizzle puts there.  Rows at or past Lk fall outside the
+// descriptor's range and read as zeros.
+template <int D, bool IS_V>
+__device__ __forceinline__ void copy_tile(const _Float16 *head, int64_t rstride, int kv0, int Lk,
+                                          uint32_t head_bytes, uint32_t lds_tile)
+{
+    using T = Tile<D>;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t start = (int64_t)kv0 * rstride * 2;
+    const uint32_t range = kv0 < Lk ? head_bytes - (uint32_t)start : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)head + start), 0, (int)range, kRsrcWord3);
+#pragma unroll
+    for (int t = 0; t < T::LOADS; t++) {
+        const int inst = wave * T::LOADS + t;
+        const int row = inst * T::ROWS_PER_LOAD + lane / T::CHUNKS;
+        const int pc = lane % T::CHUNKS;
+        const int lc = pc ^ (IS_V ? swz_v<T::CHUNKS>(row) : swz_k(row));
+        const uint32_t voff = (uint32_t)((int64_t)row * rstride * 2) + (uint32_t)(lc * 16);
+        dma16(rsrc, voff, __builtin_amdgcn_readfirstlane(lds_tile + inst * 1024));
+    }
+}
+
+struct AttnParams {
+    const _Float16 *Q, *K, *V;
+    _Float16 *O;
+    float *lse;                 // [B][H][Lq] or nullptr
+    int B, H, group, Lq, Lk;    // group = H / Hkv
+    int64_t qs[3], ks[3], vs[3], os[3];   // {batch, head, row} strides, elements
+    uint32_t k_bytes, v_bytes;  // descriptor range of one head's K / V rows
+    float scale_log2;           // scale * log2(e)
+    int nqb;                    // query blocks per head
+    int causal;
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
+{
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h = lane >> 5;        // lane half
+    const int col = lane & 31;      // the lane's query within the wave
+
+    // workgroup -> (batch, head, query block); each XCD gets a contiguous
+    // range, so the query blocks of a head share that XCD's L2
+    const int total = p.B * p.H * p.nqb;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int t_log = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int bh = t_log / p.nqb;
+    int qb = t_log - bh * p.nqb;
+    if constexpr (CAUSAL)
+        qb = p.nqb - 1 - qb;   // longest rows first
+    const int b = bh / p.H, hq = bh - b * p.H, hk = hq / p.group;
+    const int q_wg = qb * BQ;
+    const int q0 = q_wg + wave * 32;      // the wave's first query
+    const int query = q0 + col;
+    const int shift = p.Lk - p.Lq;        // causal: key j visible to query i iff j <= i + shift
+
+    // key tiles this workgroup needs
+    int nblk = (p.Lk + BKV - 1) / BKV;
+    if constexpr (CAUSAL) {
+        const int last_q = min(q_wg + BQ, p.Lq) - 1;
+        const int last_key = last_q + shift;
+        nblk = last_key < 0 ? 0 : min(nblk, last_key / BKV + 1);
+    }
+
+    const _Float16 *Kh = p.K + b * p.ks[0] + hk * p.ks[1];
+    const _Float16 *Vh = p.V + b * p.vs[0] + hk * p.vs[1];
+    const uint32_t lds0 = lds_addr(smem);
+    if (nblk > 0) {
+        copy_tile<D, false>(Kh, p.ks[2], 0, p.Lk, p.k_bytes, lds0);
+        copy_tile<D, true>(Vh, p.vs[2], 0, p.Lk, p.v_bytes, lds0 + T::BYTES);
+    }
+
+    // the wave's queries as second-source fragments: lane l holds
+    // Q[query][16 ks + 8 h .. +7]
+    half8 qf[T::DK];
+    {
+        const bool ok = query < p.Lq;
+        const _Float16 *qrow = p.Q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? query : 0) * p.qs[2];
+#pragma unroll
+        for (int ks = 0; ks < T::DK; ks++) {
+            const half8 v = *(const half8 *)(qrow + 16 * ks + 8 * h);
+            qf[ks] = ok ? v : half8{};
+        }
+    }
+
+    // per-lane LDS offsets of the fragment reads
+    int koff[T::DK];
+#pragma unroll
+    for (int ks = 0; ks < T::DK; ks++)
+        koff[ks] = col * T::ROWB + (((2 * ks + h) ^ swz_k(col)) * 16);
+    int voff[T::DT];
+    {
+        const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+        const int row = 4 * h + e;
+        const int cg = 2 * (G & 1) + (q >> 1);
+#pragma unroll
+        for (int dt = 0; dt < T::DT; dt++)
+            voff[dt] = row * T::ROWB + ((((4 * dt) | cg) ^ swz_v<T::CHUNKS>(row)) * 16) +
+                       (q & 1) * 8;
+    }
+
+    float16v acc[T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; dt++)
+        acc[dt] = float16v{};
+    float m = -INFINITY;   // running maximum of the scaled scores (log2 units)
+    float l = 0.f;         // the lane's share of the running sum
+
+    for (int j = 0; j < nblk; j++) {
+        wait_vmcnt0();
+        lds_barrier();   // tile j in LDS; every wave done with the other stage
+        if (j + 1 < nblk) {
+            const uint32_t st = lds0 + ((j + 1) & 1) * T::STAGE;
+            copy_tile<D, false>(Kh, p.ks[2], (j + 1) * BKV, p.Lk, p.k_bytes, st);
+            copy_tile<D, true>(Vh, p.vs[2], (j + 1) * BKV, p.Lk, p.v_bytes, st + T::BYTES);
+        }
+        const char *ks_tile = smem + (j & 1) * T::STAGE;
+        const char *vs_tile = ks_tile + T::BYTES;
+        const int kv0 = j * BKV;
+
+        // scores of 64 keys x 32 queries: two 32-key tiles
+        float16v s[2] = {float16v{}, float16v{}};
+#pragma unroll
+        for (int ks = 0; ks < T::DK; ks++) {
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const half8 kf = *(const half8 *)(ks_tile + koff[ks] + t * 32 * T::ROWB);
+                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[t], 0, 0, 0);
+            }
+        }
+
+        // scale, mask, tile maximum
+        const bool edge = kv0 + BKV > p.Lk || (CAUSAL && kv0 + BKV - 1 > q0 + shift);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float v = s[t][r] * p.scale_log2;
+                if (edge) {
+                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = key < p.Lk && (!CAUSAL || key <= query + shift);
+                    v = vis ? v : -INFINITY;
+                }
+                s[t][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // nothing visible yet
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        m = m_new;
+
+        // weights, row sum, fp16 weights as second-source fragments
+        half8 pf[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float w = __builtin_amdgcn_exp2f(s[t][r] - m_use);
+                rs += w;
+                pf[2 * t + r / 8][r % 8] = (_Float16)w;
+            }
+        }
+        l = l * alpha + rs;
+
+        // O^T = alpha O^T + V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < T::DT; dt++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[dt][r] *= alpha;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+#pragma unroll
+            for (int dt = 0; dt < T::DT; dt++) {
+                const char *a = vs_tile + voff[dt] + 16 * c * T::ROWB;
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4v *)TGA_LDS(a));
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4v *)TGA_LDS(a + 8 * T::ROWB));
+                const half8 vf = __builtin_bit_cast(
+                    half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], acc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // O = O^T / l, row by row; lse = (m + log2 l) ln 2
+    const float lsum = l + __shfl_xor(l, 32);
+    if (query < p.Lq) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        _Float16 *orow = p.O + b * p.os[0] + hq * p.os[1] + (int64_t)query * p.os[2];
+#pragma unroll
+        for (int dt = 0; dt < T::DT; dt++) {
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const half4 v = {(_Float16)(acc[dt][4 * g] * inv), (_Float16)(acc[dt][4 * g + 1] * inv),
+                                 (_Float16)(acc[dt][4 * g + 2] * inv),
+                                 (_Float16)(acc[dt][4 * g + 3] * inv)};
+                *(half4 *)(orow + 32 * dt + 8 * g + 4 * h) = v;
+            }
+        }
+        if (p.lse != nullptr && h == 0)
+            p.lse[((int64_t)b * p.H + hq) * p.Lq + query] =
+                lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.6931471805599453f : -INFINITY;
+    }
+}
+
+}  // namespace attn
+
+hipError_t launch_attention(const AttentionArgs &a, hipStream_t s)
+{
+    attn::AttnParams p;
+    p.Q = static_cast<const _Float16 *>(a.Q);
+    p.K = static_cast<const _Float16 *>(a.K);
+    p.V = static_cast<const _Float16 *>(a.V);
+    p.O = static_cast<_Float16 *>(a.O);
+    p.lse = a.lse;
+    p.B = a.B;
+    p.H = a.H;
+    p.group = a.H / a.Hkv;
+    p.Lq = a.Lq;
+    p.Lk = a.Lk;
+    for (int i = 0; i < 3; i++) {
+        p.qs[i] = a.qs[i];
+        p.ks[i] = a.ks[i];
+        p.vs[i] = a.vs[i];
+        p.os[i] = a.os[i];
+    }
+    p.k_bytes = a.k_bytes;
+    p.v_bytes = a.v_bytes;
+    p.scale_log2 = a.scale * 1.4426950408889634f;
+    p.nqb = (a.Lq + attn::BQ - 1) / attn::BQ;
+    p.causal = a.causal;
+    const int64_t blocks = (int64_t)a.B * a.H * p.nqb;
+    if (blocks <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(attn::THREADS);
+    if (a.d == 64) {
+        if (a.causal)
+            hipLaunchKernelGGL((attn::attn_fwd<64, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn::attn_fwd<64, false>), grid, block, 0, s, p);
+    } else if (a.d == 128) {
+        if (a.causal)
+            hipLaunchKernelGGL((attn::attn_fwd<128, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn::attn_fwd<128, false>), grid, block, 0, s, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tg

@@ -4,8 +4,9 @@ oracle (oracle/tgref_attention.c).
 Tolerance, from the kernel's arithmetic: the scores and the softmax are fp32
 (relative error ~1e-6), the weights are rounded to fp16 before the second
 product (each off by at most 2^-11 of itself, or 2^-25 absolute below the
-fp16 normal range, with the largest weight exactly 1), and O is rounded to
-fp16 once.  Per element:
+fp16 normal range; they are taken relative to a reference maximum at most
+2^8 below the row's, so the largest is in [1, 256] and the sum is at least
+1), and O is rounded to fp16 once.  Per element:
     |O - O_ref| <= 2^-10 A + n 2^-24 max|V| + ulp16(O_ref)
 with A the softmax-weighted mean |V| the oracle returns and n the number of
 visible keys (twice the weight-rounding bound, for the fp32 terms).  The
@@ -171,3 +172,57 @@ def test_torch_wrapper_and_errors():
     assert tg.tg_attention_fwd(host.ctypes.data, k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                None, B, H, H, L, L, d, st, st, st, st, 0.1, 0,
                                s) == tg.TG_ERROR_NOT_DEVICE_MEMORY
+
+
+def run_values(Qv, Kv, Vv, causal, scale, what):
+    """Attention on given float arrays [B, H, L, d] (rounded to fp16)."""
+    B, H, Lq, d = Qv.shape
+    Hkv, Lk = Kv.shape[1], Kv.shape[2]
+    Q, K, V = (np.ascontiguousarray(x, np.float64).astype(np.float16).view(np.uint16).reshape(-1)
+               for x in (Qv, Kv, Vv))
+    qs, ks = (H * Lq * d, Lq * d, d), (Hkv * Lk * d, Lk * d, d)
+    log("%s B=%d H=%d Lq=%d Lk=%d d=%d causal=%d scale=%g" % (what, B, H, Lq, Lk, d, causal, scale))
+    tq, tk, tv = dev(Q), dev(K), dev(V)
+    to = torch.full((B * H * Lq * d,), F16_NAN, dtype=torch.int16, device="cuda")
+    tl = torch.empty(B * H * Lq, dtype=torch.float32, device="cuda")
+    st = tg.tg_attention_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr(),
+                             tl.data_ptr(), B, H, Hkv, Lq, Lk, d, qs, ks, ks, qs, scale, causal,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == tg.TG_SUCCESS, tg.tg_status_string(st)
+    torch.cuda.synchronize()
+    O = to.cpu().numpy().view(np.uint16).reshape(B, H, Lq, d)
+    lse = tl.cpu().numpy().reshape(B, H, Lq)
+    Oref, lref, A = oracle.attention_ref(Q, K, V, B, H, Hkv, Lq, Lk, d, qs, ks, ks, scale, causal)
+    vmax = np.abs(Vv).max()
+    nv = np.broadcast_to(n_visible(Lq, Lk, causal), (B, H, Lq))
+    check(O, lse, Oref, lref, A, vmax, nv, what)
+
+
+@pytest.mark.parametrize("scale", [-0.1, 0.0, 0.7])
+def test_scale_sign_and_zero(scale):
+    rng = np.random.default_rng(3)
+    Qv, Kv, Vv = (rng.standard_normal((1, 2, 160, 64)) for _ in range(3))
+    run_values(Qv, Kv, Vv, True, scale, "scale %g" % scale)
+
+
+def test_running_maximum_keeps_growing():
+    """Scores rise along the keys (0.8 per key for most rows), so the row
+    maximum jumps past the reference again and again."""
+    L, d = 512, 64
+    rng = np.random.default_rng(4)
+    Qv = 2.0 + 0.1 * rng.standard_normal((1, 1, L, d))
+    Kv = (0.05 * np.arange(L))[None, None, :, None] * np.ones((1, 1, L, d))
+    Vv = rng.standard_normal((1, 1, L, d))
+    for causal in (False, True):
+        run_values(Qv, Kv, Vv, causal, 0.125, "growing max causal=%d" % causal)
+
+
+def test_score_levels_far_from_zero():
+    """All scores near -128 or +120 (natural units): only their differences
+    matter."""
+    L, d = 300, 64
+    rng = np.random.default_rng(5)
+    Kv = -2.0 + 0.05 * rng.standard_normal((1, 2, L, d))
+    Vv = rng.standard_normal((1, 2, L, d))
+    Qv = np.concatenate([np.full((1, 1, L, d), 2.0), np.full((1, 1, L, d), -1.875)], axis=1)
+    run_values(Qv, Kv, Vv, True, 0.125, "far score levels")

@@ -50,8 +50,12 @@ struct Tile {
     static constexpr int ROWB = 2 * D;           // bytes of a K or V row
     static constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per row
     static constexpr int BYTES = BKV * ROWB;     // one K or V tile
-    static constexpr int STAGE = 2 * BYTES;      // K tile, then V tile
-    static constexpr int LDS = 2 * STAGE;        // two-stage ring
+    // d = 128: the scores of tile j + 1 are computed while tile j's softmax
+    // runs (K in a three-stage ring); d = 64 keeps the plain order, where the
+    // fewer registers let more waves share a SIMD instead (measured faster).
+    static constexpr bool PIPE = D == 128;
+    static constexpr int KST = PIPE ? 3 : 2;     // K ring depth; V: two stages
+    static constexpr int LDS = (KST + 2) * BYTES;
     static constexpr int LOADS = BYTES / 1024 / WAVES;   // copies per wave per tile
     static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
     static constexpr int DK = D / 16;            // k-steps of the score product
@@ -138,7 +142,8 @@ struct AttnParams {
     int B, H, group, Lq, Lk;    // group = H / Hkv
     int64_t qs[3], ks[3], vs[3], os[3];   // {batch, head, row} strides, elements
     uint32_t k_bytes, v_bytes;  // descriptor range of one head's K / V rows
-    float scale_log2;           // scale * log2(e)
+    float scale_log2;           // |scale| * log2(e)
+    int negate_q;               // scale < 0: Q is negated on load
     int nqb;                    // query blocks per head
     int causal;
 };
@@ -149,7 +154,7 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
     using T = Tile<D>;
     __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;        // lane half
     const int col = lane & 31;      // the lane's query within the wave
 
@@ -180,11 +185,16 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
 
     const _Float16 *Kh = p.K + b * p.ks[0] + hk * p.ks[1];
     const _Float16 *Vh = p.V + b * p.vs[0] + hk * p.vs[1];
+    // K tiles in a KST-stage ring, V tiles in a two-stage ring; with the
+    // pipelined order K runs two tiles ahead of V.
     const uint32_t lds0 = lds_addr(smem);
+    const uint32_t lds_v = lds0 + T::KST * T::BYTES;
     if (nblk > 0) {
         copy_tile<D, false>(Kh, p.ks[2], 0, p.Lk, p.k_bytes, lds0);
-        copy_tile<D, true>(Vh, p.vs[2], 0, p.Lk, p.v_bytes, lds0 + T::BYTES);
+        copy_tile<D, true>(Vh, p.vs[2], 0, p.Lk, p.v_bytes, lds_v);
     }
+    if (T::PIPE && nblk > 1)
+        copy_tile<D, false>(Kh, p.ks[2], BKV, p.Lk, p.k_bytes, lds0 + T::BYTES);
 
     // the wave's queries as second-source fragments: lane l holds
     // Q[query][16 ks + 8 h .. +7]
@@ -192,10 +202,12 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
     {
         const bool ok = query < p.Lq;
         const _Float16 *qrow = p.Q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? query : 0) * p.qs[2];
+        // a negative scale is applied as |scale| to -Q (negation is exact), so
+        // that the scores are always scaled by a non-negative factor
 #pragma unroll
         for (int ks = 0; ks < T::DK; ks++) {
             const half8 v = *(const half8 *)(qrow + 16 * ks + 8 * h);
-            qf[ks] = ok ? v : half8{};
+            qf[ks] = ok ? (p.negate_q ? -v : v) : half8{};
         }
     }
 
@@ -219,76 +231,141 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
 #pragma unroll
     for (int dt = 0; dt < T::DT; dt++)
         acc[dt] = float16v{};
-    float m = -INFINITY;   // running maximum of the scaled scores (log2 units)
-    float l = 0.f;         // the lane's share of the running sum
+    float m = -INFINITY;   // reference maximum of the scaled scores (log2 units)
+    float l = 0.f;         // the lane's share of the running sum, relative to m
+
+    // scores of 64 keys x 32 queries (two 32-key tiles) from a K tile
+    auto score_mfma = [&](const char *kt, int ks, int t, float16v &acc_s) {
+        const half8 kf = *(const half8 *)(kt + koff[ks] + t * 32 * T::ROWB);
+        acc_s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], acc_s, 0, 0, 0);
+    };
+
+    float16v s[2] = {float16v{}, float16v{}};
+    if (T::PIPE && nblk > 0) {
+        wait_vmcnt0();
+        lds_barrier();
+#pragma unroll
+        for (int ks = 0; ks < T::DK; ks++)
+#pragma unroll
+            for (int t = 0; t < 2; t++)
+                score_mfma(smem, ks, t, s[t]);
+    }
 
     for (int j = 0; j < nblk; j++) {
-        wait_vmcnt0();
-        lds_barrier();   // tile j in LDS; every wave done with the other stage
-        if (j + 1 < nblk) {
-            const uint32_t st = lds0 + ((j + 1) & 1) * T::STAGE;
-            copy_tile<D, false>(Kh, p.ks[2], (j + 1) * BKV, p.Lk, p.k_bytes, st);
-            copy_tile<D, true>(Vh, p.vs[2], (j + 1) * BKV, p.Lk, p.v_bytes, st + T::BYTES);
+        if (!T::PIPE || j > 0) {
+            wait_vmcnt0();
+            // pipelined: K tile j+1 and V tile j in LDS; plain: K and V tile j.
+            // Every wave is past the tiles the copies below overwrite.
+            lds_barrier();
         }
-        const char *ks_tile = smem + (j & 1) * T::STAGE;
-        const char *vs_tile = ks_tile + T::BYTES;
+        if constexpr (T::PIPE) {
+            if (j + 2 < nblk)
+                copy_tile<D, false>(Kh, p.ks[2], (j + 2) * BKV, p.Lk, p.k_bytes,
+                                    lds0 + ((j + 2) % 3) * T::BYTES);
+        } else {
+            if (j + 1 < nblk)
+                copy_tile<D, false>(Kh, p.ks[2], (j + 1) * BKV, p.Lk, p.k_bytes,
+                                    lds0 + ((j + 1) & 1) * T::BYTES);
+        }
+        if (j + 1 < nblk)
+            copy_tile<D, true>(Vh, p.vs[2], (j + 1) * BKV, p.Lk, p.v_bytes,
+                               lds_v + ((j + 1) & 1) * T::BYTES);
+        const char *k_next = smem + ((j + 1) % 3) * T::BYTES;   // stale on the last tile
+        const char *vs_tile = smem + T::KST * T::BYTES + (j & 1) * T::BYTES;
         const int kv0 = j * BKV;
-
-        // scores of 64 keys x 32 queries: two 32-key tiles
-        float16v s[2] = {float16v{}, float16v{}};
+        if constexpr (!T::PIPE) {
+            const char *k_tile = smem + (j & 1) * T::BYTES;
+            s[0] = float16v{};
+            s[1] = float16v{};
 #pragma unroll
-        for (int ks = 0; ks < T::DK; ks++) {
+            for (int ks = 0; ks < T::DK; ks++)
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const half8 kf = *(const half8 *)(ks_tile + koff[ks] + t * 32 * T::ROWB);
-                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[t], 0, 0, 0);
-            }
+                for (int t = 0; t < 2; t++)
+                    score_mfma(k_tile, ks, t, s[t]);
         }
 
-        // scale, mask, tile maximum
+        // Tile maximum of the raw scores.  Only tiles that reach past Lk or
+        // across the causal diagonal of the wave's first query mask anything
+        // (a uniform branch: the others skip the per-key test).
         const bool edge = kv0 + BKV > p.Lk || (CAUSAL && kv0 + BKV - 1 > q0 + shift);
         float mx = -INFINITY;
+        if (edge) {
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
+            for (int t = 0; t < 2; t++) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                float v = s[t][r] * p.scale_log2;
-                if (edge) {
+                for (int r = 0; r < 16; r++) {
                     const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool vis = key < p.Lk && (!CAUSAL || key <= query + shift);
-                    v = vis ? v : -INFINITY;
+                    s[t][r] = vis ? s[t][r] : -INFINITY;
                 }
-                s[t][r] = v;
-                mx = fmaxf(mx, v);
             }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // nothing visible yet
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        m = m_new;
-
-        // weights, row sum, fp16 weights as second-source fragments
-        half8 pf[4];
-        float rs = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float w = __builtin_amdgcn_exp2f(s[t][r] - m_use);
-                rs += w;
-                pf[2 * t + r / 8][r % 8] = (_Float16)w;
-            }
-        }
-        l = l * alpha + rs;
-
-        // O^T = alpha O^T + V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < T::DT; dt++) {
+        for (int t = 0; t < 2; t++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                acc[dt][r] *= alpha;
+                mx = fmaxf(mx, s[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+        // Lazy rescale: the weights are taken relative to a reference m that
+        // moves only when some row's maximum exceeds it by more than 2^8, so
+        // the weights stay below 256 (exact range for fp16) and O^T and l are
+        // rescaled rarely -- the first tile, and when the maximum jumps.
+        // m stays -inf while a row has seen no visible key.
+        const float mt = mx * p.scale_log2;          // tile maximum, log2 units
+        if (__builtin_amdgcn_ballot_w64(mt > m + 8.f) != 0) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+            for (int dt = 0; dt < T::DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    acc[dt][r] *= alpha;
+            l *= alpha;
+            m = m_new;
         }
+        // a row with no visible key yet has only -inf scores: weight 0
+        const float m_w = m == -INFINITY ? 0.f : m;
+
+        // The next tile's scores on the matrix cores, interleaved with this
+        // tile's weights exp2(s scale log2e - m), row sum and fp16 weights
+        // on the vector unit.
+        float16v sn[2] = {float16v{}, float16v{}};
+        half8 pf[4];
+        float rs = 0.f;
+        if constexpr (!T::PIPE) {
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float w =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], p.scale_log2, -m_w));
+                    rs += w;
+                    pf[2 * t + r / 8][r % 8] = (_Float16)w;
+                }
+            }
+        }
+        // pipelined: 2 DK MFMAs and 32 weights, 32 / (2 DK) weights per MFMA
+        constexpr int NM = 2 * T::DK, WPM = 32 / NM;
+        half8 kf_next = T::PIPE ? *(const half8 *)(k_next + koff[0]) : half8{};
+#pragma unroll
+        for (int i = 0; i < (T::PIPE ? NM : 0); i++) {
+            const int ks = i / 2, t = i % 2;
+            const half8 kf = kf_next;
+            if (i + 1 < NM)
+                kf_next = *(const half8 *)(k_next + koff[(i + 1) / 2] + ((i + 1) % 2) * 32 * T::ROWB);
+            sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sn[t], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < WPM; u++) {
+                const int e = i * WPM + u, tt = e / 16, r = e % 16;
+                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], p.scale_log2, -m_w));
+                rs += w;
+                pf[2 * tt + r / 8][r % 8] = (_Float16)w;
+            }
+        }
+        l += rs;
+
+        // O^T += V^T P^T
 #pragma unroll
         for (int c = 0; c < 4; c++) {
 #pragma unroll
@@ -302,6 +379,10 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
                     half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], acc[dt], 0, 0, 0);
             }
+        }
+        if constexpr (T::PIPE) {
+            s[0] = sn[0];
+            s[1] = sn[1];
         }
     }
 
@@ -349,7 +430,14 @@ hipError_t launch_attention(const AttentionArgs &a, hipStream_t s)
     }
     p.k_bytes = a.k_bytes;
     p.v_bytes = a.v_bytes;
-    p.scale_log2 = a.scale * 1.4426950408889634f;
+    // The kernel scales raw scores by this factor inside the exponent, with
+    // -inf for masked keys; a zero scale (uniform weights) becomes 1e-30,
+    // which keeps -inf * factor = -inf and changes a weight by a relative
+    // 1e-30 |s| at most.
+    p.scale_log2 = fabsf(a.scale) * 1.4426950408889634f;
+    if (p.scale_log2 < 1e-30f)
+        p.scale_log2 = 1e-30f;
+    p.negate_q = a.scale < 0.f;
     p.nqb = (a.Lq + attn::BQ - 1) / attn::BQ;
     p.causal = a.causal;
     const int64_t blocks = (int64_t)a.B * a.H * p.nqb;

@@ -47,6 +47,24 @@ TRAFFIC_BYTES = {
 }
 
 
+# The same for the fused attention kernel, keyed by workload and a digest of
+# its sources.
+ATTN_TRAFFIC_BYTES = {
+    # FETCH_SIZE 49250 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
+    ("attn_b2h16l4096d128", "7a3336028ff3addc"): 134942720,
+}
+
+
+def attention_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_gemm_08_amd", "csrc")
+    for name in ("tg_attention.hip", "tg_attention.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def kernel_source_digest():
     import hashlib
     h = hashlib.sha256()
@@ -350,7 +368,8 @@ def bench_attention(a):
                    "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": ATTN_TRAFFIC_BYTES.get((a.workload, attention_source_digest()))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -51,7 +51,7 @@ TRAFFIC_BYTES = {
 # its sources.
 ATTN_TRAFFIC_BYTES = {
     # FETCH_SIZE 49250 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
-    ("attn_b2h16l4096d128", "7a3336028ff3addc"): 134942720,
+    ("attn_b2h16l4096d128", "8b5565eeac876f68"): 134942720,
 }
 
 

@@ -164,11 +164,23 @@ __global__ void __launch_bounds__(THREADS, 2) attn_fwd(AttnParams p)
     const int bid = blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
     const int per = total >> 3, rem = total & 7;
-    const int t_log = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const int bh = t_log / p.nqb;
+    const int start = xcd * per + (xcd < rem ? xcd : rem);
+    const int t_log = start + slot;
+    int bh = t_log / p.nqb;
     int qb = t_log - bh * p.nqb;
-    if constexpr (CAUSAL)
-        qb = p.nqb - 1 - qb;   // longest rows first
+    if constexpr (CAUSAL) {
+        // longest rows first: when the XCD's range holds whole heads, walk it
+        // by query block (longest first) across those heads, so that every
+        // CU of the XCD starts on long work; else longest first per head
+        const int cnt = per + (xcd < rem ? 1 : 0);
+        if (start % p.nqb == 0 && cnt % p.nqb == 0) {
+            const int heads = cnt / p.nqb;
+            bh = start / p.nqb + slot % heads;
+            qb = p.nqb - 1 - slot / heads;
+        } else {
+            qb = p.nqb - 1 - qb;
+        }
+    }
     const int b = bh / p.H, hq = bh - b * p.H, hk = hq / p.group;
     const int q_wg = qb * BQ;
     const int q0 = q_wg + wave * 32;      // the wave's first query

@@ -9,8 +9,10 @@ N(0,1)/sqrt(K) values from seed 2, fp32 accumulation, fp16 C).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--config ID]
 
 Reported: whole-job TFLOP/s (2MNK per step), the dominant kernel's MFMA
-roofline fraction measured with HIP events on the launch stream, and the
-CPU oracle timed on a bounded sample of the same workload on the host cores.
+roofline fraction measured with HIP events on the launch stream, the median
+and minimum of single launches (timed separately, after the K steps), and
+the CPU oracle timed on a bounded sample of the same workload on the host
+cores.
 Before timing, the output is checked against the oracle on sampled entries;
 a failing check prints no throughput.
 """
@@ -42,8 +44,8 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # digest of the kernel sources: a kernel changed since the counters were
 # taken reports null.
 TRAFFIC_BYTES = {
-    # FETCH_SIZE 804839 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
-    ("sq8192", "pipe_256x256x64_s2_w2x4_mi32_c0", "1a83d4263a30edfe"): 1782528000,
+    # FETCH_SIZE 816401 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x4_mi32_c0", "33f26c9a316014b6"): 1806207236,
 }
 
 
@@ -73,6 +75,31 @@ def kernel_source_digest():
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def launch_stats(step, stream, n=20):
+    """Median and minimum time of single launches, each between its own pair
+    of events on the launch stream (a separate loop after the timed steps)."""
+    import torch
+    times = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return {"median_ms": round(times[len(times) // 2], 5), "min_ms": round(times[0], 5),
+            "launches": n}
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "cus": p.multi_processor_count}
 
 
 def parse():
@@ -142,15 +169,22 @@ def main():
     pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
     pbias = bias.data_ptr() if fused else None
     op_a, op_b, lda, ldb = w["op_a"], w["op_b"], w["lda"], w["ldb"]
-    cid = a.config
+    # the dispatcher's call (tg_gemm_ex), copies of packed operands included,
+    # unless a configuration is named
+    cid, packed = a.config, 0
     if cid is None:
-        cid = tg.tg_select_config(pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, op_a=op_a,
-                                  op_b=op_b)
+        st, cid, packed, _ = tg.tg_select_plan(pa, pb, pbias, pc, M, N, K, lda, ldb, N, code,
+                                               op_a=op_a, op_b=op_b)
+        assert st == tg.TG_SUCCESS
     info = tg.tg_config_info(cid)
+    forced = a.config is not None
 
     def step():
-        st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s,
-                                    op_a=op_a, op_b=op_b)
+        if forced:
+            st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s,
+                                        op_a=op_a, op_b=op_b)
+        else:
+            st = tg.tg_gemm_ex(op_a, op_b, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s)
         if st != tg.TG_SUCCESS:
             raise RuntimeError(tg.tg_status_string(st))
 
@@ -198,6 +232,7 @@ def main():
     elapsed = max(wall, gpu_ms / 1e3)
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
+    single = launch_stats(step, stream)
 
     # ---- CPU oracle baseline on a bounded sample (whole rows of C)
     cpu = None
@@ -242,7 +277,11 @@ def main():
         "config": {"workload": a.workload, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
                    "fused_bias_relu": fused, "op_a": "T" if op_a else "N",
                    "op_b": "T" if op_b else "N", "kernel": info["name"],
+                   "packed_operands": "".join(x for x, bit in (("A", 1), ("B", 2))
+                                              if packed & bit) or None,
                    "pct_of_peak": round(100.0 * value / peak, 2)},
+        "single_launch": single,
+        "device": device_info(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic},
@@ -328,6 +367,7 @@ def bench_attention(a):
     elapsed = max(wall, gpu_ms / 1e3)
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
+    single = launch_stats(step, stream)
 
     # ---- CPU oracle baseline: whole query rows, sampled
     cpu = None
@@ -366,6 +406,8 @@ def bench_attention(a):
         "config": {"workload": a.workload, "B": B, "H": H, "Hkv": Hkv, "Lq": Lq, "Lk": Lk,
                    "d": d, "causal": bool(causal), "kernel": "attn_fwd<%d,%s>" % (d, bool(causal)),
                    "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+        "single_launch": single,
+        "device": device_info(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS, 4),

@@ -200,11 +200,13 @@ const char *tg_status_string(tg_status s);
  *   1. the run-time tuning cache below (exact shape, orientation, C dtype and
  *      fused flag),
  *   2. a compiled table of exact shapes,
- *   3. a compiled shape-class grid: the nearest grid point in log2 distance
- *      along M, N and K, whose configurations are ranked by on-device timing,
+ *   3. a compiled cost model: per configuration, the time of a full and of a
+ *      lone round of workgroups as a function of K, fitted to on-device
+ *      timings; the configuration with the least predicted time wins,
  *   4. the register-staged kernels, which take any alignment,
  * and at each step uses the configuration only if it can run the problem
- * (tg_config_supports). */
+ * (tg_config_supports).  After steps 2-4, operands that rule out the direct
+ * copies may be packed first (see "packed operands" below). */
 
 typedef struct {
     int id;
@@ -235,8 +237,10 @@ int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void
                        const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
 
-/* The configuration id the dispatcher would use for this call, or -1 for
- * invalid arguments.  Touches no device state. */
+/* The configuration id the dispatcher would run on the operands as passed,
+ * or -1 for invalid arguments (when it packs operands first, the call runs
+ * the configuration tg_select_plan reports instead).  Touches no device
+ * state. */
 int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
                      const void *C, int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
@@ -249,6 +253,66 @@ tg_status tg_gemm_with_config(int config_id, tg_op op_a, tg_op op_b, const void 
                               int64_t M, int64_t N, int64_t K,
                               int64_t lda, int64_t ldb, int64_t ldc,
                               tg_dtype c_dtype, hipStream_t stream);
+
+/* ---- packed operands and library scratch ---------------------------------
+ * The direct configurations copy 16-byte chunks of A and B straight to LDS;
+ * an operand whose base is not 16-byte aligned, or whose leading dimension or
+ * row length is not a multiple of 16 bytes, otherwise goes to a register-
+ * staged configuration.  The dispatcher (tg_gemm, tg_gemm_bias_relu and
+ * tg_gemm_ex; never for a tuning-cache hit, and never tg_gemm_with_config or
+ * tg_gemm_splitk) may instead copy such an
+ * operand first into a packed layout -- the same stored rows, each padded
+ * with zeros to a multiple of 16 bytes, which is also the copy's leading
+ * dimension -- and run a direct configuration on the copy with K rounded up
+ * to a whole chunk.  It does so when its cost model predicts the copy plus
+ * the direct kernel to be faster.  Results equal the unpacked ones within
+ * the usual rounding (zeros added to a sum change nothing; on integer inputs
+ * they are bit-identical).
+ *
+ * The copy lives in device memory the library allocates (hipMalloc) and
+ * keeps: one buffer per (device, stream), grown when a call needs more
+ * (growing waits for the stream and frees the old buffer).  While a stream
+ * is being captured into a graph the library never allocates: a call whose
+ * copy does not fit the stream's buffer runs unpacked.  Calls on different
+ * streams use different buffers; calls from several host threads on one
+ * stream are serialized while they enqueue their kernels, so they never
+ * share a copy.  A buffer is kept until tg_scratch_release or the end of the
+ * process, also after its stream is destroyed.  A graph captured from a
+ * packed call refers to its stream's buffer: when a later call replaces that
+ * buffer with a larger one, the old one is kept (not freed) until
+ * tg_scratch_release, so the graph stays valid until then.
+ *
+ * Policy: TG_PACK_AUTO (the default) packs as above; TG_PACK_NEVER never
+ * packs (the library then allocates nothing); TG_PACK_ALWAYS packs whenever
+ * an operand rules out the direct copies and a direct configuration can run
+ * the copies.  The initial policy comes from the environment variable
+ * TG_PACK ("auto", "never" or "always"; anything else: auto), read at the
+ * first call that needs it. */
+enum { TG_PACK_AUTO = 0, TG_PACK_NEVER = 1, TG_PACK_ALWAYS = 2 };
+
+/* Set the pack policy for the process; returns the previous one, or -1 (and
+ * changes nothing) for an unknown value.  Takes effect for later calls. */
+int tg_set_pack_policy(int policy);
+
+/* What the dispatcher does for this call: *config_id the configuration that
+ * runs (-1 for an empty problem), *packed a bit mask of the operands copied
+ * first (1: A, 2: B; 0: none) and *scratch_bytes the scratch those copies
+ * need (the call may still run unpacked under stream capture, see above).
+ * Touches no device state; TG_ERROR_INVALID_VALUE for invalid arguments or
+ * NULL outputs. */
+tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                         int *config_id, int *packed, size_t *scratch_bytes);
+
+/* Free the scratch of every device and stream, after waiting for each device
+ * that holds some to finish its work.  Must not race with GEMM calls, and
+ * graphs captured from packed calls must not be replayed afterwards.
+ * TG_ERROR_LAUNCH if a HIP call fails (the buffers are forgotten anyway). */
+tg_status tg_scratch_release(void);
+
+/* Bytes of scratch the library holds, over all devices and streams. */
+size_t tg_scratch_held(void);
 
 /* ---- run-time tuning cache ------------------------------------------------
  * Exact-shape records written by the on-device sweep (the sweep's --tune

@@ -27,11 +27,16 @@ TG_ERROR_FILE = 5
 TG_OP_N = 0
 TG_OP_T = 1
 
+TG_PACK_AUTO = 0
+TG_PACK_NEVER = 1
+TG_PACK_ALWAYS = 2
+
 # every function declared in include/tg.h
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
             "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk",
+            "tg_select_plan", "tg_scratch_release", "tg_scratch_held", "tg_set_pack_policy",
             "tg_attention_fwd", "tg_version")
 
 
@@ -91,6 +96,14 @@ def _load():
     L.tg_gemm_splitk.restype = I
     L.tg_select_splitk.argtypes = [I, I] + shape_args + [SZ, IP, IP]
     L.tg_select_splitk.restype = I
+    L.tg_select_plan.argtypes = [I, I] + shape_args + [IP, IP, ctypes.POINTER(SZ)]
+    L.tg_select_plan.restype = I
+    L.tg_scratch_release.argtypes = []
+    L.tg_scratch_release.restype = I
+    L.tg_scratch_held.argtypes = []
+    L.tg_scratch_held.restype = SZ
+    L.tg_set_pack_policy.argtypes = [I]
+    L.tg_set_pack_policy.restype = I
     L.tg_attention_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
                                    ctypes.c_float, I, P]
     L.tg_attention_fwd.restype = I
@@ -153,6 +166,26 @@ def tg_config_supports(config_id, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype
 def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_N,
                      op_b=TG_OP_N):
     return lib.tg_select_config(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
+
+
+def tg_select_plan(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_N, op_b=TG_OP_N):
+    """(status, config id, packed-operand mask (1: A, 2: B), scratch bytes)."""
+    cid, packed, scratch = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_size_t(0)
+    st = lib.tg_select_plan(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                            ctypes.byref(cid), ctypes.byref(packed), ctypes.byref(scratch))
+    return st, cid.value, packed.value, scratch.value
+
+
+def tg_scratch_release():
+    return lib.tg_scratch_release()
+
+
+def tg_scratch_held():
+    return lib.tg_scratch_held()
+
+
+def tg_set_pack_policy(policy):
+    return lib.tg_set_pack_policy(policy)
 
 
 def tg_splitk_workspace_bytes(M, N, splits):

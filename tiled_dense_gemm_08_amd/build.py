@@ -32,6 +32,7 @@ FLAGS = ["-O3", "-std=c++20", "--offload-arch=" + ARCH,
 
 SHARDS = 8   # kernel compilations run in parallel (tg_kernels.hip, TG_SHARD=i)
 ATTN = os.path.join(CSRC, "tg_attention.hip")
+PACK = os.path.join(CSRC, "tg_pack.hip")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 
@@ -80,9 +81,10 @@ def build_lib():
     api = os.path.join(BUILD_DIR, "tg_api.%s.o" % tag)
     objs.append(api)
     cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", api, os.path.join(CSRC, "tg_api.cpp")])
-    att = os.path.join(BUILD_DIR, "tg_attention.%s.o" % tag)
-    objs.append(att)
-    cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", att, ATTN])
+    for src in (ATTN, PACK):
+        o = os.path.join(BUILD_DIR, "%s.%s.o" % (os.path.basename(src)[:-4], tag))
+        objs.append(o)
+        cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", o, src])
     try:
         _run_all(cmds)
         tmp = LIB + ".tmp" + tag
@@ -100,10 +102,12 @@ def device_asm(path=None):
     path = path or os.path.join(BUILD_DIR, "tg_kernels.s")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     kern = os.path.join(CSRC, "tg_kernels.hip")
-    parts = [path + ".%d" % i for i in range(SHARDS)] + [path + ".attn"]
+    extra = (ATTN, PACK)
+    parts = [path + ".%d" % i for i in range(SHARDS)] + [path + ".x%d" % i for i in range(len(extra))]
     _run_all([[HIPCC] + FLAGS + _shard_flags(i) + ["--cuda-device-only", "-S", "-o", parts[i], kern]
               for i in range(SHARDS)] +
-             [[HIPCC] + FLAGS + ["--cuda-device-only", "-S", "-o", parts[-1], ATTN]])
+             [[HIPCC] + FLAGS + ["--cuda-device-only", "-S", "-o", parts[SHARDS + i], src]
+              for i, src in enumerate(extra)])
     with open(path, "w") as f:
         for q in parts:
             f.write(open(q).read())

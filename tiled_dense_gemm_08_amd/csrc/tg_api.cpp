@@ -16,13 +16,17 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <map>
 #include <memory>
 #include <mutex>
 #include <unordered_map>
+#include <utility>
+#include <vector>
 
 #include "tg.h"
 #include "tg_attention.h"
 #include "tg_kernels.h"
+#include "tg_pack.h"
 
 namespace {
 
@@ -234,14 +238,15 @@ bool row_applies(const ModelRow &r, const Problem &p, int pad)
 }
 
 // The modelled configuration with the least predicted time that can run the
-// problem (ties: the lower id), or -1.
-int model_lookup(const Problem &p)
+// problem (ties: the lower id), or -1; its predicted time in *t_out.
+// direct_only: among the direct-copy configurations only.
+int model_lookup(const Problem &p, double *t_out = nullptr, bool direct_only = false)
 {
     const int pad = operands_aligned(p) ? 0 : 1;
     int best = -1;
     double best_t = 0.0;
     for (const ModelRow &r : kModel) {
-        if (!row_applies(r, p, pad))
+        if (!row_applies(r, p, pad) || (direct_only && !kConfigs[r.id].direct))
             continue;
         const double t = model_time(r, kConfigs[r.id], p);
         if (best < 0 || t < best_t || (t == best_t && r.id < best)) {
@@ -249,6 +254,8 @@ int model_lookup(const Problem &p)
             best_t = t;
         }
     }
+    if (t_out)
+        *t_out = best_t;
     return best;
 }
 
@@ -555,9 +562,6 @@ tg_status make_params(const KernelConfig &cfg, const Problem &p, Params *out)
     const int64_t b_span = elem_size(p) * span_elems(b_rows(p), b_cols(p), p.ldb);
     k.a_bytes = (uint32_t)(a_span < kMaxSpan ? a_span : 0);
     k.b_bytes = (uint32_t)(b_span < kMaxSpan ? b_span : 0);
-    const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
-    k.vec_store = (p.ldc % 4 == 0) && aligned(p.C, 4 * c_elem);
-    k.line_store = ((p.ldc * c_elem) % 16 == 0) && aligned(p.C, 16);
     k.vec_bias = p.fused && aligned(p.bias, 16);
     k.splits = 1;
     if ((int64_t)k.tiles_m * k.tiles_n > kMaxDim)
@@ -588,6 +592,236 @@ tg_status launch_config(int id, const Params &k, bool f16_out, bool bias, hipStr
     return launch(k, f16_out, bias, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
 }
 
+// ---- packed operands -----------------------------------------------------------
+// An operand the direct global->LDS copies cannot take (base not 16-byte
+// aligned, or leading dimension or row length not a multiple of 16 bytes) is
+// otherwise served by the register-staged kernels, which hide less memory
+// latency.  The dispatcher may instead copy it into library-held scratch, in a
+// packed layout: the same stored rows, each padded with zeros to a multiple of
+// 16 bytes, which is also the copy's leading dimension (tg_pack.hip).  The
+// direct kernel then runs on the copy; the kernel's K is K rounded up to a
+// whole 16-byte chunk (the padding holds zeros, and the rows past K of an
+// operand whose rows run along K lie past its copy range, which reads zeros).
+// Chosen when the modelled time of the best direct configuration on the copy,
+// plus the copy's modelled time, is below the best modelled time without it.
+// Copy time: a fixed part (the extra launch) and the bytes read and written
+// at an effective rate; fitted to on-device traces of the copy kernel for
+// copies of 0.5 MB .. 0.5 GB (3.4 us + bytes / 6.1e6 per us), rounded up.
+constexpr double kPackFixedUs = 4.0;
+constexpr double kPackBytesPerUs = 5.5e6;
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct PackPlan {
+    int id = -1;                 // direct configuration run on the copies
+    bool pack[2] = {false, false};
+    Problem kp;                  // the problem the kernel sees (copy pointers set at run time)
+    tg::PackOperand op[2];       // the copies' geometry (src set, dst set at run time)
+    int64_t copy_bytes[2] = {0, 0};   // bytes of each copy
+    int64_t range[2] = {0, 0};        // copy ranges of the kernel's operands (bytes)
+    size_t scratch = 0;          // scratch bytes for both copies
+    double t = 0.0;              // modelled time, copies included
+};
+
+bool operand_direct_layout(const Problem &p, bool is_a)
+{
+    const void *ptr = is_a ? p.A : p.B;
+    const OperandShape o = is_a ? OperandShape{p.op_a == 0, p.M, p.lda, 0}
+                                : OperandShape{p.op_b == 1, p.N, p.ldb, 0};
+    return aligned(ptr, 16) && chunks_aligned(o, p);
+}
+
+// Pack policy (TG_PACK_AUTO / _NEVER / _ALWAYS): initial value from the
+// environment variable TG_PACK ("auto", "never", "always"), read once.
+std::atomic<int> g_pack_policy{-1};
+
+int pack_policy()
+{
+    int v = g_pack_policy.load(std::memory_order_relaxed);
+    if (v >= 0)
+        return v;
+    const char *e = getenv("TG_PACK");
+    v = TG_PACK_AUTO;
+    if (e && strcmp(e, "never") == 0)
+        v = TG_PACK_NEVER;
+    else if (e && strcmp(e, "always") == 0)
+        v = TG_PACK_ALWAYS;
+    int expected = -1;
+    g_pack_policy.compare_exchange_strong(expected, v, std::memory_order_relaxed);
+    return g_pack_policy.load(std::memory_order_relaxed);
+}
+
+// The pack plan for p, or false when the policy rules packing out, no direct
+// configuration can run the copies, or (policy auto) the plan is not
+// predicted to be faster than the best modelled configuration without copies.
+bool plan_pack(const Problem &p, PackPlan *out)
+{
+    const int policy = pack_policy();
+    if (policy == TG_PACK_NEVER || p.M == 0 || p.N == 0 || p.K == 0 || operands_aligned(p))
+        return false;
+    double t_plain = 0.0;
+    if (model_lookup(p, &t_plain) < 0 && policy != TG_PACK_ALWAYS)
+        return false;
+    const int64_t es = elem_size(p), ce = 16 / es;
+    PackPlan pl;
+    pl.pack[0] = !operand_direct_layout(p, true);
+    pl.pack[1] = !operand_direct_layout(p, false);
+    Problem kp = p;
+    kp.K = round_up(p.K, ce);
+    // the problem the eligibility check sees: packed rows along M or N are
+    // whole chunks of the copy
+    Problem chk = kp;
+    double bytes = 0.0;
+    for (int w = 0; w < 2; w++) {
+        const bool is_a = w == 0;
+        const bool kmaj = is_a ? p.op_a == 0 : p.op_b == 1;
+        const int64_t rows = is_a ? a_rows(p) : b_rows(p);
+        const int64_t cols = is_a ? a_cols(p) : b_cols(p);
+        const int64_t ld = is_a ? p.lda : p.ldb;
+        if (!pl.pack[w]) {
+            // unpacked: its own rows; an operand whose rows run along K keeps
+            // its K rows in range, so the kernel's extra K rows read zeros
+            pl.range[w] = es * span_elems(rows, cols, ld);
+            continue;
+        }
+        const int64_t cols_p = round_up(cols, ce);
+        const int64_t copy = rows * cols_p * es;
+        if (copy >= kMaxSpan)
+            return false;
+        pl.op[w] = tg::PackOperand{is_a ? p.A : p.B, nullptr, rows, cols, ld, cols_p, (int)es};
+        pl.copy_bytes[w] = copy;
+        pl.range[w] = copy;
+        pl.scratch += (size_t)round_up(copy, 256);
+        bytes += (double)(es * span_elems(rows, cols, ld) + copy);
+        if (is_a) {
+            kp.lda = cols_p;
+            chk.lda = cols_p;
+            if (!kmaj)
+                chk.M = cols_p;
+        } else {
+            kp.ldb = cols_p;
+            chk.ldb = cols_p;
+            if (!kmaj)
+                chk.N = cols_p;
+        }
+    }
+    // stand-in 16-byte-aligned addresses for the eligibility check
+    chk.A = pl.pack[0] ? reinterpret_cast<const void *>(uintptr_t(256)) : p.A;
+    chk.B = pl.pack[1] ? reinterpret_cast<const void *>(uintptr_t(512)) : p.B;
+    if (!operands_aligned(chk))
+        return false;
+    double t_direct = 0.0;
+    const int id = model_lookup(chk, &t_direct, true);
+    if (id < 0)
+        return false;
+    pl.id = id;
+    pl.kp = kp;
+    pl.t = t_direct + kPackFixedUs + bytes / kPackBytesPerUs;
+    if (policy == TG_PACK_AUTO && !(pl.t < t_plain))
+        return false;
+    *out = pl;
+    return true;
+}
+
+// Library-held scratch for the copies: one buffer per (device, stream), grown
+// on demand and kept until tg_scratch_release or the end of the process.
+// Calls on one stream are ordered by the stream, so they share its buffer; the
+// lock is held from taking the buffer until the kernels that use it are
+// enqueued, so two host threads on one stream cannot interleave their copies.
+struct Scratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    bool captured = false;   // a captured graph may refer to this buffer
+};
+struct Retired {
+    int dev;
+    void *ptr;
+    size_t bytes;
+};
+std::mutex g_scratch_mu;
+std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
+std::vector<Retired> g_retired;   // replaced buffers that captured graphs may use
+
+// A buffer of at least `bytes` on the current device `dev` for `stream`
+// (caller holds g_scratch_mu), or nullptr: never allocated while the stream
+// is being captured into a graph, nor when the allocation fails.  A buffer
+// that a captured call used is not freed when it is replaced (a graph may
+// still replay that call) but kept until tg_scratch_release.
+void *scratch_for(int dev, hipStream_t stream, size_t bytes)
+{
+    Scratch &s = g_scratch[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (s.bytes >= bytes) {
+        s.captured = s.captured || capturing;
+        return s.ptr;
+    }
+    if (capturing)
+        return nullptr;
+    if (s.ptr != nullptr) {
+        if (s.captured) {
+            g_retired.push_back(Retired{dev, s.ptr, s.bytes});
+        } else {
+            // earlier work on this stream may still read the old buffer
+            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(s.ptr) != hipSuccess) {
+                (void)hipGetLastError();
+                return nullptr;
+            }
+        }
+        s.ptr = nullptr;
+        s.bytes = 0;
+        s.captured = false;
+    }
+    const size_t want = (size_t)round_up((int64_t)(bytes + bytes / 4), int64_t(1) << 21);
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    s.ptr = ptr;
+    s.bytes = want;
+    return ptr;
+}
+
+// Runs the plan: copies, then the direct kernel on them.  TG_ERROR_UNSUPPORTED
+// when no scratch can be had (the caller then runs the problem unpacked).
+tg_status run_packed(const PackPlan &plan, const Problem &p, int dev, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    char *buf = static_cast<char *>(scratch_for(dev, stream, plan.scratch));
+    if (buf == nullptr)
+        return TG_ERROR_UNSUPPORTED;
+    Problem kp = plan.kp;
+    tg::PackOperand ops[2];
+    int n = 0;
+    size_t at = 0;
+    for (int w = 0; w < 2; w++) {
+        if (!plan.pack[w])
+            continue;
+        ops[n] = plan.op[w];
+        ops[n].dst = buf + at;
+        (w == 0 ? kp.A : kp.B) = buf + at;
+        at += (size_t)round_up(plan.copy_bytes[w], 256);
+        n++;
+    }
+    (void)hipGetLastError();
+    if (tg::launch_pack(ops, n, stream) != hipSuccess)
+        return TG_ERROR_LAUNCH;
+    const KernelConfig &cfg = kConfigs[plan.id];
+    Params k;
+    tg_status st = make_params(cfg, kp, &k);
+    if (st != TG_SUCCESS)
+        return st;
+    k.a_bytes = (uint32_t)plan.range[0];
+    k.b_bytes = (uint32_t)plan.range[1];
+    (void)p;
+    return launch_config(plan.id, k, kp.c_dtype == TG_DTYPE_F16, kp.fused, stream);
+}
+
 tg_status run(int config_id, const Problem &p, hipStream_t stream)
 {
     tg_status st = validate(p);
@@ -604,6 +838,12 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     int dev = 0;
     if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
         return st;
+    PackPlan plan;
+    if (config_id < 0 && tuned_lookup(p) < 0 && plan_pack(p, &plan)) {
+        st = run_packed(plan, p, dev, stream);
+        if (st != TG_ERROR_UNSUPPORTED)
+            return st;
+    }
     Params k;
     if ((st = make_params(cfg, p, &k)) != TG_SUCCESS)
         return st;
@@ -957,6 +1197,85 @@ int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void
     if (id < 0 || id >= kNumConfigs || validate(p) != TG_SUCCESS)
         return -1;
     return supports(kConfigs[id], p) ? 1 : 0;
+}
+
+tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                         int *config_id, int *packed, size_t *scratch_bytes)
+{
+    if (config_id == nullptr || packed == nullptr || scratch_bytes == nullptr)
+        return TG_ERROR_INVALID_VALUE;
+    *config_id = -1;
+    *packed = 0;
+    *scratch_bytes = 0;
+    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
+              op_a, op_b};
+    const tg_status st = validate(p);
+    if (st != TG_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_SUCCESS;
+    PackPlan plan;
+    if (tuned_lookup(p) < 0 && plan_pack(p, &plan)) {
+        *config_id = plan.id;
+        *packed = (plan.pack[0] ? 1 : 0) | (plan.pack[1] ? 2 : 0);
+        *scratch_bytes = plan.scratch;
+        return TG_SUCCESS;
+    }
+    *config_id = choose(p);
+    return TG_SUCCESS;
+}
+
+tg_status tg_scratch_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    std::vector<Retired> all = g_retired;
+    for (const auto &e : g_scratch)
+        if (e.second.ptr != nullptr)
+            all.push_back(Retired{e.first.first, e.second.ptr, e.second.bytes});
+    g_scratch.clear();
+    g_retired.clear();
+    tg_status st = TG_SUCCESS;
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    std::vector<int> synced;
+    for (const Retired &r : all) {
+        bool done = false;
+        for (int d : synced)
+            done = done || d == r.dev;
+        if (!done) {
+            if (hipSetDevice(r.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+                st = TG_ERROR_LAUNCH;
+            synced.push_back(r.dev);
+        }
+        if (hipFree(r.ptr) != hipSuccess)
+            st = TG_ERROR_LAUNCH;
+    }
+    if (have_cur)
+        (void)hipSetDevice(cur);
+    (void)hipGetLastError();
+    return st;
+}
+
+int tg_set_pack_policy(int policy)
+{
+    if (policy != TG_PACK_AUTO && policy != TG_PACK_NEVER && policy != TG_PACK_ALWAYS)
+        return -1;
+    const int prev = pack_policy();
+    g_pack_policy.store(policy, std::memory_order_relaxed);
+    return prev;
+}
+
+size_t tg_scratch_held(void)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    size_t n = 0;
+    for (const auto &e : g_scratch)
+        n += e.second.bytes;
+    for (const Retired &r : g_retired)
+        n += r.bytes;
+    return n;
 }
 
 int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,

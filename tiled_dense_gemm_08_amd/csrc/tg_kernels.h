@@ -20,8 +20,6 @@ struct Params {
     int tiles_m, tiles_n, group_m;
     uint32_t a_bytes, b_bytes;
     int trans_a, trans_b;   // A stored K x M / B stored N x K
-    int vec_store;   // C rows allow 4-element vector stores (alignment)
-    int line_store;  // C rows allow 16-byte stores: staged, full-line epilogue
     int vec_bias;    // bias allows 16-byte loads
     // K slicing (split-K), used when splits > 1: workgroup row blockIdx.y = z
     // multiplies the K range [z k_split, min((z + 1) k_split, K)) and writes

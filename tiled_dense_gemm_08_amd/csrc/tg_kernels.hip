@@ -399,43 +399,6 @@ __device__ __forceinline__ void store4(char *dst, V v)
     }
 }
 
-// Direct epilogue: each lane stores its 4-column runs straight to C.  Used when
-// C's rows do not allow 16-byte stores (unaligned base or leading dimension).
-template <class C, typename OutT, bool BIAS>
-__device__ __forceinline__ void epilogue_direct(const Params &p, int m_base, int n_base,
-                                                typename C::acc_t (&acc)[C::MT][C::NT])
-{
-    const int lane = threadIdx.x & 63;
-    const bool vec_ok = p.vec_store != 0;
-    constexpr int RUNS = C::ACC / 4;
-#pragma unroll
-    for (int nt = 0; nt < C::NT; nt++) {
-#pragma unroll
-        for (int run = 0; run < RUNS; run++) {
-            const int col = n_base + run_col<C>(nt, run);
-            float4v bv = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS)
-                bv = load_bias4(p, col);
-#pragma unroll
-            for (int mt = 0; mt < C::MT; mt++) {
-                const int row = m_base + mt * C::MI + lane % C::MI;
-                if (row >= p.M)
-                    continue;
-                const val4_t<C> v = epi_value<C, BIAS>(acc[mt][nt], run, bv);
-                OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
-                if (vec_ok && col + 3 < p.N) {
-                    store4<OutT>((char *)dst, v);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        if (col + r < p.N)
-                            dst[r] = (OutT)v[r];
-                }
-            }
-        }
-    }
-}
-
 // Largest power-of-two fraction of the wave tile's rows that fits the budget.
 constexpr int pass_rows(int tm, int fit)
 {
@@ -445,15 +408,20 @@ constexpr int pass_rows(int tm, int fit)
     return r;
 }
 
-// Staged epilogue: the wave writes its converted tile, PR rows at a time, into
-// a private LDS region in row-major order (rows padded by 16 bytes so that the
+// Epilogue: the wave writes its converted tile, PR rows at a time, into a
+// private LDS region in row-major order (rows padded by 16 bytes so that the
 // 32 rows one MFMA block spans spread over the banks), then reads it back so
 // that consecutive lanes hold consecutive 16-byte chunks of a row, and stores
-// those: every store instruction writes whole 128-byte lines of C instead of
-// 16 bytes in each of 32 rows.  The caller has made the workgroup's LDS free
-// (no copy in flight, every wave past its last fragment read).
+// those: every store instruction writes runs of whole 128-byte lines of C
+// instead of 16 bytes in each of 32 rows.  A row of C that does not start on
+// a 16-byte boundary (leading dimension or base not a multiple of 16 bytes)
+// takes the same 16-byte stores, misaligned (the memory system serves
+// misaligned vector stores to global memory); its runs then straddle one
+// more line.  The row's last, partial chunk is stored element by element.
+// The caller has made the workgroup's LDS free (no copy in flight, every
+// wave past its last fragment read).
 template <class C, typename OutT, bool BIAS>
-__device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_base, int n_base,
+__device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base, int n_base,
                                              typename C::acc_t (&acc)[C::MT][C::NT])
 {
     constexpr int ES = sizeof(OutT);
@@ -499,7 +467,7 @@ __device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_
             if (row < p.M) {
                 OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
                 if (col + 16 / ES <= p.N) {
-                    *(float4v *)dst = v;
+                    __builtin_memcpy(dst, &v, 16);   // any alignment of the element size
                 } else {
                     const OutT *e = (const OutT *)&v;
 #pragma unroll
@@ -512,15 +480,6 @@ __device__ __forceinline__ void epilogue_lds(const Params &p, char *smem, int m_
     }
 }
 
-template <class C, typename OutT, bool BIAS>
-__device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base, int n_base,
-                                         typename C::acc_t (&acc)[C::MT][C::NT])
-{
-    if (p.line_store)
-        epilogue_lds<C, OutT, BIAS>(p, smem, m_base, n_base, acc);
-    else
-        epilogue_direct<C, OutT, BIAS>(p, m_base, n_base, acc);
-}
 
 // ============================================================================
 // Direct copies: 16-byte global->LDS DMA.  Requires 16-byte aligned A and B,
@@ -955,15 +914,21 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 
 // ============================================================================
 // General path: register-staged copies; any pointer alignment (2-byte) and any
-// leading dimensions.  Whole 16-byte chunks are read with one unaligned vector
-// load (the memory system serves misaligned vector loads of global memory);
-// chunks that cross the K or N edge are read element by element.  Same LDS
+// leading dimensions.  Every 16-byte chunk of a tile is one unaligned vector
+// load (the memory system serves misaligned vector loads of global memory).
+// A chunk that crosses the K or N edge, or lies past it, is still loaded as
+// 16 bytes -- from a place inside the operand's footprint, see src() -- and
+// the elements outside the matrix are cleared when the chunk is written to
+// LDS, after its data has arrived anyway.  So the loads of a K step never
+// wait on each other, and edge tiles pipeline like interior ones.  Same LDS
 // layout and fragment reads as the direct path, two LDS stages.
 // ============================================================================
 // One operand's share of a K step, register-staged.  Chunk t of this thread
 // sits at the same LDS position as the direct copies would put it; offsets
 // are in elements from the tile corner (x0, k0) of a k-major operand or
-// (k0, x0) of an mn-major one, where x runs along M (A) or N (B).
+// (k0, x0) of an mn-major one, where x runs along M (A) or N (B).  The
+// operand's footprint is the element range [0, (rows - 1) ld + cols) of its
+// stored rows; every element of it is readable.
 template <class C, bool KMAJ, int R, int NLOADS>
 struct OperandStage {
     static constexpr int ES = C::ES;
@@ -991,27 +956,101 @@ struct OperandStage {
         return (uint32_t)(row(t) * ld + col(t));
     }
 
-    // Load chunk t: zeros past x = X (rows of a k-major tile, columns of an
-    // mn-major one) and past K.
-    __device__ __forceinline__ static half8 load(const char *ptr, int ld, uint32_t o, int t,
-                                                 int x0, int X, int k0, int K)
+    // Stored rows of the tile inside the matrix, and elements of a tile row
+    // inside it, for the tile at (x0, k0) of an operand with X rows along x.
+    __device__ __forceinline__ static int rows_in(int x0, int X, int k0, int K)
+    {
+        return KMAJ ? X - x0 : K - k0;
+    }
+    __device__ __forceinline__ static int cols_in(int x0, int X, int k0, int K)
+    {
+        return KMAJ ? K - k0 : X - x0;
+    }
+    // Elements of chunk t inside the matrix, from its first: 0 .. CE.
+    __device__ __forceinline__ static int valid(int t, int rin, int cin)
+    {
+        return row(t) < rin ? min(max(cin - col(t), 0), CE) : 0;
+    }
+    // Footprint in elements, or 0 when it cannot serve the 16-byte loads:
+    // fewer than CE elements in all, or rows shorter than a chunk (then a
+    // partial chunk of any row may end past the footprint).
+    __device__ __forceinline__ static int64_t footprint(int X, int K, int ld)
+    {
+        const int rows = KMAJ ? X : K, cols = KMAJ ? K : X;
+        const int64_t f = (int64_t)(rows - 1) * ld + cols;
+        return (ld < CE || f < CE) ? 0 : f;
+    }
+
+    // Element index of the 16 bytes loaded for chunk t (footprint >= CE):
+    //  - a chunk with all CE elements inside the matrix: the chunk itself;
+    //  - a partial chunk of any row but the matrix's last: the chunk itself,
+    //    whose tail past the row end is padding or the next row, inside the
+    //    footprint since rows are at least CE long;
+    //  - the partial chunk of the last row, which would end past the
+    //    footprint: the CE elements ending at the footprint's end, i.e. the
+    //    chunk moved back by CE - n elements (undone at the LDS write);
+    //  - a chunk wholly outside the matrix: element 0 (any readable place;
+    //    its data is replaced by zeros at the LDS write).
+    __device__ __forceinline__ static int64_t src(int t, int64_t corner, uint32_t o, int rin,
+                                                  int cin)
+    {
+        const int n = valid(t, rin, cin);
+        int64_t e = corner + o;
+        if (n < CE && row(t) == rin - 1)
+            e -= CE - n;
+        return n == 0 ? 0 : e;
+    }
+
+    // The chunk's elements as they go to LDS: moved forward again for the
+    // last row's partial chunk, and zeros past the matrix edge.
+    __device__ __forceinline__ static half8 fix(half8 v, int t, int rin, int cin)
+    {
+        const int n = valid(t, rin, cin);
+        if (n < CE) {   // partial or outside: rare, skipped when no lane has one
+            uint32_t w[4];
+            __builtin_memcpy(w, &v, 16);
+            if (n > 0 && row(t) == rin - 1) {
+                // the loaded bytes start (CE - n) elements early: shift the
+                // 16 bytes down by that many (q dwords and b bytes)
+                const int sb = (CE - n) * ES, q = sb >> 2, b = sb & 3;
+                uint32_t x[5];
+#pragma unroll
+                for (int i = 0; i < 5; i++) {
+                    uint32_t y = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        y = (i + j < 4 && q == j) ? w[i + j] : y;
+                    x[i] = y;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    w[i] = __builtin_amdgcn_alignbyte(x[i + 1], x[i], b);
+            }
+            const int keep = n * ES;   // bytes of the chunk inside the matrix
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kb = keep - 4 * i;
+                w[i] = kb >= 4 ? w[i] : (kb <= 0 ? 0u : w[i] & ((1u << (8 * kb)) - 1u));
+            }
+            __builtin_memcpy(&v, w, 16);
+        }
+        return v;
+    }
+
+    // Element-by-element load of chunk t with zeros past the edge: taken by
+    // both operands when either one's footprint cannot serve 16-byte loads
+    // (under CE elements, or rows shorter than a chunk).
+    __device__ __forceinline__ static half8 load_small(const char *ptr, uint32_t o, int t,
+                                                       int64_t corner, int rin, int cin)
     {
         half8 v = {};
-        const int rvalid = KMAJ ? X - x0 : K - k0;   // rows of the tile inside the matrix
-        const int cleft = (KMAJ ? K - k0 : X - x0) - col(t);   // valid elements of the chunk
-        const int64_t corner = KMAJ ? (int64_t)x0 * ld + k0 : (int64_t)k0 * ld + x0;
-        if (row(t) < rvalid && cleft > 0) {
-            const char *src = ptr + (corner + o) * ES;
-            if (cleft >= CE) {
-                __builtin_memcpy(&v, src, 16);   // 16-byte load, any element alignment
-            } else {
-                char *d = (char *)&v;
+        const int n = valid(t, rin, cin);
+        const char *src = ptr + (corner + o) * ES;
+        char *d = (char *)&v;
 #pragma unroll
-                for (int e = 0; e < CE; e++)
-                    if (e < cleft)
-                        __builtin_memcpy(d + e * ES, src + e * ES, ES);
-            }
-        }
+        for (int e = 0; e < CE; e++)
+            if (e < n)
+                __builtin_memcpy(d + e * ES, src + e * ES, ES);
         return v;
     }
 };
@@ -1023,6 +1062,8 @@ struct StagedLoader {
     half8 r[C::LOADS];       // one K step of this thread's chunks: A first, then B
     uint32_t off[C::LOADS];  // element offset of each chunk from the tile corner
                              // (host: in-tile offsets stay below 2^31)
+    bool small;              // an operand's footprint is too small for 16-byte
+                             // loads (uniform)
 
     __device__ __forceinline__ void init(const Params &p)
     {
@@ -1032,45 +1073,91 @@ struct StagedLoader {
 #pragma unroll
         for (int t = 0; t < C::B_LOADS; t++)
             off[C::A_LOADS + t] = BS::off(t, p.ldb);
+        small = AS::footprint(p.M, p.K, p.lda) == 0 || BS::footprint(p.N, p.K, p.ldb) == 0;
     }
 
-    // Load K step kt into registers; zeros past M, N and K (so steps past the
-    // end load zeros).  Whole 16-byte chunks are one unaligned vector load.
+    __device__ __forceinline__ static bool interior(const Params &p, int m0, int n0, int kt)
+    {
+        return m0 + C::BM <= p.M && n0 + C::BN <= p.N && (kt + 1) * C::BK <= p.K;
+    }
+    __device__ __forceinline__ static int64_t a_corner(const Params &p, int m0, int k0)
+    {
+        return C::A_KMAJ ? (int64_t)m0 * p.lda + k0 : (int64_t)k0 * p.lda + m0;
+    }
+    __device__ __forceinline__ static int64_t b_corner(const Params &p, int n0, int k0)
+    {
+        return C::B_KMAJ ? (int64_t)n0 * p.ldb + k0 : (int64_t)k0 * p.ldb + n0;
+    }
+
+    // Load K step kt into registers: one 16-byte load per chunk, issued
+    // back to back; the LDS write clears what lies outside the matrix (so
+    // steps past the end write zeros).  Three exclusive paths: interior
+    // tiles, edge tiles, and (tiny operands only) element-by-element loads
+    // that finish before the path ends, so that no load of that path is
+    // still counted where the paths join and the loads of the other two
+    // paths never wait for one another.
     __device__ __forceinline__ void load(const Params &p, int m0, int n0, int kt)
     {
         const int k0 = kt * C::BK;
-        if (m0 + C::BM <= p.M && n0 + C::BN <= p.N && k0 + C::BK <= p.K) {
-            // interior: every chunk is whole
-            const char *a0 = (const char *)p.A + (C::A_KMAJ ? (int64_t)m0 * p.lda + k0
-                                                            : (int64_t)k0 * p.lda + m0) * C::ES;
-            const char *b0 = (const char *)p.B + (C::B_KMAJ ? (int64_t)n0 * p.ldb + k0
-                                                            : (int64_t)k0 * p.ldb + n0) * C::ES;
+        const char *pa = (const char *)p.A, *pb = (const char *)p.B;
+        const int64_t ca = a_corner(p, m0, k0), cb = b_corner(p, n0, k0);
+        if (interior(p, m0, n0, kt)) {
 #pragma unroll
             for (int t = 0; t < C::LOADS; t++)
-                __builtin_memcpy(&r[t], (t < C::A_LOADS ? a0 : b0) + (int64_t)off[t] * C::ES, 16);
+                __builtin_memcpy(&r[t], t < C::A_LOADS ? pa + (ca + off[t]) * C::ES
+                                                       : pb + (cb + off[t]) * C::ES, 16);
             return;
         }
+        const int ra = AS::rows_in(m0, p.M, k0, p.K), qa = AS::cols_in(m0, p.M, k0, p.K);
+        const int rb = BS::rows_in(n0, p.N, k0, p.K), qb = BS::cols_in(n0, p.N, k0, p.K);
+        if (!small) {
+            int64_t e[C::LOADS];
 #pragma unroll
-        for (int t = 0; t < C::A_LOADS; t++)
-            r[t] = AS::load((const char *)p.A, p.lda, off[t], t, m0, p.M, k0, p.K);
+            for (int t = 0; t < C::A_LOADS; t++)
+                e[t] = AS::src(t, ca, off[t], ra, qa);
 #pragma unroll
-        for (int t = 0; t < C::B_LOADS; t++)
-            r[C::A_LOADS + t] = BS::load((const char *)p.B, p.ldb, off[C::A_LOADS + t], t, n0,
-                                         p.N, k0, p.K);
+            for (int t = 0; t < C::B_LOADS; t++)
+                e[C::A_LOADS + t] = BS::src(t, cb, off[C::A_LOADS + t], rb, qb);
+#pragma unroll
+            for (int t = 0; t < C::LOADS; t++)
+                __builtin_memcpy(&r[t], (t < C::A_LOADS ? pa : pb) + e[t] * C::ES, 16);
+        } else {
+#pragma unroll
+            for (int t = 0; t < C::A_LOADS; t++)
+                r[t] = AS::load_small(pa, off[t], t, ca, ra, qa);
+#pragma unroll
+            for (int t = 0; t < C::B_LOADS; t++)
+                r[C::A_LOADS + t] = BS::load_small(pb, off[C::A_LOADS + t], t, cb, rb, qb);
+            wait_vmcnt<0>();
+        }
     }
 
-    // Registers -> LDS stage S, in the layout the direct copies produce.
+    // Registers of K step kt -> LDS stage S, in the layout the direct copies
+    // produce; chunks of an edge step are first put right (fix()).
     template <int S>
-    __device__ __forceinline__ void store(char *smem) const
+    __device__ __forceinline__ void store(const Params &p, char *smem, int m0, int n0,
+                                          int kt) const
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const bool edge = !interior(p, m0, n0, kt);
+        const int k0 = kt * C::BK;
+        const int ra = AS::rows_in(m0, p.M, k0, p.K), qa = AS::cols_in(m0, p.M, k0, p.K);
+        const int rb = BS::rows_in(n0, p.N, k0, p.K), qb = BS::cols_in(n0, p.N, k0, p.K);
 #pragma unroll
-        for (int t = 0; t < C::A_LOADS; t++)
-            *(half8 *)(smem + S * C::A_BYTES + (wave * C::A_LOADS + t) * 1024 + lane * 16) = r[t];
+        for (int t = 0; t < C::A_LOADS; t++) {
+            half8 v = r[t];
+            if (edge && !small)
+                v = AS::fix(v, t, ra, qa);
+            *(half8 *)(smem + S * C::A_BYTES + (wave * C::A_LOADS + t) * 1024 + lane * 16) = v;
+        }
 #pragma unroll
-        for (int t = 0; t < C::B_LOADS; t++)
+        for (int t = 0; t < C::B_LOADS; t++) {
+            half8 v = r[C::A_LOADS + t];
+            if (edge && !small)
+                v = BS::fix(v, t, rb, qb);
             *(half8 *)(smem + C::STAGES * C::A_BYTES + S * C::B_BYTES +
-                       (wave * C::B_LOADS + t) * 1024 + lane * 16) = r[C::A_LOADS + t];
+                       (wave * C::B_LOADS + t) * 1024 + lane * 16) = v;
+        }
     }
 };
 
@@ -1096,7 +1183,7 @@ __device__ __forceinline__ void staged_kstep(const Params &p, StagedLoader<C> &l
     } else if constexpr (!LAST) {
         constexpr int SN = (S + 1) % 2;
         mfma_range<C, 0, H>(st.fa[P], st.fb[P], st.acc);
-        ld.template store<SN>(smem);                 // K step kt0+S+1 (its stage is free)
+        ld.template store<SN>(p, smem, m0, n0, kt0 + S + 1);   // its stage is free
         lds_barrier();                               // publishes it; stage S is free
         read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
                       st.fa[1 - P], st.fb[1 - P]);
@@ -1146,7 +1233,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
         StagedLoader<C> ld;
         ld.init(p);
         ld.load(p, m0, n0, 0);
-        ld.template store<0>(smem);
+        ld.template store<0>(p, smem, m0, n0, 0);
         if (nk > 1)
             ld.load(p, m0, n0, 1);
         lds_barrier();

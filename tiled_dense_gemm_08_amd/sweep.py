@@ -27,6 +27,10 @@ transpose) and leading dimensions of A and B one element wider than stored
     python -m tiled_dense_gemm_08_amd.sweep --grid --out grid.csv [--unaligned]
     python -m tiled_dense_gemm_08_amd.costmodel grid.csv grid_pad.csv --emit
 
+    # time the dispatcher's own call (tg_gemm_ex), copies of packed operands
+    # included; TG_PACK=always|never|auto sets the pack policy
+    python -m tiled_dense_gemm_08_amd.sweep --dispatch --shape 3001x5003x1031:f32:pad
+
 Timing: `reps` launches are captured into one HIP graph which is replayed, so
 that small problems measure kernel time rather than host launch overhead
 (--timing loop launches from Python instead).
@@ -137,16 +141,19 @@ def time_launch(launch, reps, timing="graph"):
         if st != tg.TG_SUCCESS:
             raise tg.TgError(st, "timed call")
 
+    # the first launch runs outside capture, on the stream the capture uses:
+    # argument errors surface here, and the library's per-stream scratch for
+    # packed operands exists before capture (none is allocated under capture)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        go()   # first launch outside capture: argument errors surface here
+        go()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if timing == "graph":
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+        with torch.cuda.graph(graph, stream=side, capture_error_mode="relaxed"):
             for _ in range(reps):
                 go()
         graph.replay()
@@ -178,6 +185,15 @@ def time_config(cid, sh, bufs, reps, timing="graph"):
     args = _args(sh, bufs)
     return time_launch(lambda s: tg.tg_gemm_with_config(cid, *args, s, op_a=sh.op_a,
                                                         op_b=sh.op_b), reps, timing)
+
+
+def time_dispatch(sh, bufs, reps, timing="graph"):
+    """Average milliseconds per dispatcher call (tg_gemm_ex: the library's own
+    choice, copies of packed operands included) and the plan it reports."""
+    args = _args(sh, bufs)
+    plan = tg.tg_select_plan(*args, op_a=sh.op_a, op_b=sh.op_b)
+    ms = time_launch(lambda s: tg.tg_gemm_ex(sh.op_a, sh.op_b, *args, s), reps, timing)
+    return ms, plan
 
 
 def time_split(cid, splits, sh, bufs, ws, reps, timing="graph"):
@@ -371,6 +387,8 @@ def main():
     ap.add_argument("--splits", help="also time K slicing: slice counts, e.g. 2,4,8")
     ap.add_argument("--split-out", metavar="CSV", help="write the sliced timings to CSV")
     ap.add_argument("--out", metavar="CSV", help="write every timing to CSV")
+    ap.add_argument("--dispatch", action="store_true",
+                    help="time the dispatcher's own call for each --shape (with TG_PACK)")
     a = ap.parse_args()
     ids = (list(range(tg.tg_num_configs())) if a.configs == "all"
            else [int(x) for x in a.configs.split(",")])
@@ -390,6 +408,18 @@ def main():
     if not a.shape:
         ap.error("--shape is required unless --grid or --random is given")
     shapes = [Shape.parse(s) for s in a.shape]
+    if a.dispatch:
+        for sh in shapes:
+            bufs = Buffers(sh)
+            ms, (st, cid, packed, scratch) = time_dispatch(sh, bufs, a.reps, a.timing)
+            flop = 2.0 * sh.M * sh.N * sh.K
+            print(json.dumps({"shape": str(sh), "config": cid,
+                              "name": tg.tg_config_info(cid)["name"] if cid >= 0 else None,
+                              "packed": packed, "scratch_bytes": scratch,
+                              "us": round(ms * 1e3, 2),
+                              "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}), flush=True)
+            del bufs
+        return 0
     if a.splits:
         counts = [int(x) for x in a.splits.split(",")]
         rows = {}

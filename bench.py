@@ -95,6 +95,46 @@ def launch_stats(step, stream, n=20):
             "launches": n}
 
 
+def mfma_ceiling(a_bits, b_bits, stream, iters=20000, workgroups=1024, reps=3):
+    """The matrix cores' sustained fp16 rate (tg_mfma_ceiling) on operand
+    fragments taken from the workload's own A and B values, for both MFMA
+    shapes: the ceiling a GEMM on such data can approach under the board's
+    power limit.  TFLOP/s, median of `reps` launches after one warm-up."""
+    import torch
+
+    import tiled_dense_gemm_08_amd as tg
+    n = tg.TG_CEILING_OPERAND_BYTES // 4     # fp16 values per operand
+    a = np.ascontiguousarray(a_bits).reshape(-1)[:n]
+    b = np.ascontiguousarray(b_bits).reshape(-1)[:n]
+    if a.size < n or b.size < n:
+        return None
+    # thread t, set s: 8 A chunks then 8 B chunks of 8 values
+    buf = np.empty((256, 2, 2, 8, 8), np.uint16)
+    buf[:, :, 0] = a.view(np.uint16).reshape(256, 2, 8, 8)
+    buf[:, :, 1] = b.view(np.uint16).reshape(256, 2, 8, 8)
+    ops = torch.from_numpy(buf.reshape(-1).view(np.int16)).to("cuda:0")
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda:0")
+    flop = workgroups * 4.0 * iters * 2 * 128 * 128 * 32
+    out = {}
+    for mi in (32, 16):
+        times = []
+        for r in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = tg.tg_mfma_ceiling(mi, ops.data_ptr(), sink.data_ptr(), iters, workgroups,
+                                    stream.cuda_stream)
+            e1.record(stream)
+            if st != tg.TG_SUCCESS:
+                raise RuntimeError(tg.tg_status_string(st))
+            e1.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        times.sort()
+        out["tflops_%dx%dx%d" % (mi, mi, 512 // mi)] = round(flop / (times[len(times) // 2] / 1e3) / 1e12, 1)
+    return out
+
+
 def device_info():
     import torch
     p = torch.cuda.get_device_properties(0)
@@ -233,6 +273,15 @@ def main():
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
     single = launch_stats(step, stream)
+    ceiling = None
+    if not is_i8:
+        ceiling = mfma_ceiling(w["A"], w["B"], stream)
+        if ceiling:
+            mi = 16 if "_mi16_" in info["name"] else 32
+            own = ceiling["tflops_%dx%dx%d" % (mi, mi, 512 // mi)]
+            ceiling.update({"operands": "32768 values each of A and B (their first elements)",
+                            "kernel_mfma": "%dx%dx%d" % (mi, mi, 512 // mi),
+                            "frac_of_ceiling": round(achieved / own, 4)})
 
     # ---- CPU oracle baseline on a bounded sample (whole rows of C)
     cpu = None
@@ -286,6 +335,7 @@ def main():
                      "peak": round(peak, 1), "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "mfma_ceiling": ceiling,
     }
     print(json.dumps(line))
     return 0

@@ -355,6 +355,39 @@ tg_status tg_tuning_clear(void);
 /* Number of keys in the cache. */
 int tg_tuning_count(void);
 
+/* ---- diagnostics: the matrix cores' rate on given operand values ----
+ * No passage of the pages defines this call; it is a measurement aid for the
+ * GEMM's roofline.  Under the board's power limit the shader clock drops as
+ * the bits of the MFMA operands toggle, so the dense fp16 rate that any
+ * kernel can sustain depends on the data: all-zero operands reach the nominal
+ * peak, random ones stay well below it.  This call runs the matrix cores
+ * alone on operands taken from `operands`, with no memory traffic in its loop,
+ * and so measures the ceiling a GEMM on such values can approach.
+ *
+ * mfma:       32 (v_mfma_f32_32x32x16_f16, the shape of the GEMM kernels) or
+ *             16 (v_mfma_f32_16x16x32_f16).
+ * operands:   TG_CEILING_OPERAND_BYTES bytes of fp16 values in device memory
+ *             (16-byte aligned), read once per thread: thread t of every
+ *             workgroup takes the 32 16-byte chunks at byte 512 t -- chunks
+ *             16 s + j (j < 8) are its A fragments of set s, chunks
+ *             16 s + 8 + j its B fragments.
+ * sink:       workgroups * 256 floats of device memory; thread t of
+ *             workgroup w writes the sum of its accumulators to
+ *             sink[256 w + t] (so the work is not optimised away).
+ * iters:      k-steps of 32 per wave: even, 2 .. 2^30.  The two operand sets
+ *             alternate from one k-step to the next.
+ * workgroups: 1 .. 2^20 workgroups of 4 waves, one per SIMD.
+ * Work: workgroups * 4 * iters * 2 * 128 * 128 * 32 FLOP (every wave holds a
+ * 128 x 128 fp32 accumulator tile).  Asynchronous on `stream`; time it with
+ * events on that stream.
+ * Errors: TG_ERROR_INVALID_VALUE (bad mfma, iters or workgroups; NULL or
+ * misaligned pointer; a buffer that does not fit inside its allocation),
+ * TG_ERROR_NOT_DEVICE_MEMORY, TG_ERROR_UNSUPPORTED (not gfx950),
+ * TG_ERROR_LAUNCH. */
+#define TG_CEILING_OPERAND_BYTES 131072
+tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t iters,
+                          int64_t workgroups, hipStream_t stream);
+
 /* Library version string (static). */
 const char *tg_version(void);
 

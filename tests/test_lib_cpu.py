@@ -172,3 +172,14 @@ def test_int8_validation_without_gpu():
     for c in tg.configs():
         sup = tg.tg_config_supports(c["id"], PA, PB, None, PC, 512, 512, 512, 512, 512, 512, I32)
         assert sup == (1 if c["elem_bytes"] == 1 else 0)
+
+
+@pytest.mark.parametrize("args", [
+    (8, PA, PC, 2, 1), (0, PA, PC, 2, 1),            # unknown MFMA shape
+    (32, 0, PC, 2, 1), (32, PA, 0, 2, 1),            # NULL buffers
+    (32, PA, PC, 0, 1), (32, PA, PC, 3, 1),          # iters not even and >= 2
+    (16, PA, PC, (1 << 30) + 2, 1),                  # too many iters
+    (16, PA, PC, 2, 0), (16, PA, PC, 2, (1 << 20) + 1),   # workgroups out of range
+])
+def test_mfma_ceiling_rejects_bad_arguments(args):
+    assert tg.tg_mfma_ceiling(*args) == tg.TG_ERROR_INVALID_VALUE

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libtg.so")
 TG_DTYPE_F16 = 1
 TG_DTYPE_F32 = 2
 TG_DTYPE_I32 = 3   # int8 operands, int32 C
+TG_CEILING_OPERAND_BYTES = 131072   # operand buffer of tg_mfma_ceiling
 
 TG_SUCCESS = 0
 TG_ERROR_INVALID_VALUE = 1
@@ -37,7 +38,7 @@ EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "t
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
             "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk",
             "tg_select_plan", "tg_scratch_release", "tg_scratch_held", "tg_set_pack_policy",
-            "tg_attention_fwd", "tg_version")
+            "tg_attention_fwd", "tg_mfma_ceiling", "tg_version")
 
 
 class TgError(RuntimeError):
@@ -113,6 +114,8 @@ def _load():
     L.tg_tuning_clear.restype = I
     L.tg_tuning_count.argtypes = []
     L.tg_tuning_count.restype = I
+    L.tg_mfma_ceiling.argtypes = [I, P, P, I64, I64, P]
+    L.tg_mfma_ceiling.restype = I
     L.tg_version.argtypes = []
     L.tg_version.restype = ctypes.c_char_p
     return L
@@ -233,6 +236,10 @@ def tg_tuning_clear():
 
 def tg_tuning_count():
     return lib.tg_tuning_count()
+
+
+def tg_mfma_ceiling(mfma, operands, sink, iters, workgroups, stream=0):
+    return lib.tg_mfma_ceiling(mfma, operands, sink, iters, workgroups, stream or None)
 
 
 def tg_version():

@@ -25,6 +25,7 @@
 
 #include "tg.h"
 #include "tg_attention.h"
+#include "tg_ceiling.h"
 #include "tg_kernels.h"
 #include "tg_pack.h"
 
@@ -1347,6 +1348,44 @@ tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
                      Problem{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype,
                              bias != nullptr, op_a, op_b},
                      ws, workspace_bytes, nullptr, config_id, splits, false);
+}
+
+tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t iters,
+                          int64_t workgroups, hipStream_t stream)
+{
+    if ((mfma != 16 && mfma != 32) || operands == nullptr || sink == nullptr || iters < 2 ||
+        iters > (int64_t(1) << 30) || (iters & 1) || workgroups < 1 ||
+        workgroups > (int64_t(1) << 20))
+        return TG_ERROR_INVALID_VALUE;
+    int dev = 0;
+    tg_status st;
+    if ((st = check_device(&dev)) != TG_SUCCESS || (st = check_pointer(operands, dev)) != TG_SUCCESS ||
+        (st = check_pointer(sink, dev)) != TG_SUCCESS)
+        return st;
+    // both buffers must lie inside their allocations
+    const struct {
+        const void *p;
+        size_t bytes;
+    } spans[2] = {{operands, (size_t)TG_CEILING_OPERAND_BYTES},
+                  {sink, (size_t)workgroups * 256 * sizeof(float)}};
+    for (const auto &sp : spans) {
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)sp.p) != hipSuccess) {
+            (void)hipGetLastError();
+            return TG_ERROR_NOT_DEVICE_MEMORY;
+        }
+        const uintptr_t lo = (uintptr_t)base, at = (uintptr_t)sp.p;
+        if (at < lo || at - lo > size || size - (at - lo) < sp.bytes)
+            return TG_ERROR_INVALID_VALUE;
+    }
+    if (!aligned(operands, 16) || !aligned(sink, 4))
+        return TG_ERROR_INVALID_VALUE;
+    (void)hipGetLastError();
+    return tg::launch_mfma_ceiling(mfma, operands, sink, (int)iters, (int)workgroups, stream) ==
+                   hipSuccess
+               ? TG_SUCCESS
+               : TG_ERROR_LAUNCH;
 }
 
 const char *tg_version(void) { return "tg 0.4.0 (gfx950)"; }

@@ -156,7 +156,25 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the "
                          "known-size reference for scaling the HBM byte counters), then exit")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only measure the matrix cores' rate (tg_mfma_ceiling) on the "
+                         "workload's A and B values and on zero operands, then exit")
     return ap.parse_args()
+
+
+def ceiling_only(a):
+    """The MFMA ceiling on the workload's own values next to the same loop on
+    all-zero operands, which toggle no bits: the gap is the power limit's
+    response to the data, with no memory traffic involved."""
+    import torch
+    w = gen.workload(a.workload)
+    stream = torch.cuda.current_stream()
+    zeros = np.zeros(1 << 16, np.uint16)
+    print(json.dumps({"workload": a.workload,
+                      "mfma_ceiling_workload_values": mfma_ceiling(w["A"], w["B"], stream),
+                      "mfma_ceiling_zero_operands": mfma_ceiling(zeros, zeros, stream),
+                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s"}))
+    return 0
 
 
 def copy_calibration(mib):
@@ -182,6 +200,11 @@ def main():
         return 2
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
+    if a.ceiling_only:
+        if a.workload in gen.ATTN_WORKLOADS or gen.WORKLOADS[a.workload]["kind"] == "i8":
+            print("--ceiling-only needs an fp16 GEMM workload", file=sys.stderr)
+            return 2
+        return ceiling_only(a)
     if a.workload in gen.ATTN_WORKLOADS:
         return bench_attention(a)
     import torch

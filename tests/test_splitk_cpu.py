@@ -83,6 +83,11 @@ def test_choice_is_a_kernel_that_can_run_it():
             assert info["elem_bytes"] == es and info["ops"] >> (2 * op_a + op_b) & 1
 
 
+# Configurations the library's chooser never slices by itself (the 4-stage
+# 64x64 kernel, whose model row is fitted on unsliced launches only).
+NO_AUTO_SLICING = {21}
+
+
 @pytest.mark.parametrize("fname,mean_limit,worst_limit", [
     ("split_grid.csv.gz", 1.03, 1.25),
     ("split_random_seed3.csv.gz", 1.07, 1.45),
@@ -94,6 +99,8 @@ def test_split_choice_is_close_to_the_measured_best(fname, mean_limit, worst_lim
     t, _ = costmodel.read_split_timings(os.path.join(TIMINGS, fname))
     ratios = []
     for (dt, layout, M, N, K), per in t.items():
+        # the pairs the chooser can pick: it runs NO_AUTO_SLICING kernels unsliced
+        per = {k: v for k, v in per.items() if k[1] == 1 or k[0] not in NO_AUTO_SLICING}
         op_a, op_b = "nt".index(layout[0]), "nt".index(layout[1])
         dtype = {"f16": F16, "f32": F32, "i32": I32}[dt]
         st, cid, sp = select(M, N, K, 1 << 34, dtype, op_a, op_b)

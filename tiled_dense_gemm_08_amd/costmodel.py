@@ -134,7 +134,12 @@ def fit_config(samples, bm, bn, lds_bytes=0):
         rms = math.sqrt(sq / n)
         if best is None or rms < best[4] - 1e-9:
             best = (occ, Ks, full, mn, rms)
-    return best
+    # a longer K never takes less time: where the per-K fits dip (noise at the
+    # smallest K, where launch latency dominates) carry the larger value on
+    occ, Ks, full, mn, rms = best
+    full = [float(v) for v in np.maximum.accumulate(full)]
+    mn = [float(v) for v in np.maximum.accumulate(mn)]
+    return occ, Ks, full, mn, rms
 
 
 def padded(layout):

@@ -886,6 +886,21 @@ double reduce_time(const Problem &p, int64_t slices)
     return kReduceFixedUs + bytes / kReduceBytesPerUs + kSliceUs * (double)slices;
 }
 
+// Configurations that the chooser runs unsliced only, unless the caller names
+// both the configuration and a slice count: the 4-stage 64x64 kernel's model
+// row is fitted on unsliced launches, and on the slicing calibration shapes
+// its sliced predictions chose kernels 1.056x slower than the fastest on
+// average (up to 1.27x), against 1.015x without them.
+constexpr int kNoAutoSlicing[] = {21};
+
+bool auto_slicing_ok(int id)
+{
+    for (int x : kNoAutoSlicing)
+        if (x == id)
+            return false;
+    return true;
+}
+
 struct SplitChoice {
     int id;
     int64_t slices;    // 1: no K slicing
@@ -916,7 +931,7 @@ SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int onl
         };
         if (only_splits <= 1)
             consider(1, p.K);
-        if (only_splits == 1)
+        if (only_splits == 1 || (only_splits == 0 && !auto_slicing_ok(r.id)))
             continue;
         const int one[] = {only_splits};
         const int *cand = only_splits > 1 ? one : kSplitCandidates;

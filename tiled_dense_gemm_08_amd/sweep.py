@@ -230,11 +230,12 @@ def search_splits(sh, config_ids, split_counts, reps, timing):
     nbytes = ws.numel() * ws.element_size()
     st, cid, sl = tg.tg_select_splitk(*a, nbytes, op_a=sh.op_a, op_b=sh.op_b)
     auto = (cid, sl, time_split(-1, 0, sh, bufs, ws, reps, timing))
-    best = min(out, key=out.get)
-    print(json.dumps({"shape": str(sh), "auto": list(auto[:2]), "auto_ms": round(auto[2], 5),
-                      "best": list(best), "best_ms": round(out[best], 5),
-                      "unsliced_best_ms": round(min(v for k, v in out.items() if k[1] == 1), 5)}),
-          flush=True)
+    rec = {"shape": str(sh), "auto": list(auto[:2]), "auto_ms": round(auto[2], 5)}
+    if out:   # none of the named configurations can run this shape: the dispatcher's call only
+        best = min(out, key=out.get)
+        rec.update({"best": list(best), "best_ms": round(out[best], 5),
+                    "unsliced_best_ms": round(min(v for k, v in out.items() if k[1] == 1), 5)})
+    print(json.dumps(rec), flush=True)
     del bufs, ws
     torch.cuda.empty_cache()
     return out, auto

@@ -184,6 +184,11 @@ struct Cfg {
     static constexpr int TM = BM / WM_, TN = BN / WN_;     // wave tile
     static constexpr int MT = TM / MI, NT = TN / MI;       // MFMA blocks per wave
     static constexpr int KS = BK / KI;                     // MFMA k-steps per K step
+    // A fragments single-buffered and refilled row by row (pipe_kstep_roll):
+    // the 16x16x32 MFMA needs twice the fragment registers of 32x32x16 for
+    // the same wave tile, and with two waves per SIMD (8 waves) the double-
+    // buffered set would not fit in a wave's 256 registers.
+    static constexpr bool ROLL = MI_ == 16 && WM_ * WN_ == 8 && SCHED_ == 0;
     static constexpr int A_BYTES = BM * BK * ES;
     static constexpr int B_BYTES = BK * BN * ES;
     static constexpr int KROWB = BK * ES;                  // bytes of a k-major tile row
@@ -275,31 +280,35 @@ __device__ __forceinline__ void fragment_offsets(int wm, int wn, int (&a_off)[C:
         mnmajor_offsets<C, C::BN>(wn * C::TN, b_off);
 }
 
+template <class C, bool KMAJ, int R, int NOFF>
+__device__ __forceinline__ half8 read_block(const char *tile, int ks, const int (&off)[NOFF], int b)
+{
+    if constexpr (KMAJ) {
+        return *(const half8 *)(tile + off[ks] + b * C::MI * C::KROWB);
+    } else if constexpr (C::ES == 2) {
+        const char *q = tile + off[b] + ks * C::KI * R * 2;
+        short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v *)TG_LDS(q));
+        short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * R * 2));
+        return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+        const char *q = tile + off[b] + ks * C::KI * R;
+        int2v lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2v *)TG_LDS(q));
+        int2v hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2v *)TG_LDS(q + 8 * R));
+        return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+    }
+}
+
 template <class C, bool KMAJ, int R, int NOFF, int NBLK>
 __device__ __forceinline__ void read_operand(const char *tile, int ks, const int (&off)[NOFF],
                                              half8 (&frag)[NBLK])
 {
 #pragma unroll
-    for (int b = 0; b < NBLK; b++) {
-        if constexpr (KMAJ) {
-            frag[b] = *(const half8 *)(tile + off[ks] + b * C::MI * C::KROWB);
-        } else if constexpr (C::ES == 2) {
-            const char *q = tile + off[b] + ks * C::KI * R * 2;
-            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4v *)TG_LDS(q));
-            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4v *)TG_LDS(q + 4 * R * 2));
-            frag[b] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
-                                                                        6, 7));
-        } else {
-            const char *q = tile + off[b] + ks * C::KI * R;
-            int2v lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) int2v *)TG_LDS(q));
-            int2v hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) int2v *)TG_LDS(q + 8 * R));
-            frag[b] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
-        }
-    }
+    for (int b = 0; b < NBLK; b++)
+        frag[b] = read_block<C, KMAJ, R>(tile, ks, off, b);
 }
 
 // B fragments first (transpose reads in the normal orientation), then A.
@@ -745,6 +754,83 @@ __device__ __forceinline__ void mfma_window(const Params &p, DirectLoader<C> &ld
     }
 }
 
+// LDS read instructions of one fragment block: 1 (k-major, ds_read_b128) or
+// 2 (mn-major, two transpose reads).
+template <class C, bool KMAJ>
+constexpr int reads_per_block()
+{
+    return KMAJ ? 1 : 2;
+}
+
+// MFMAs of block row mt (all NT columns) of the current k-step.
+template <class C, int MT_>
+__device__ __forceinline__ void mfma_row(const half8 &fa, const half8 (&fb)[C::NT],
+                                         typename C::acc_t (&acc)[C::MT][C::NT])
+{
+#pragma unroll
+    for (int nt = 0; nt < C::NT; nt++)
+        acc[MT_][nt] = mfma<C>(fb[nt], fa, acc[MT_][nt]);
+}
+
+// Rows [LO, HI) of the k-step: each row's MFMAs, then (REFILL) the A block
+// of that row for k-step ks_next of tile `as`, read into the register the
+// row has just finished with, and XB of the next k-step's B reads.
+template <class C, int LO, int HI, bool REFILL, int XB>
+__device__ __forceinline__ void roll_rows(PipeState<C> &st, int P, const char *as, int ks_next)
+{
+    if constexpr (LO < HI) {
+        mfma_row<C, LO>(st.fa[0][LO], st.fb[P], st.acc);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);
+        if constexpr (REFILL) {
+            st.fa[0][LO] = read_block<C, C::A_KMAJ, C::BM>(as, ks_next, st.a_off, LO);
+            __builtin_amdgcn_sched_group_barrier(0x100, reads_per_block<C, C::A_KMAJ>() + XB, 0);
+        } else if constexpr (XB > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, XB, 0);
+        }
+        roll_rows<C, LO + 1, HI, REFILL, XB>(st, P, as, ks_next);
+    }
+}
+
+// The k-step with rolling A fragments (C::ROLL).  B fragments stay double-
+// buffered by k-step parity P (all of them are needed until the last row);
+// A block row mt is re-read for the next k-step as soon as row mt's MFMAs
+// are issued.  In the k-step that ends a stage, rows before the barrier
+// cannot refill (the next stage is not published yet): their blocks are read
+// right after it, with the next B fragments and the copies of the freed stage.
+template <class C, int U, bool FINAL>
+__device__ __forceinline__ void pipe_kstep_roll(const Params &p, DirectLoader<C> &ld,
+                                                const char *smem, int kt0, int nk, int m0, int n0,
+                                                PipeState<C> &st)
+{
+    constexpr int S = U / C::KS, ks = U % C::KS, P = U % 2;
+    constexpr int HM = C::MT / 2;
+    constexpr int BRD = C::NT * reads_per_block<C, C::B_KMAJ>();   // B read instructions
+    constexpr bool BARRIER = ks + 1 == C::KS && (!FINAL || S + 1 < C::STAGES);
+    static_assert(C::MT % 2 == 0 && BRD % HM == 0, "rolling rows");
+    if constexpr (ks + 1 < C::KS) {
+        // next k-step of the same stage: its B fragments spread over the
+        // first half of the rows, each A block after its own row
+        read_operand<C, C::B_KMAJ, C::BN>(b_stage<C, S>(smem), ks + 1, st.b_off, st.fb[1 - P]);
+        roll_rows<C, 0, HM, true, BRD / HM>(st, P, a_stage<C, S>(smem), ks + 1);
+        roll_rows<C, HM, C::MT, true, 0>(st, P, a_stage<C, S>(smem), ks + 1);
+    } else if constexpr (BARRIER) {
+        constexpr int SN = (S + 1) % C::STAGES;
+        roll_rows<C, 0, HM, false, 0>(st, P, nullptr, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
+        lds_barrier();                               // everyone's did; stage S is free
+        read_operand<C, C::B_KMAJ, C::BN>(b_stage<C, SN>(smem), 0, st.b_off, st.fb[1 - P]);
+#pragma unroll
+        for (int mt = 0; mt < HM; mt++)
+            st.fa[0][mt] = read_block<C, C::A_KMAJ, C::BM>(a_stage<C, SN>(smem), 0, st.a_off, mt);
+        ld.template issue<S>(p, kt0 + S + C::STAGES, nk, m0, n0);
+        __builtin_amdgcn_sched_barrier(0);
+        roll_rows<C, HM, C::MT, true, 0>(st, P, a_stage<C, SN>(smem), 0);
+    } else {
+        roll_rows<C, 0, C::MT, false, 0>(st, P, nullptr, 0);
+    }
+}
+
 // k-step U (0 .. STAGES*KS-1) of a loop body; FINAL: the body that ends the
 // K loop (no barrier, reads or copies after its last k-step).
 template <class C, int U, bool FINAL>
@@ -757,7 +843,9 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
     constexpr int H = NMF / 2;
     constexpr int R = H / NRD > 0 ? H / NRD : 1;
     constexpr bool BARRIER = ks + 1 == C::KS && (!FINAL || S + 1 < C::STAGES);
-    if constexpr (C::SCHED == 1) {
+    if constexpr (C::ROLL) {
+        pipe_kstep_roll<C, U, FINAL>(p, ld, smem, kt0, nk, m0, n0, st);
+    } else if constexpr (C::SCHED == 1) {
         // position of this k-step's first MFMA in window S-1
         constexpr int OFF = H + ks * NMF;
         if constexpr (!BARRIER) {

@@ -41,8 +41,8 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # each scaled by what the same counter reads for a plain 1 GiB device copy
 # (--copy-calibration 1024: FETCH_SIZE reads 0.5 GiB, WRITE_SIZE 1 GiB, so the
 # factors are 2.0 and 1.0).  Keyed by workload, kernel configuration and a
-# digest of the kernel sources: a kernel changed since the counters were
-# taken reports null.
+# digest of the kernel sources and the configuration's row: a kernel changed
+# since the counters were taken reports null.
 TRAFFIC_BYTES = {
     # FETCH_SIZE 790906 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
     ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c0", "036ed570bce32d97"): 1753993631,
@@ -67,13 +67,20 @@ def attention_source_digest():
     return h.hexdigest()[:16]
 
 
-def kernel_source_digest():
+def kernel_source_digest(config_id):
+    """Digest of what one compiled configuration is built from: the kernel
+    sources and that configuration's row of the table (other rows may come
+    and go without changing it)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_dense_gemm_08_amd", "csrc")
-    for name in ("tg_kernels.hip", "tg_kernels.h", "tg_config_list.inc"):
+    for name in ("tg_kernels.hip", "tg_kernels.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "tg_config_list.inc")) as f:
+        rows = [l.strip() for l in f if l.startswith("TG_CONFIG_ROW(%d," % config_id)]
+    assert len(rows) == 1, "configuration %d: %d rows" % (config_id, len(rows))
+    h.update(rows[0].encode())
     return h.hexdigest()[:16]
 
 
@@ -329,7 +336,7 @@ def main():
                "sample": "first %d of %d rows of C (%dx%dx%d %s dot products), %.1f s"
                          % (rows, M, rows, N, K, "int64" if is_i8 else "fp64", dt)}
 
-    traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest()))
+    traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest(cid)))
     peak = PEAK_TOPS_INT8 if is_i8 else PEAK_TFLOPS
     unit = "TOPS" if is_i8 else "TFLOP/s"
     line = {

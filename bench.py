@@ -44,8 +44,8 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # digest of the kernel sources and the configuration's row: a kernel changed
 # since the counters were taken reports null.
 TRAFFIC_BYTES = {
-    # FETCH_SIZE 790906 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
-    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c0", "036ed570bce32d97"): 1753993631,
+    # FETCH_SIZE 792936 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c0", "2e13aea2d5ceab3e"): 1758151229,
 }
 
 

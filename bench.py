@@ -448,6 +448,13 @@ def bench_attention(a):
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
     single = launch_stats(step, stream)
+    # the matrix cores' rate on operands from Q and K (the score product's
+    # inputs; both products run on 32x32x16)
+    ceiling = mfma_ceiling(w["Q"], w["K"], stream)
+    if ceiling:
+        ceiling.update({"operands": "32768 values each of Q and K (their first elements)",
+                        "kernel_mfma": "32x32x16",
+                        "frac_of_ceiling": round(achieved / ceiling["tflops_32x32x16"], 4)})
 
     # ---- CPU oracle baseline: whole query rows, sampled
     cpu = None
@@ -493,6 +500,7 @@ def bench_attention(a):
                      "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": ATTN_TRAFFIC_BYTES.get((a.workload, attention_source_digest()))},
         "cpu_baseline": cpu,
+        "mfma_ceiling": ceiling,
     }
     print(json.dumps(line))
     return 0

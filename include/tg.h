@@ -376,11 +376,13 @@ int tg_tuning_count(void);
  *             sink[256 w + t] (so the work is not optimised away).
  * iters:      k-steps of 32 per wave: even, 2 .. 2^30.  The two operand sets
  *             alternate from one k-step to the next.
- * workgroups: 1 .. 2^20 workgroups of 4 waves, one per SIMD.
+ * workgroups: 1 .. 2^20 workgroups of 4 waves, one per SIMD; iters *
+ *             workgroups at most 2^32 (about ten seconds of work).
  * Work: workgroups * 4 * iters * 2 * 128 * 128 * 32 FLOP (every wave holds a
  * 128 x 128 fp32 accumulator tile).  Asynchronous on `stream`; time it with
  * events on that stream.
- * Errors: TG_ERROR_INVALID_VALUE (bad mfma, iters or workgroups; NULL or
+ * Errors: TG_ERROR_INVALID_VALUE (bad mfma, iters or workgroups, or too much
+ * work; NULL or
  * misaligned pointer; a buffer that does not fit inside its allocation),
  * TG_ERROR_NOT_DEVICE_MEMORY, TG_ERROR_UNSUPPORTED (not gfx950),
  * TG_ERROR_LAUNCH. */

@@ -180,6 +180,7 @@ def test_int8_validation_without_gpu():
     (32, PA, PC, 0, 1), (32, PA, PC, 3, 1),          # iters not even and >= 2
     (16, PA, PC, (1 << 30) + 2, 1),                  # too many iters
     (16, PA, PC, 2, 0), (16, PA, PC, 2, (1 << 20) + 1),   # workgroups out of range
+    (32, PA, PC, 1 << 13, (1 << 19) + 1),            # more than 2^32 k-steps in all
 ])
 def test_mfma_ceiling_rejects_bad_arguments(args):
     assert tg.tg_mfma_ceiling(*args) == tg.TG_ERROR_INVALID_VALUE

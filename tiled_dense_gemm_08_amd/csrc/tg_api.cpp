@@ -1368,9 +1368,11 @@ tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
 tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t iters,
                           int64_t workgroups, hipStream_t stream)
 {
+    // iters * workgroups is capped at 2^32 (about ten seconds of matrix-core
+    // work) so that one call cannot hold the device for minutes
     if ((mfma != 16 && mfma != 32) || operands == nullptr || sink == nullptr || iters < 2 ||
         iters > (int64_t(1) << 30) || (iters & 1) || workgroups < 1 ||
-        workgroups > (int64_t(1) << 20))
+        workgroups > (int64_t(1) << 20) || iters * workgroups > (int64_t(1) << 32))
         return TG_ERROR_INVALID_VALUE;
     int dev = 0;
     tg_status st;

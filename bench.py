@@ -163,6 +163,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the "
                          "known-size reference for scaling the HBM byte counters), then exit")
+    ap.add_argument("--vendor-context", action="store_true",
+                    help="only time this library's call against torch.matmul (the ROCm "
+                         "vendor BLAS) on the workload's data, in alternating rounds, then "
+                         "exit: context, not a target")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the matrix cores' rate (tg_mfma_ceiling) on the "
                          "workload's A and B values and on zero operands, then exit")
@@ -181,6 +185,56 @@ def ceiling_only(a):
                       "mfma_ceiling_workload_values": mfma_ceiling(w["A"], w["B"], stream),
                       "mfma_ceiling_zero_operands": mfma_ceiling(zeros, zeros, stream),
                       "peak": PEAK_TFLOPS, "unit": "TFLOP/s"}))
+    return 0
+
+
+def vendor_context(a, rounds=8, reps=30):
+    """This library's dispatcher call and torch.matmul on the same device
+    buffers (the workload's A and B, fp16 C), timed in
+    alternating rounds of `reps` launches with HIP events on one stream."""
+    import statistics
+
+    import torch
+
+    import tiled_dense_gemm_08_amd as tg
+    w = gen.workload(a.workload)
+    if w["op_a"] or w["op_b"] or w["bias"] is not None or w["c_dtype"] != "f16":
+        print("--vendor-context needs a plain A.B workload with fp16 C", file=sys.stderr)
+        return 2
+    M, N, K = w["M"], w["N"], w["K"]
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
+    B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
+    C = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def ours():
+        st = tg.tg_gemm(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, K, N, N,
+                        tg.TG_DTYPE_F16, stream.cuda_stream)
+        if st != tg.TG_SUCCESS:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    def vendor():
+        torch.matmul(A, B, out=C)
+
+    impls = {"tg": ours, "torch.matmul": vendor}
+    res = {k: [] for k in impls}
+    for r in range(rounds):
+        for k in (list(impls) if r % 2 == 0 else list(impls)[::-1]):
+            for _ in range(5):
+                impls[k]()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                impls[k]()
+            e1.record(stream)
+            e1.synchronize()
+            res[k].append(2.0 * M * N * K / (e0.elapsed_time(e1) / reps / 1e3) / 1e12)
+    print(json.dumps({"workload": a.workload, "unit": "TFLOP/s", "rounds": rounds, "reps": reps,
+                      "context_only": True,
+                      "median": {k: round(statistics.median(v), 1) for k, v in res.items()},
+                      "per_round": {k: [round(x, 1) for x in v] for k, v in res.items()}}))
     return 0
 
 
@@ -207,6 +261,11 @@ def main():
         return 2
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
+    if a.vendor_context:
+        if a.workload in gen.ATTN_WORKLOADS:
+            print("--vendor-context needs a GEMM workload", file=sys.stderr)
+            return 2
+        return vendor_context(a)
     if a.ceiling_only:
         if a.workload in gen.ATTN_WORKLOADS or gen.WORKLOADS[a.workload]["kind"] == "i8":
             print("--ceiling-only needs an fp16 GEMM workload", file=sys.stderr)

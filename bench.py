@@ -149,6 +149,53 @@ def device_info():
             "cus": p.multi_processor_count}
 
 
+def board_sample(step, stream, max_s=15.0):
+    """Socket power and shader clocks (amd-smi) while `step` runs back to back:
+    1.5 s of launches first, then launches until the amd-smi sample has been
+    taken.  None when amd-smi is missing or fails.  Outside the timed
+    region."""
+    import re
+    import shutil
+    import subprocess
+    if shutil.which("amd-smi") is None:
+        return None
+    # the readings average over a window of about a second: load the device
+    # for 1.5 s before the sample starts
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < 1.5:
+        step()
+        n += 1
+        if n % 8 == 0:
+            stream.synchronize()
+    try:
+        pr = subprocess.Popen(["amd-smi", "metric", "-g", "0", "-p", "-c"],
+                              stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    n = 0
+    while pr.poll() is None and time.perf_counter() - t0 < max_s:
+        step()
+        n += 1
+        if n % 8 == 0:
+            stream.synchronize()  # keep the queue short, the device busy
+    if pr.poll() is None:
+        pr.kill()
+        pr.wait()
+        return None
+    out = pr.stdout.read()
+    stream.synchronize()
+    pw = re.search(r"SOCKET_POWER:\s*(\d+)", out)
+    clk = [int(x) for x in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", out)]
+    if pw is None and not clk:
+        return None
+    return {"socket_power_w": int(pw.group(1)) if pw else None,
+            "gfx_clock_mhz_mean": round(sum(clk) / len(clk)) if clk else None,
+            "gfx_clock_mhz_range": [min(clk), max(clk)] if clk else None,
+            "launches_during_sample": n, "source": "amd-smi metric -p -c, one sample"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +409,7 @@ def main():
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
     single = launch_stats(step, stream)
+    board = board_sample(step, stream)
     ceiling = None
     if not is_i8:
         ceiling = mfma_ceiling(w["A"], w["B"], stream)
@@ -425,6 +473,7 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
+        "board_under_load": board,
     }
     print(json.dumps(line))
     return 0

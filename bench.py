@@ -556,6 +556,7 @@ def bench_attention(a):
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
     single = launch_stats(step, stream)
+    board = board_sample(step, stream)
     # the matrix cores' rate on operands from Q and K (the score product's
     # inputs; both products run on 32x32x16)
     ceiling = mfma_ceiling(w["Q"], w["K"], stream)
@@ -609,6 +610,7 @@ def bench_attention(a):
                      "traffic": ATTN_TRAFFIC_BYTES.get((a.workload, attention_source_digest()))},
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
+        "board_under_load": board,
     }
     print(json.dumps(line))
     return 0

@@ -442,6 +442,14 @@ def main():
                "cores": threads, "kind": "oracle",
                "sample": "first %d of %d rows of C (%dx%dx%d %s dot products), %.1f s"
                          % (rows, M, rows, N, K, "int64" if is_i8 else "fp64", dt)}
+        if rows == M and M * N * K <= 1 << 30 and not is_i8:
+            # the whole product fits the sample: also one core's rate
+            t = time.perf_counter()
+            oracle.gemm_ref(w["A"], w["B"], M, N, K, lda=lda, ldb=ldb, bias=w["bias"],
+                            nthreads=1, op_a=op_a, op_b=op_b)
+            dt1 = time.perf_counter() - t
+            cpu["single_core"] = {"value": round(2.0 * M * N * K / dt1 / 1e12, 6),
+                                  "seconds": round(dt1, 3)}
 
     traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest(cid)))
     peak = PEAK_TOPS_INT8 if is_i8 else PEAK_TFLOPS

@@ -712,9 +712,16 @@ bool plan_pack(const Problem &p, PackPlan *out)
     if (!operands_aligned(chk))
         return false;
     double t_direct = 0.0;
-    const int id = model_lookup(chk, &t_direct, true);
+    int id = model_lookup(chk, &t_direct, true);
     if (id < 0)
         return false;
+    // a measured exact-shape record for the copies' problem overrides the
+    // model's kernel (the predicted time still decides whether to pack)
+    if (elem_size(p) == 2) {
+        const int exact = dispatch_exact(chk.M, chk.N, chk.K, chk.fused);
+        if (exact >= 0 && kConfigs[exact].direct && supports(kConfigs[exact], chk))
+            id = exact;
+    }
     pl.id = id;
     pl.kp = kp;
     pl.t = t_direct + kPackFixedUs + bytes / kPackBytesPerUs;

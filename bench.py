@@ -52,8 +52,8 @@ TRAFFIC_BYTES = {
 # The same for the fused attention kernel, keyed by workload and a digest of
 # its sources.
 ATTN_TRAFFIC_BYTES = {
-    # FETCH_SIZE 49250 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
-    ("attn_b2h16l4096d128", "8b5565eeac876f68"): 134942720,
+    # FETCH_SIZE 49244 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
+    ("attn_b2h16l4096d128", "ca1c153ab08ea7a4"): 134930432,
 }
 
 
@@ -214,6 +214,9 @@ def parse():
                     help="only time this library's call against torch.matmul (the ROCm "
                          "vendor BLAS) on the workload's data, in alternating rounds, then "
                          "exit: context, not a target")
+    ap.add_argument("--no-board", action="store_true",
+                    help="skip the amd-smi power and clock sample (its extra launches "
+                         "crowd profiler traces)")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the matrix cores' rate (tg_mfma_ceiling) on the "
                          "workload's A and B values and on zero operands, then exit")
@@ -409,7 +412,7 @@ def main():
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
     single = launch_stats(step, stream)
-    board = board_sample(step, stream)
+    board = None if a.no_board else board_sample(step, stream)
     ceiling = None
     if not is_i8:
         ceiling = mfma_ceiling(w["A"], w["B"], stream)
@@ -564,7 +567,7 @@ def bench_attention(a):
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
     single = launch_stats(step, stream)
-    board = board_sample(step, stream)
+    board = None if a.no_board else board_sample(step, stream)
     # the matrix cores' rate on operands from Q and K (the score product's
     # inputs; both products run on 32x32x16)
     ceiling = mfma_ceiling(w["Q"], w["K"], stream)

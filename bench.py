@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the tiled fp16 GEMM on one MI355X, as one JSON line.
 
-A step is one launch of the whole hot path -- tg_gemm (or tg_gemm_bias_relu
-for the fused workload) over one batch of seeded synthetic fp16 input already
-resident in HBM.  The default workload is the 8192^3 GEMM (fp16 A and B with
-N(0,1)/sqrt(K) values from seed 2, fp32 accumulation, fp16 C).
+A step is one call of the whole hot path -- the dispatcher's call with the
+workspace its fastest plan uses (tg_gemm_ws: on the workloads' aligned
+operands the same single kernel launch as tg_gemm / tg_gemm_bias_relu; on the
+ragged workload the operand copies plus the kernel) over one batch of seeded
+synthetic fp16 input already resident in HBM.  The default workload is the
+8192^3 GEMM (fp16 A and B with N(0,1)/sqrt(K) values from seed 2, fp32
+accumulation, fp16 C); its line also carries the fused 4096 x 11008 x 4096
+GEMM + bias + ReLU as a record of its own ("fused").
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--config ID]
 
-Reported: whole-job TFLOP/s (2MNK per step), the dominant kernel's MFMA
-roofline fraction measured with HIP events on the launch stream, the median
-and minimum of single launches (timed separately, after the K steps), and
-the CPU oracle timed on a bounded sample of the same workload on the host
-cores.
-Before timing, the output is checked against the oracle on sampled entries;
-a failing check prints no throughput.
+Reported per workload: whole-job TFLOP/s (2MNK per step) over exactly K timed
+steps, the dominant kernel's MFMA roofline fraction measured with HIP events
+on the launch stream, 5 further loops of at least 100 ms each (per-launch
+median and minimum), the matrix cores' own rate on the workload's values,
+and the CPU oracle timed on the whole product on the host cores.  The GPU's
+output of the first call is compared with that oracle output entry by entry
+(the parity gate); a failing gate prints no throughput.
 """
 import argparse
 import json
@@ -82,24 +86,6 @@ def kernel_source_digest(config_id):
     assert len(rows) == 1, "configuration %d: %d rows" % (config_id, len(rows))
     h.update(rows[0].encode())
     return h.hexdigest()[:16]
-
-
-def launch_stats(step, stream, n=20):
-    """Median and minimum time of single launches, each between its own pair
-    of events on the launch stream (a separate loop after the timed steps)."""
-    import torch
-    times = []
-    for _ in range(n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        e1.synchronize()
-        times.append(e0.elapsed_time(e1))
-    times.sort()
-    return {"median_ms": round(times[len(times) // 2], 5), "min_ms": round(times[0], 5),
-            "launches": n}
 
 
 def mfma_ceiling(a_bits, b_bits, stream, iters=20000, workgroups=1024, reps=3):
@@ -204,16 +190,15 @@ def parse():
     ap.add_argument("--workload", default="sq8192",
                     choices=sorted(gen.WORKLOADS) + sorted(gen.ATTN_WORKLOADS))
     ap.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle on the whole product; the parity gate then "
+                         "checks --samples sampled entries")
     ap.add_argument("--samples", type=int, default=2048, help="parity-gate sample size")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="sq8192 only: leave out the fused 4096x11008x4096 record")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the "
                          "known-size reference for scaling the HBM byte counters), then exit")
-    ap.add_argument("--vendor-context", action="store_true",
-                    help="only time this library's call against torch.matmul (the ROCm "
-                         "vendor BLAS) on the workload's data, in alternating rounds, then "
-                         "exit: context, not a target")
     ap.add_argument("--no-board", action="store_true",
                     help="skip the amd-smi power and clock sample (its extra launches "
                          "crowd profiler traces)")
@@ -235,56 +220,6 @@ def ceiling_only(a):
                       "mfma_ceiling_workload_values": mfma_ceiling(w["A"], w["B"], stream),
                       "mfma_ceiling_zero_operands": mfma_ceiling(zeros, zeros, stream),
                       "peak": PEAK_TFLOPS, "unit": "TFLOP/s"}))
-    return 0
-
-
-def vendor_context(a, rounds=8, reps=30):
-    """This library's dispatcher call and torch.matmul on the same device
-    buffers (the workload's A and B, fp16 C), timed in
-    alternating rounds of `reps` launches with HIP events on one stream."""
-    import statistics
-
-    import torch
-
-    import tiled_dense_gemm_08_amd as tg
-    w = gen.workload(a.workload)
-    if w["op_a"] or w["op_b"] or w["bias"] is not None or w["c_dtype"] != "f16":
-        print("--vendor-context needs a plain A.B workload with fp16 C", file=sys.stderr)
-        return 2
-    M, N, K = w["M"], w["N"], w["K"]
-    dev = torch.device("cuda:0")
-    A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
-    B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
-    C = torch.empty((M, N), dtype=torch.float16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def ours():
-        st = tg.tg_gemm(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, K, N, N,
-                        tg.TG_DTYPE_F16, stream.cuda_stream)
-        if st != tg.TG_SUCCESS:
-            raise RuntimeError(tg.tg_status_string(st))
-
-    def vendor():
-        torch.matmul(A, B, out=C)
-
-    impls = {"tg": ours, "torch.matmul": vendor}
-    res = {k: [] for k in impls}
-    for r in range(rounds):
-        for k in (list(impls) if r % 2 == 0 else list(impls)[::-1]):
-            for _ in range(5):
-                impls[k]()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                impls[k]()
-            e1.record(stream)
-            e1.synchronize()
-            res[k].append(2.0 * M * N * K / (e0.elapsed_time(e1) / reps / 1e3) / 1e12)
-    print(json.dumps({"workload": a.workload, "unit": "TFLOP/s", "rounds": rounds, "reps": reps,
-                      "context_only": True,
-                      "median": {k: round(statistics.median(v), 1) for k, v in res.items()},
-                      "per_round": {k: [round(x, 1) for x in v] for k, v in res.items()}}))
     return 0
 
 
@@ -311,11 +246,6 @@ def main():
         return 2
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
-    if a.vendor_context:
-        if a.workload in gen.ATTN_WORKLOADS:
-            print("--vendor-context needs a GEMM workload", file=sys.stderr)
-            return 2
-        return vendor_context(a)
     if a.ceiling_only:
         if a.workload in gen.ATTN_WORKLOADS or gen.WORKLOADS[a.workload]["kind"] == "i8":
             print("--ceiling-only needs an fp16 GEMM workload", file=sys.stderr)
@@ -323,23 +253,66 @@ def main():
         return ceiling_only(a)
     if a.workload in gen.ATTN_WORKLOADS:
         return bench_attention(a)
+    line = gemm_record(a, a.workload, a.steps, a.warmup)
+    if line is None:
+        return 1
+    if a.workload == "sq8192" and a.config is None and not a.no_fused:
+        # the metric names the fused bias + ReLU workload too: its own record,
+        # timed the same way, in the same line
+        fused = gemm_record(a, "fused4096x11008x4096", a.steps, a.warmup)
+        if fused is None:
+            return 1
+        line["fused"] = {k: fused[k] for k in ("value", "unit", "ms_per_step", "config",
+                                               "loops", "roofline", "cpu_baseline",
+                                               "mfma_ceiling", "board_under_load")}
+    print(json.dumps(line))
+    return 0
+
+
+def timed_loops(step, stream, launches, n=5):
+    """n loops of `launches` back-to-back launches, each loop between its own
+    pair of events on the launch stream: per-launch milliseconds of every
+    loop, their median and minimum."""
+    import torch
+    per = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            step()
+        e1.record(stream)
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) / launches)
+    srt = sorted(per)
+    return {"loops": n, "launches_per_loop": launches,
+            "per_launch_ms": [round(x, 5) for x in per],
+            "median_ms": round(srt[n // 2], 5), "min_ms": round(srt[0], 5)}
+
+
+def gemm_record(a, name, steps, warmup):
+    """One GEMM workload: the parity gate, exactly `steps` timed launches
+    after `warmup`, 5 loops of at least 100 ms, the MFMA ceiling on the
+    workload's values, the board's power and clock, and the CPU oracle on the
+    whole product (also the gate's reference).  Returns the JSON record, or
+    None (after printing an error line) when the gate fails."""
     import torch
 
     import oracle
     import tiled_dense_gemm_08_amd as tg
-
-    w = gen.workload(a.workload)
+    w = gen.workload(name)
     M, N, K = w["M"], w["N"], w["K"]
     fused = w["bias"] is not None
     c_dtype = w["c_dtype"]
-    dev = torch.device("cuda:0")
-    A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
-    B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
-    bias = torch.from_numpy(w["bias"]).to(dev) if fused else None
     is_i8 = c_dtype == "i32"
+    dev = torch.device("cuda:0")
     if is_i8:
         A = torch.from_numpy(w["A"]).to(dev)
         B = torch.from_numpy(w["B"]).to(dev)
+    else:
+        A = torch.from_numpy(w["A"].view(np.float16)).to(dev)
+        B = torch.from_numpy(w["B"].view(np.float16)).to(dev)
+    bias = torch.from_numpy(w["bias"]).to(dev) if fused else None
     tdt = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[c_dtype]
     C = torch.empty((M, N), dtype=tdt, device=dev)
     code = {"f16": tg.TG_DTYPE_F16, "f32": tg.TG_DTYPE_F32, "i32": tg.TG_DTYPE_I32}[c_dtype]
@@ -348,70 +321,55 @@ def main():
     pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
     pbias = bias.data_ptr() if fused else None
     op_a, op_b, lda, ldb = w["op_a"], w["op_b"], w["lda"], w["ldb"]
-    # the dispatcher's call (tg_gemm_ex), copies of packed operands included,
-    # unless a configuration is named
-    cid, packed = a.config, 0
-    if cid is None:
-        st, cid, packed, _ = tg.tg_select_plan(pa, pb, pbias, pc, M, N, K, lda, ldb, N, code,
-                                               op_a=op_a, op_b=op_b)
-        assert st == tg.TG_SUCCESS
-    info = tg.tg_config_info(cid)
+    # the dispatcher's call with the workspace its fastest plan uses (packed
+    # operands, K slices), unless a configuration is named
     forced = a.config is not None
+    slices, packed, used = 1, 0, 0
+    if forced:
+        cid = a.config
+    else:
+        st, cid, slices, packed, used = tg.tg_select_plan(pa, pb, pbias, pc, M, N, K, lda, ldb,
+                                                          N, code, op_a=op_a, op_b=op_b)
+        assert st == tg.TG_SUCCESS
+    ws = torch.empty(max(used, 16), dtype=torch.uint8, device=dev)
+    info = tg.tg_config_info(cid)
 
     def step():
         if forced:
             st = tg.tg_gemm_with_config(cid, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s,
                                         op_a=op_a, op_b=op_b)
         else:
-            st = tg.tg_gemm_ex(op_a, op_b, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code, s)
+            st = tg.tg_gemm_ws(-1, 0, pa, pb, pbias, pc, M, N, K, lda, ldb, N, code,
+                               ws.data_ptr(), used, s, op_a=op_a, op_b=op_b)
         if st != tg.TG_SUCCESS:
             raise RuntimeError(tg.tg_status_string(st))
 
-    # ---- parity gate on sampled outputs
+    # ---- one launch on a poisoned C, kept for the parity gate
     C.fill_(2 ** 31 - 1 if is_i8 else float("nan"))
     step()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(123)
-    r = rng.integers(0, M, a.samples)
-    c = rng.integers(0, N, a.samples)
     out = C.cpu().numpy()
-    if is_i8:
-        cref = oracle.gemm_i8_entries(w["A"], w["B"], r, c, K, lda, ldb, op_a=op_a, op_b=op_b)
-        ok = bool(np.array_equal(out[r, c].astype(np.int64), cref)) and \
-            not np.any(out == 2 ** 31 - 1)
-    else:
-        vals = out[r, c].astype(np.float64)
-        cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, lda, ldb, bias=w["bias"],
-                                   op_a=op_a, op_b=op_b)
-        tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
-                                            2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
-                                   if c_dtype == "f16" else 0.0)
-        ok = bool(np.all(np.abs(vals - cref) <= tol)) and not np.isnan(out).any()
-    if not ok:
-        print(json.dumps({"error": "parity gate failed", "workload": a.workload,
-                          "config": info["name"]}))
-        return 1
 
-    # ---- timing: warmup, then exactly K steps between two synchronisations
-    for _ in range(a.warmup):
+    # ---- timing: warmup, then exactly `steps` launches between two synchronisations
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(a.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    per_launch_s = gpu_ms / 1e3 / a.steps
+    per_launch_s = gpu_ms / 1e3 / steps
     flop = 2.0 * M * N * K
     elapsed = max(wall, gpu_ms / 1e3)
-    value = flop * a.steps / elapsed / 1e12
+    value = flop * steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
-    single = launch_stats(step, stream)
+    loops = timed_loops(step, stream, max(1, int(np.ceil(0.1 / per_launch_s))))
     board = None if a.no_board else board_sample(step, stream)
     ceiling = None
     if not is_i8:
@@ -423,61 +381,85 @@ def main():
                             "kernel_mfma": "%dx%dx%d" % (mi, mi, 512 // mi),
                             "frac_of_ceiling": round(achieved / own, 4)})
 
-    # ---- CPU oracle baseline on a bounded sample (whole rows of C)
+    # ---- CPU oracle: the whole product on the host cores, then the gate
+    threads = oracle.default_threads()
     cpu = None
-    if a.cpu_seconds > 0:
-        threads = oracle.default_threads()
-        rows = 8
-        while True:
-            t = time.perf_counter()
-            if is_i8:
-                oracle.gemm_i8_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K,
-                                   lda=lda, ldb=ldb, nthreads=threads, op_a=op_a, op_b=op_b)
-            else:
-                oracle.gemm_ref(w["A"] if op_a else w["A"][:rows], w["B"], rows, N, K, lda=lda,
-                                ldb=ldb, bias=w["bias"], nthreads=threads, op_a=op_a, op_b=op_b)
-            dt = time.perf_counter() - t
-            if dt >= 0.8 * a.cpu_seconds or rows >= M:
-                break
-            rows = min(M, max(rows + 1, int(rows * a.cpu_seconds / max(dt, 1e-3))))
-        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6),
-               "unit": "TOPS" if is_i8 else "TFLOP/s",
+    if a.no_cpu:
+        # the gate on sampled entries only
+        rng = np.random.default_rng(123)
+        r = rng.integers(0, M, a.samples)
+        c = rng.integers(0, N, a.samples)
+        if is_i8:
+            cref = oracle.gemm_i8_entries(w["A"], w["B"], r, c, K, lda, ldb, op_a=op_a, op_b=op_b)
+        else:
+            cref = oracle.gemm_entries(w["A"], w["B"], r, c, K, lda, ldb, bias=w["bias"],
+                                       op_a=op_a, op_b=op_b)
+        got = out[r, c]
+        gate = "%d sampled entries" % a.samples
+    else:
+        t = time.perf_counter()
+        if is_i8:
+            cref = oracle.gemm_i8_ref(w["A"], w["B"], M, N, K, lda=lda, ldb=ldb, nthreads=threads,
+                                      op_a=op_a, op_b=op_b)
+        else:
+            cref = oracle.gemm_ref(w["A"], w["B"], M, N, K, lda=lda, ldb=ldb, bias=w["bias"],
+                                   nthreads=threads, op_a=op_a, op_b=op_b)
+        dt = time.perf_counter() - t
+        cpu = {"value": round(flop / dt / 1e12, 6), "unit": "TOPS" if is_i8 else "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": "first %d of %d rows of C (%dx%dx%d %s dot products), %.1f s"
-                         % (rows, M, rows, N, K, "int64" if is_i8 else "fp64", dt)}
-        if rows == M and M * N * K <= 1 << 30 and not is_i8:
-            # the whole product fits the sample: also one core's rate
+               "sample": "whole: all %dx%d outputs of %dx%dx%d (%s dot products), %.1f s"
+                         % (M, N, M, N, K, "int64" if is_i8 else "fp64", dt),
+               "seconds": round(dt, 2), "cpu_model": oracle.cpu_model(),
+               "host_cpus_visible": len(os.sched_getaffinity(0))}
+        if M * N * K <= 1 << 30 and not is_i8:
+            # a small product: also one core's rate
             t = time.perf_counter()
             oracle.gemm_ref(w["A"], w["B"], M, N, K, lda=lda, ldb=ldb, bias=w["bias"],
                             nthreads=1, op_a=op_a, op_b=op_b)
             dt1 = time.perf_counter() - t
-            cpu["single_core"] = {"value": round(2.0 * M * N * K / dt1 / 1e12, 6),
-                                  "seconds": round(dt1, 3)}
+            cpu["single_core"] = {"value": round(flop / dt1 / 1e12, 6), "seconds": round(dt1, 3)}
+        got = out
+        gate = "every output"
+    if is_i8:
+        ok = bool(np.array_equal(got.astype(np.int64), cref)) and not np.any(out == 2 ** 31 - 1)
+    else:
+        vals = got.astype(np.float64)
+        tol = 1e-3 * np.sqrt(K) + (np.where(np.abs(cref) < 2.0 ** -14, 2.0 ** -24,
+                                            2.0 ** (np.floor(np.log2(np.maximum(np.abs(cref), 2.0 ** -14))) - 10))
+                                   if c_dtype == "f16" else 0.0)
+        ok = bool(np.all(np.abs(vals - cref) <= tol)) and not np.isnan(out).any()
+    if not ok:
+        print(json.dumps({"error": "parity gate failed", "workload": name,
+                          "config": info["name"], "checked": gate}))
+        return None
 
-    traffic = TRAFFIC_BYTES.get((a.workload, info["name"], kernel_source_digest(cid)))
+    traffic = TRAFFIC_BYTES.get((name, info["name"], kernel_source_digest(cid)))
     peak = PEAK_TOPS_INT8 if is_i8 else PEAK_TFLOPS
     unit = "TOPS" if is_i8 else "TFLOP/s"
-    line = {
+    return {
         "metric": ("int8 GEMM TOPS and % of MI355X int8 MFMA peak" if is_i8 else
                    "GEMM TFLOP/s and % of MI355X fp16 MFMA peak at 8192^3; fused bias+ReLU"),
         "value": round(value, 2),
         "unit": unit,
         "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(elapsed * 1e3 / a.steps, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed * 1e3 / steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8" if is_i8 else "f16",
         "data": "synthetic",
-        "config": {"workload": a.workload, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
+        "config": {"workload": name, "M": M, "N": N, "K": K, "c_dtype": c_dtype,
                    "fused_bias_relu": fused, "op_a": "T" if op_a else "N",
                    "op_b": "T" if op_b else "N", "kernel": info["name"],
+                   "k_slices": slices,
                    "packed_operands": "".join(x for x, bit in (("A", 1), ("B", 2))
                                               if packed & bit) or None,
+                   "workspace_bytes": used,
                    "pct_of_peak": round(100.0 * value / peak, 2)},
-        "single_launch": single,
+        "parity_gate": gate,
+        "loops": loops,
         "device": device_info(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": unit,
@@ -486,8 +468,10 @@ def main():
         "mfma_ceiling": ceiling,
         "board_under_load": board,
     }
-    print(json.dumps(line))
-    return 0
+
+
+# CPU time of the attention oracle's sample of query rows (seconds)
+ATTN_CPU_SECONDS = 12.0
 
 
 def attention_flop(w, rows=None):
@@ -566,7 +550,7 @@ def bench_attention(a):
     elapsed = max(wall, gpu_ms / 1e3)
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
-    single = launch_stats(step, stream)
+    loops = timed_loops(step, stream, max(1, int(np.ceil(0.1 / (gpu_ms / 1e3 / a.steps)))))
     board = None if a.no_board else board_sample(step, stream)
     # the matrix cores' rate on operands from Q and K (the score product's
     # inputs; both products run on 32x32x16)
@@ -578,7 +562,7 @@ def bench_attention(a):
 
     # ---- CPU oracle baseline: whole query rows, sampled
     cpu = None
-    if a.cpu_seconds > 0:
+    if not a.no_cpu:
         threads = oracle.default_threads()
         nr = 32
         while True:
@@ -588,9 +572,9 @@ def bench_attention(a):
             oracle.attention_rows(w["Q"], w["K"], w["V"], B, H, Hkv, Lq, Lk, d, w["qs"],
                                   w["ks"], w["vs"], scale, causal, sel, nthreads=threads)
             dt = time.perf_counter() - t
-            if dt >= 0.8 * a.cpu_seconds or nr >= 1 << 16:
+            if dt >= 0.8 * ATTN_CPU_SECONDS or nr >= 1 << 16:
                 break
-            nr = min(1 << 16, max(nr + 1, int(nr * a.cpu_seconds / max(dt, 1e-3))))
+            nr = min(1 << 16, max(nr + 1, int(nr * ATTN_CPU_SECONDS / max(dt, 1e-3))))
         f, _ = attention_flop(w, sel[:, 2])
         cpu = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle",
@@ -613,7 +597,7 @@ def bench_attention(a):
         "config": {"workload": a.workload, "B": B, "H": H, "Hkv": Hkv, "Lq": Lq, "Lk": Lk,
                    "d": d, "causal": bool(causal), "kernel": "attn_fwd<%d,%s>" % (d, bool(causal)),
                    "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
-        "single_launch": single,
+        "loops": loops,
         "device": device_info(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",

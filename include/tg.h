@@ -17,10 +17,12 @@
  *
  * Ownership: the caller owns every buffer.  A, B, C and bias must be device
  * memory of the current HIP device (hipMalloc, or a framework allocation on
- * that device).  The library allocates no device memory, keeps no per-call
- * state and is safe to call from several host threads.  Calls are
- * asynchronous on `stream` (NULL = the default stream): the buffers must stay
- * alive, and C must not be read, until the stream has passed the launch.
+ * that device).  The library never allocates device memory: the calls that
+ * can use more memory than their operands (tg_gemm_ws) take a workspace the
+ * caller owns.  Apart from the read-only tuning cache, the library keeps no
+ * state between calls and is safe to call from several host threads.  Calls
+ * are asynchronous on `stream` (NULL = the default stream): the buffers must
+ * stay alive, and C must not be read, until the stream has passed the launch.
  * C must not alias A, B or bias.
  *
  * Errors: arguments are validated on the host before any device work; on an
@@ -31,7 +33,12 @@
  *                              a NULL pointer when the call has work to do; a
  *                              NULL bias in the fused call; an unknown dtype;
  *                              a pointer not aligned to its element size; an
- *                              unknown config id
+ *                              unknown config id; a buffer whose elements run
+ *                              past the end of the allocation that holds it
+ *                              (A over its (rows - 1) * lda + cols stored
+ *                              elements, B and C likewise, bias over N; checked
+ *                              with hipMemGetAddressRange, i.e. against the
+ *                              whole hipMalloc block of a pooled allocation)
  *   TG_ERROR_NOT_DEVICE_MEMORY a pointer that is host or unregistered memory,
  *                              or device memory of another device (a host
  *                              pointer would otherwise read as garbage or an
@@ -40,6 +47,8 @@
  *   TG_ERROR_UNSUPPORTED       the current device is not gfx950, or an operand
  *                              spans 2 GiB or more (32-bit buffer offsets)
  *   TG_ERROR_LAUNCH            the HIP runtime rejected the kernel launch
+ *   TG_ERROR_WORKSPACE         (tg_gemm_ws) the plan the caller named needs
+ *                              more workspace than the call provides
  *
  * Edge cases: M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros
  * (the empty sum), or relu(bias[j]) in the fused call.
@@ -70,7 +79,8 @@ typedef enum {
     TG_ERROR_NOT_DEVICE_MEMORY = 2,
     TG_ERROR_UNSUPPORTED = 3,
     TG_ERROR_LAUNCH = 4,
-    TG_ERROR_FILE = 5            /* tg_tuning_load: the file cannot be opened or read */
+    TG_ERROR_FILE = 5,           /* tg_tuning_load: the file cannot be opened or read */
+    TG_ERROR_WORKSPACE = 6       /* tg_gemm_ws: workspace too small for the named plan */
 } tg_status;
 
 /* C = A.B (overwrites C; no alpha/beta scaling).  A, B: fp16; C: c_dtype. */
@@ -108,53 +118,85 @@ tg_status tg_gemm_ex(tg_op op_a, tg_op op_b, const void *A, const void *B,
                      int64_t lda, int64_t ldb, int64_t ldc,
                      tg_dtype c_dtype, hipStream_t stream);
 
-/* ---- split-K: K cut into slices, with a caller-owned workspace ------------
- * For problems with few output tiles and a long K (M*N small next to the
- * 256 CUs, K large), one workgroup per output tile leaves most of the chip
- * idle.  These calls cut K into `splits` slices of k_split elements (K/splits
- * rounded up to the kernel's K step; fewer slices when K is short), run every
- * slice's product as its own set of workgroups, each writing an fp32 (int32
- * for int8 operands) partial product of C to the workspace, and then sum the
- * partials in slice order, add the bias, apply ReLU and convert to C's type
- * in a second kernel on the same stream.  The order is fixed, so a result is
- * reproducible; it may differ from the unsliced call's by fp32 rounding (for
- * integer inputs and int8 operands it is exact and equal).  The product is
- * the one defined at the top of this file; only the grouping of the K sum
- * changes.
+/* ---- the dispatcher with a caller-owned workspace --------------------------
+ * The same product as tg_gemm_ex, run by a plan that may use device memory
+ * beyond the operands: a workspace the caller passes in.  Two techniques use
+ * it, alone or together:
  *
+ *  K slices (split-K).  For problems with few output tiles and a long K (M*N
+ *  small next to the 256 CUs, K large) one workgroup per output tile leaves
+ *  most of the chip idle.  K is cut into `slices` slices of k_split elements
+ *  (K/slices rounded up to the kernel's K step; fewer slices when K is short);
+ *  every slice's product runs as its own set of workgroups, each writing an
+ *  fp32 (int32 for int8 operands) partial product of C to the workspace, and
+ *  a second kernel on the same stream sums the partials in slice order, adds
+ *  the bias, applies ReLU and converts to C's type.  The order is fixed, so a
+ *  result is reproducible; it may differ from the unsliced call's by fp32
+ *  rounding (for integer inputs and int8 operands it is exact and equal).
+ *  Partials take slices * M * N * 4 bytes.
+ *
+ *  Packed operands.  The direct configurations copy 16-byte chunks of A and
+ *  B straight to LDS; an operand whose base is not 16-byte aligned, or whose
+ *  leading dimension or row length is not a multiple of 16 bytes, is
+ *  otherwise read by a register-staged configuration (what tg_gemm_ex does).
+ *  The plan may instead copy such an operand into the workspace in a packed
+ *  layout -- the same stored rows, each padded with zeros to a multiple of
+ *  16 bytes, which is also the copy's leading dimension -- and run a direct
+ *  configuration on the copy with K rounded up to a whole chunk.  Zeros added
+ *  to a sum change nothing (on integer inputs the result is bit-identical).
+ *  A copy takes rows * (cols rounded up to 16 bytes) bytes, rounded up to 256.
+ *
+ * The product is the one defined at the top of this file; only the grouping
+ * of the K sum changes.  Workspace layout: the copies first, then the
+ * partials.
+ *
+ * config_id: -1 = the dispatcher's choice, else that configuration.
+ * splits:    0 = chosen: with config_id == -1, the plan with the least
+ *            modelled time among the operands as passed (unsliced, or in 2..32
+ *            slices) and packed copies (unsliced or sliced) whose workspace
+ *            fits workspace_bytes (a tuning-cache record for the exact problem
+ *            is run as recorded: unpacked, unsliced); with a named
+ *            configuration, the slice count only (never packed);
+ *            1 = unsliced and unpacked (the workspace is not used);
+ *            2..64 = that many slices of the operands as passed (never
+ *            packed).
  * workspace: device memory of the current device, 16-byte aligned, not
- * overlapping A, B, C or bias, of at least tg_splitk_workspace_bytes(M, N,
- * slices) bytes for the slice count used; owned by the caller, who must keep
- * it alive and not reuse it until the stream has passed the call.  Calls
- * that share a workspace must be ordered (same stream, or synchronised). */
+ *            overlapping A, B, C or bias; NULL only with workspace_bytes 0.
+ *            Owned by the caller, who keeps it alive and does not reuse it
+ *            until the stream has passed the call: calls that share a
+ *            workspace must be ordered (same stream, or synchronised).  The
+ *            library writes every workspace byte it reads in the same call,
+ *            so no clearing is needed.
+ * Errors: as tg_gemm_ex; additionally TG_ERROR_INVALID_VALUE for splits
+ * outside 0..64, an unknown config_id, a NULL workspace with nonzero
+ * workspace_bytes or one not 16-byte aligned; TG_ERROR_WORKSPACE when the
+ * named slice count needs more than workspace_bytes; TG_ERROR_UNSUPPORTED when
+ * the named configuration cannot run the problem; TG_ERROR_NOT_DEVICE_MEMORY
+ * or TG_ERROR_INVALID_VALUE for a workspace that is not device memory of the
+ * current device or whose used part runs past its allocation. */
+tg_status tg_gemm_ws(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
+                     const void *B, const float *bias, void *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes for `splits` slices: splits * M * N * 4 (0 if splits <= 1
- * or M, N <= 0; 0 also for splits > 64, which the calls reject). */
+/* Partial-product bytes of `splits` K slices: splits * M * N * 4 (0 if
+ * splits <= 1 or M, N <= 0; 0 also for splits > 64, which the calls reject). */
 size_t tg_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
 
-/* As tg_gemm_ex (and tg_gemm_with_config when config_id >= 0), computed in K
- * slices.  config_id: -1 = the dispatcher's choice.  splits: 0 = chosen by
- * the dispatcher's cost model among 1 (no slicing) and 2..32 slices whose
- * partials fit in workspace_bytes (with a NULL workspace only 1); 1 = no
- * slicing (then the workspace is not used); 2..64 = that many slices.
- * Additional errors: TG_ERROR_INVALID_VALUE for splits outside 0..64, or
- * when slicing is used and the workspace is NULL, not 16-byte aligned or too
- * small; TG_ERROR_NOT_DEVICE_MEMORY for a workspace that is not device memory
- * of the current device. */
-tg_status tg_gemm_splitk(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
-                         const void *B, const float *bias, void *C,
-                         int64_t M, int64_t N, int64_t K,
+/* What tg_gemm_ws(-1, 0, ..., workspace_bytes, ...) runs: *config_id the
+ * configuration (-1 for an empty problem), *splits the slice count (1:
+ * unsliced), *packed a bit mask of the operands copied first (1: A, 2: B) and
+ * *workspace_used the workspace bytes the plan uses (<= workspace_bytes).
+ * With workspace_bytes = SIZE_MAX, *workspace_used is the workspace the
+ * dispatcher's fastest plan needs.  Touches no device state; returns the
+ * argument errors the call would (TG_ERROR_INVALID_VALUE, also for NULL
+ * outputs). */
+tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
                          int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* The configuration and slice count tg_gemm_splitk(-1, 0, ...) would use
- * with a workspace of workspace_bytes (*splits = 1: no slicing; for an empty
- * problem *config_id = -1).  Touches no device state; returns
- * TG_ERROR_INVALID_VALUE for invalid arguments, as the call would. */
-tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
-                           const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
-                           int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                           size_t workspace_bytes, int *config_id, int *splits);
+                         size_t workspace_bytes, int *config_id, int *splits, int *packed,
+                         size_t *workspace_used);
 
 /* ---- fused attention (forward) -------------------------------------------
  * O = softmax(scale * Q K^T [+ causal mask]) V for every batch b < B and
@@ -165,7 +207,8 @@ tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
  *   lse[b][h][i]  = log sum_j exp(s_ij)            (natural log)
  * over the visible keys: j < Lk and, with causal = 1, j <= i + (Lk - Lq)
  * (the mask aligned at the bottom right: with Lq == Lk, j <= i).  A query
- * that sees no key gets O = 0 and lse = -inf.
+ * that sees no key gets O = 0 and lse = -inf.  scale may have either sign;
+ * scale == 0 gives every visible key the same weight, exactly.
  *
  * Q, K, V, O: fp16; scores, softmax and the weighted sum in fp32, the
  * softmax weights rounded to fp16 for the second product.  Layout: element
@@ -205,8 +248,9 @@ const char *tg_status_string(tg_status s);
  *      timings; the configuration with the least predicted time wins,
  *   4. the register-staged kernels, which take any alignment,
  * and at each step uses the configuration only if it can run the problem
- * (tg_config_supports).  After steps 2-4, operands that rule out the direct
- * copies may be packed first (see "packed operands" below). */
+ * (tg_config_supports).  tg_gemm, tg_gemm_bias_relu and tg_gemm_ex run that
+ * configuration on the operands as passed; tg_gemm_ws may also slice K or
+ * pack operands (above). */
 
 typedef struct {
     int id;
@@ -237,10 +281,8 @@ int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void
                        const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
 
-/* The configuration id the dispatcher would run on the operands as passed,
- * or -1 for invalid arguments (when it packs operands first, the call runs
- * the configuration tg_select_plan reports instead).  Touches no device
- * state. */
+/* The configuration id tg_gemm_ex runs for these arguments, or -1 for
+ * invalid arguments.  Touches no device state. */
 int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
                      const void *C, int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype);
@@ -253,66 +295,6 @@ tg_status tg_gemm_with_config(int config_id, tg_op op_a, tg_op op_b, const void 
                               int64_t M, int64_t N, int64_t K,
                               int64_t lda, int64_t ldb, int64_t ldc,
                               tg_dtype c_dtype, hipStream_t stream);
-
-/* ---- packed operands and library scratch ---------------------------------
- * The direct configurations copy 16-byte chunks of A and B straight to LDS;
- * an operand whose base is not 16-byte aligned, or whose leading dimension or
- * row length is not a multiple of 16 bytes, otherwise goes to a register-
- * staged configuration.  The dispatcher (tg_gemm, tg_gemm_bias_relu and
- * tg_gemm_ex; never for a tuning-cache hit, and never tg_gemm_with_config or
- * tg_gemm_splitk) may instead copy such an
- * operand first into a packed layout -- the same stored rows, each padded
- * with zeros to a multiple of 16 bytes, which is also the copy's leading
- * dimension -- and run a direct configuration on the copy with K rounded up
- * to a whole chunk.  It does so when its cost model predicts the copy plus
- * the direct kernel to be faster.  Results equal the unpacked ones within
- * the usual rounding (zeros added to a sum change nothing; on integer inputs
- * they are bit-identical).
- *
- * The copy lives in device memory the library allocates (hipMalloc) and
- * keeps: one buffer per (device, stream), grown when a call needs more
- * (growing waits for the stream and frees the old buffer).  While a stream
- * is being captured into a graph the library never allocates: a call whose
- * copy does not fit the stream's buffer runs unpacked.  Calls on different
- * streams use different buffers; calls from several host threads on one
- * stream are serialized while they enqueue their kernels, so they never
- * share a copy.  A buffer is kept until tg_scratch_release or the end of the
- * process, also after its stream is destroyed.  A graph captured from a
- * packed call refers to its stream's buffer: when a later call replaces that
- * buffer with a larger one, the old one is kept (not freed) until
- * tg_scratch_release, so the graph stays valid until then.
- *
- * Policy: TG_PACK_AUTO (the default) packs as above; TG_PACK_NEVER never
- * packs (the library then allocates nothing); TG_PACK_ALWAYS packs whenever
- * an operand rules out the direct copies and a direct configuration can run
- * the copies.  The initial policy comes from the environment variable
- * TG_PACK ("auto", "never" or "always"; anything else: auto), read at the
- * first call that needs it. */
-enum { TG_PACK_AUTO = 0, TG_PACK_NEVER = 1, TG_PACK_ALWAYS = 2 };
-
-/* Set the pack policy for the process; returns the previous one, or -1 (and
- * changes nothing) for an unknown value.  Takes effect for later calls. */
-int tg_set_pack_policy(int policy);
-
-/* What the dispatcher does for this call: *config_id the configuration that
- * runs (-1 for an empty problem), *packed a bit mask of the operands copied
- * first (1: A, 2: B; 0: none) and *scratch_bytes the scratch those copies
- * need (the call may still run unpacked under stream capture, see above).
- * Touches no device state; TG_ERROR_INVALID_VALUE for invalid arguments or
- * NULL outputs. */
-tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
-                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
-                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                         int *config_id, int *packed, size_t *scratch_bytes);
-
-/* Free the scratch of every device and stream, after waiting for each device
- * that holds some to finish its work.  Must not race with GEMM calls, and
- * graphs captured from packed calls must not be replayed afterwards.
- * TG_ERROR_LAUNCH if a HIP call fails (the buffers are forgotten anyway). */
-tg_status tg_scratch_release(void);
-
-/* Bytes of scratch the library holds, over all devices and streams. */
-size_t tg_scratch_held(void);
 
 /* ---- run-time tuning cache ------------------------------------------------
  * Exact-shape records written by the on-device sweep (the sweep's --tune
@@ -354,41 +336,6 @@ tg_status tg_tuning_clear(void);
 
 /* Number of keys in the cache. */
 int tg_tuning_count(void);
-
-/* ---- diagnostics: the matrix cores' rate on given operand values ----
- * No passage of the pages defines this call; it is a measurement aid for the
- * GEMM's roofline.  Under the board's power limit the shader clock drops as
- * the bits of the MFMA operands toggle, so the dense fp16 rate that any
- * kernel can sustain depends on the data: all-zero operands reach the nominal
- * peak, random ones stay well below it.  This call runs the matrix cores
- * alone on operands taken from `operands`, with no memory traffic in its loop,
- * and so measures the ceiling a GEMM on such values can approach.
- *
- * mfma:       32 (v_mfma_f32_32x32x16_f16, the shape of the GEMM kernels) or
- *             16 (v_mfma_f32_16x16x32_f16).
- * operands:   TG_CEILING_OPERAND_BYTES bytes of fp16 values in device memory
- *             (16-byte aligned), read once per thread: thread t of every
- *             workgroup takes the 32 16-byte chunks at byte 512 t -- chunks
- *             16 s + j (j < 8) are its A fragments of set s, chunks
- *             16 s + 8 + j its B fragments.
- * sink:       workgroups * 256 floats of device memory; thread t of
- *             workgroup w writes the sum of its accumulators to
- *             sink[256 w + t] (so the work is not optimised away).
- * iters:      k-steps of 32 per wave: even, 2 .. 2^30.  The two operand sets
- *             alternate from one k-step to the next.
- * workgroups: 1 .. 2^20 workgroups of 4 waves, one per SIMD; iters *
- *             workgroups at most 2^32 (about ten seconds of work).
- * Work: workgroups * 4 * iters * 2 * 128 * 128 * 32 FLOP (every wave holds a
- * 128 x 128 fp32 accumulator tile).  Asynchronous on `stream`; time it with
- * events on that stream.
- * Errors: TG_ERROR_INVALID_VALUE (bad mfma, iters or workgroups, or too much
- * work; NULL or
- * misaligned pointer; a buffer that does not fit inside its allocation),
- * TG_ERROR_NOT_DEVICE_MEMORY, TG_ERROR_UNSUPPORTED (not gfx950),
- * TG_ERROR_LAUNCH. */
-#define TG_CEILING_OPERAND_BYTES 131072
-tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t iters,
-                          int64_t workgroups, hipStream_t stream);
 
 /* Library version string (static). */
 const char *tg_version(void);

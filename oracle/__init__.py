@@ -71,7 +71,28 @@ def _u16(a):
 
 
 def default_threads():
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the oracle: the CPUs this process may run on, or fewer when
+    OMP_NUM_THREADS declares a smaller share of the host."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu's 'Model name'), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def decode(bits):

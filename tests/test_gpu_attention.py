@@ -205,6 +205,42 @@ def test_scale_sign_and_zero(scale):
     run_values(Qv, Kv, Vv, True, scale, "scale %g" % scale)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0, 1e-35, -1e-35])
+def test_zero_scale_gives_exactly_uniform_weights(scale):
+    """A zero (or negligible) scale: every visible key weighs the same, so O
+    is the mean of the visible V rows and lse = log(visible keys), with no
+    NaN from masked keys."""
+    B, H, Lq, Lk, d = 1, 2, 160, 96, 64
+    rng = np.random.default_rng(6)
+    Qv, Kv, Vv = (8.0 * rng.standard_normal((B, H, L, d)) for L in (Lq, Lk, Lk))
+    Q, K, V = (np.ascontiguousarray(x).astype(np.float16).view(np.uint16).reshape(-1)
+               for x in (Qv, Kv, Vv))
+    qs, ks = (H * Lq * d, Lq * d, d), (H * Lk * d, Lk * d, d)
+    tq, tk, tv = dev(Q), dev(K), dev(V)
+    to = torch.full((B * H * Lq * d,), F16_NAN, dtype=torch.int16, device="cuda")
+    tl = torch.empty(B * H * Lq, dtype=torch.float32, device="cuda")
+    assert tg.tg_attention_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr(),
+                               tl.data_ptr(), B, H, H, Lq, Lk, d, qs, ks, ks, qs, scale, 1,
+                               torch.cuda.current_stream().cuda_stream) == tg.TG_SUCCESS
+    torch.cuda.synchronize()
+    O = to.cpu().numpy().view(np.float16).astype(np.float64).reshape(B, H, Lq, d)
+    lse = tl.cpu().numpy().reshape(B, H, Lq)
+    nv = np.broadcast_to(n_visible(Lq, Lk, True), (B, H, Lq))
+    seen = nv > 0
+    assert np.all(np.abs(lse[seen] - np.log(nv[seen])) <= 4e-7 * (1 + np.log(nv[seen])))
+    assert np.all(np.isneginf(lse[~seen])) and np.all(O[~seen] == 0)
+    V16 = V.view(np.float16).astype(np.float64).reshape(B, H, Lk, d)
+    csum = np.cumsum(V16, axis=2)
+    for i in range(Lq):
+        n = int(nv[0, 0, i])
+        if n:
+            mean = csum[:, :, n - 1] / n
+            # fp16 weights of exactly 1, an fp32 sum of n terms, one division,
+            # then the fp16 rounding of O
+            tol = n * 2.0 ** -24 * np.abs(V16).max() + 2.0 ** -11 * np.abs(mean) + 2.0 ** -24
+            assert np.all(np.abs(O[:, :, i] - mean) <= tol), i
+
+
 def test_running_maximum_keeps_growing():
     """Scores rise along the keys (0.8 per key for most rows), so the row
     maximum jumps past the reference again and again."""

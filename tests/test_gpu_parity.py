@@ -44,9 +44,11 @@ def to_dev(bits_2d, rows, cols, ld, offset_elems=0):
 
 
 def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=None,
-        a_off=0, b_off=0, c_off=0, what="", op_a=0, op_b=0):
+        a_off=0, b_off=0, c_off=0, what="", op_a=0, op_b=0, ws=False):
     """A, B: the stored operands (M x K or, with op_a, K x M; K x N or, with
-    op_b, N x K)."""
+    op_b, N x K).  ws: run through tg_gemm_ws with a workspace of the size the
+    dispatcher's fastest plan uses (with `config`: that configuration,
+    unsliced, packing what it cannot take as passed)."""
     ar, ac = (K, M) if op_a else (M, K)
     br, bc = (N, K) if op_b else (K, N)
     lda = ac if lda is None else lda
@@ -70,7 +72,18 @@ def run(A, B, M, N, K, c_dtype, bias=None, lda=None, ldb=None, ldc=None, config=
         pbias = tbias.data_ptr()
     code = tg.TG_DTYPE_F16 if c_dtype == "f16" else tg.TG_DTYPE_F32
     s = torch.cuda.current_stream().cuda_stream
-    if config is not None:
+    if ws:
+        st, _, _, _, used = tg.tg_select_plan(pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code,
+                                              op_a=op_a, op_b=op_b)
+        assert st == tg.TG_SUCCESS
+        if config is not None:   # a named configuration's copies: at most both operands
+            used = 2 * (ar + br + 2) * (max(ac, bc) + 16) * 2 + 1024
+        tw = torch.full((max(used, 16) // 4 + 4,), float("nan"), dtype=torch.float32,
+                        device="cuda")
+        st = tg.tg_gemm_ws(-1 if config is None else config, 0 if config is None else 1, pa, pb,
+                           pbias, pc, M, N, K, lda, ldb, ldc, code, tw.data_ptr(), used, s,
+                           op_a=op_a, op_b=op_b)
+    elif config is not None:
         st = tg.tg_gemm_with_config(config, pa, pb, pbias, pc, M, N, K, lda, ldb, ldc, code, s,
                                     op_a=op_a, op_b=op_b)
     elif op_a or op_b:

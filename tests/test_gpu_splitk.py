@@ -1,4 +1,5 @@
-"""K-sliced (split-K) GEMM through the C ABI on gfx950, against the oracle.
+"""K-sliced (split-K) GEMM through the C ABI (tg_gemm_ws) on gfx950, against
+the oracle.
 
 Integer inputs make every partial sum exact in fp32 (int32 for int8), so the
 sliced result must equal the oracle bit for bit whatever the slicing; the
@@ -73,9 +74,9 @@ def run(A, B, M, N, K, dtype, op_a=0, op_b=0, bias=None, config=-1, splits=0, ld
     need = tg.tg_splitk_workspace_bytes(M, N, max(splits, 32))
     nbytes = need if ws_bytes is None else ws_bytes
     ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
-    st = tg.tg_gemm_splitk(config, splits, pa, pb, tbias.data_ptr() if tbias is not None else None,
-                           tc.data_ptr(), M, N, K, lda, ldb, N, CODES[dtype], ws.data_ptr(),
-                           nbytes, torch.cuda.current_stream().cuda_stream, op_a=op_a, op_b=op_b)
+    st = tg.tg_gemm_ws(config, splits, pa, pb, tbias.data_ptr() if tbias is not None else None,
+                       tc.data_ptr(), M, N, K, lda, ldb, N, CODES[dtype], ws.data_ptr(),
+                       nbytes, torch.cuda.current_stream().cuda_stream, op_a=op_a, op_b=op_b)
     assert st == tg.TG_SUCCESS, tg.tg_status_string(st)
     torch.cuda.synchronize()
     out = tc.cpu().numpy()
@@ -149,8 +150,9 @@ def test_auto_choice_slices_small_tile_count_long_k():
     result is exact on integers and equal to the unsliced call's."""
     M, N, K = 640, 640, 8192
     P = 0x100000
-    st, cid, sp = tg.tg_select_splitk(P, P, None, P, M, N, K, K, N, N, tg.TG_DTYPE_F32, 1 << 30)
-    assert st == tg.TG_SUCCESS and sp > 1
+    st, cid, sp, packed, used = tg.tg_select_plan(P, P, None, P, M, N, K, K, N, N,
+                                                  tg.TG_DTYPE_F32, 1 << 30)
+    assert st == tg.TG_SUCCESS and sp > 1 and packed == 0
     A, B = host_operands(M, N, K, 0, 0, "f16", 77)
     out = run(A, B, M, N, K, "f32", what="auto")
     check_exact(out, A, B, M, N, K, "f32", 0, 0, None, "auto")
@@ -180,12 +182,12 @@ def test_workspace_errors():
     ws = torch.empty(need // 4 + 4, dtype=torch.float32, device="cuda")
     host_ws = np.zeros(need // 4, np.float32)
     args = (pa, pb, None, tc.data_ptr(), M, N, K, K, N, N, tg.TG_DTYPE_F32)
-    assert tg.tg_gemm_splitk(-1, 4, *args, None, 0, s) == tg.TG_ERROR_INVALID_VALUE
-    assert tg.tg_gemm_splitk(-1, 4, *args, ws.data_ptr(), need - 4, s) == tg.TG_ERROR_INVALID_VALUE
-    assert tg.tg_gemm_splitk(-1, 4, *args, ws.data_ptr() + 4, need, s) == tg.TG_ERROR_INVALID_VALUE
-    assert tg.tg_gemm_splitk(-1, 4, *args, host_ws.ctypes.data, need,
-                             s) == tg.TG_ERROR_NOT_DEVICE_MEMORY
-    assert tg.tg_gemm_splitk(-1, 4, *args, ws.data_ptr(), need, s) == tg.TG_SUCCESS
+    assert tg.tg_gemm_ws(-1, 4, *args, None, 0, s) == tg.TG_ERROR_WORKSPACE
+    assert tg.tg_gemm_ws(-1, 4, *args, ws.data_ptr(), need - 4, s) == tg.TG_ERROR_WORKSPACE
+    assert tg.tg_gemm_ws(-1, 4, *args, ws.data_ptr() + 4, need, s) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_ws(-1, 4, *args, host_ws.ctypes.data, need,
+                         s) == tg.TG_ERROR_NOT_DEVICE_MEMORY
+    assert tg.tg_gemm_ws(-1, 4, *args, ws.data_ptr(), need, s) == tg.TG_SUCCESS
     torch.cuda.synchronize()
 
 

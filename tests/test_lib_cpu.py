@@ -1,5 +1,6 @@
-"""libtg.so on the CPU: it loads, exports every function include/tg.h
-declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+"""libtg.so on the CPU: it loads, exports every function include/tg.h and
+include/tg_diag.h declare, imports no HIP allocation call, and rejects bad
+arguments before any HIP call (no GPU needed)."""
 import os
 import re
 
@@ -15,9 +16,14 @@ F16, F32 = tg.TG_DTYPE_F16, tg.TG_DTYPE_F32
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "tg.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function():
@@ -27,8 +33,22 @@ def test_exports_every_declared_function():
         assert hasattr(tg.lib, name)
 
 
+def test_library_imports_no_allocation_call():
+    """The library allocates no device (or pinned host) memory: its dynamic
+    symbol table imports none of HIP's allocation or free calls, nor a
+    stream or device synchronisation."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", tg.LIB_PATH], check=True,
+                         stdout=subprocess.PIPE, text=True).stdout
+    imported = set(re.findall(r"\bU (\w+)", out))
+    hip = sorted(n for n in imported if n.startswith("hip"))
+    assert "hipLaunchKernel" in hip   # the table is read correctly
+    bad = [n for n in hip if re.search(r"Malloc|Free|Alloc|HostRegister|Synchronize|MemPool", n)]
+    assert bad == [], bad
+
+
 def test_status_strings_and_version():
-    for s in range(6):
+    for s in range(7):
         assert tg.tg_status_string(s).startswith("TG_")
     assert "gfx950" in tg.tg_version()
 

@@ -1,7 +1,7 @@
-"""Split-K entry points of libtg.so on the CPU: argument and workspace
-checks happen before any device call, and the dispatcher's choice of
-configuration and slice count (tg_select_splitk) is checked against
-recorded on-device timings."""
+"""K slicing through tg_gemm_ws on the CPU: argument and workspace checks
+happen before any device call, and the dispatcher's choice of configuration
+and slice count (tg_select_plan) is checked against recorded on-device
+timings."""
 import os
 
 import pytest
@@ -17,9 +17,14 @@ CONFIGS = {c["id"]: c for c in tg.configs()}
 
 
 def select(M, N, K, ws_bytes, dtype=F16, op_a=0, op_b=0, bias=None):
+    """(status, configuration, slices) of the dispatcher's plan; aligned
+    operands, so nothing is packed."""
     lda, ldb = (M if op_a else K), (K if op_b else N)
-    return tg.tg_select_splitk(PA, PB, bias, PC, M, N, K, lda, ldb, N, dtype, ws_bytes,
-                               op_a=op_a, op_b=op_b)
+    st, cid, sp, packed, used = tg.tg_select_plan(PA, PB, bias, PC, M, N, K, lda, ldb, N, dtype,
+                                                  ws_bytes, op_a=op_a, op_b=op_b)
+    assert packed == 0 and used <= ws_bytes
+    assert used == (tg.tg_splitk_workspace_bytes(M, N, sp) if st == tg.TG_SUCCESS else 0)
+    return st, cid, sp
 
 
 def test_workspace_bytes():
@@ -29,30 +34,31 @@ def test_workspace_bytes():
     assert tg.tg_splitk_workspace_bytes(640, 640, 65) == 0
 
 
-@pytest.mark.parametrize("splits,ws,nbytes", [
-    (-1, PW, 1 << 30),            # splits out of range
-    (65, PW, 1 << 30),
-    (4, None, 0),                 # slicing without a workspace
-    (4, PW, 4 * 640 * 640 * 4 - 4),   # too small
-    (4, PW + 8, 1 << 30),         # not 16-byte aligned
+@pytest.mark.parametrize("splits,ws,nbytes,status", [
+    (-1, PW, 1 << 30, tg.TG_ERROR_INVALID_VALUE),            # splits out of range
+    (65, PW, 1 << 30, tg.TG_ERROR_INVALID_VALUE),
+    (4, PW + 8, 1 << 30, tg.TG_ERROR_INVALID_VALUE),         # not 16-byte aligned
+    (4, None, 1 << 30, tg.TG_ERROR_INVALID_VALUE),           # NULL with a size
+    (4, None, 0, tg.TG_ERROR_WORKSPACE),                     # named slicing without one
+    (4, PW, 4 * 640 * 640 * 4 - 4, tg.TG_ERROR_WORKSPACE),   # too small
 ])
-def test_invalid_split_arguments_rejected_without_gpu(splits, ws, nbytes):
-    st = tg.tg_gemm_splitk(-1, splits, PA, PB, None, PC, 640, 640, 8192, 8192, 640, 640, F32,
-                           ws, nbytes)
-    assert st == tg.TG_ERROR_INVALID_VALUE
+def test_invalid_split_arguments_rejected_without_gpu(splits, ws, nbytes, status):
+    st = tg.tg_gemm_ws(-1, splits, PA, PB, None, PC, 640, 640, 8192, 8192, 640, 640, F32,
+                       ws, nbytes)
+    assert st == status
 
 
 def test_split_validation_follows_the_plain_call():
     # the problem's own errors come first, whatever the slicing
-    assert tg.tg_gemm_splitk(-1, 4, PA, PB, None, PC, -1, 640, 8192, 8192, 640, 640, F32, PW,
-                             1 << 30) == tg.TG_ERROR_INVALID_VALUE
-    assert tg.tg_gemm_splitk(-1, 4, PA, PB, PBIAS, PC, 64, 64, 64, 64, 64, 64, I32, PW,
-                             1 << 30) == tg.TG_ERROR_INVALID_VALUE
-    assert tg.tg_gemm_splitk(tg.tg_num_configs(), 4, PA, PB, None, PC, 64, 64, 64, 64, 64, 64,
-                             F32, PW, 1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_ws(-1, 4, PA, PB, None, PC, -1, 640, 8192, 8192, 640, 640, F32, PW,
+                         1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_ws(-1, 4, PA, PB, PBIAS, PC, 64, 64, 64, 64, 64, 64, I32, PW,
+                         1 << 30) == tg.TG_ERROR_INVALID_VALUE
+    assert tg.tg_gemm_ws(tg.tg_num_configs(), 4, PA, PB, None, PC, 64, 64, 64, 64, 64, 64,
+                         F32, PW, 1 << 30) == tg.TG_ERROR_INVALID_VALUE
     # empty problems succeed without a workspace or a device
-    assert tg.tg_gemm_splitk(-1, 4, PA, PB, None, PC, 0, 640, 8192, 8192, 640, 640, F32, None,
-                             0) == tg.TG_SUCCESS
+    assert tg.tg_gemm_ws(-1, 4, PA, PB, None, PC, 0, 640, 8192, 8192, 640, 640, F32, None,
+                         0) == tg.TG_SUCCESS
 
 
 def test_no_workspace_means_no_slicing():

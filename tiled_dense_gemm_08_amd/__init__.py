@@ -24,20 +24,16 @@ TG_ERROR_NOT_DEVICE_MEMORY = 2
 TG_ERROR_UNSUPPORTED = 3
 TG_ERROR_LAUNCH = 4
 TG_ERROR_FILE = 5
+TG_ERROR_WORKSPACE = 6
 
 TG_OP_N = 0
 TG_OP_T = 1
 
-TG_PACK_AUTO = 0
-TG_PACK_NEVER = 1
-TG_PACK_ALWAYS = 2
-
-# every function declared in include/tg.h
+# every function declared in include/tg.h and include/tg_diag.h
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
-            "tg_splitk_workspace_bytes", "tg_gemm_splitk", "tg_select_splitk",
-            "tg_select_plan", "tg_scratch_release", "tg_scratch_held", "tg_set_pack_policy",
+            "tg_splitk_workspace_bytes", "tg_gemm_ws", "tg_select_plan",
             "tg_attention_fwd", "tg_mfma_ceiling", "tg_version")
 
 
@@ -93,18 +89,10 @@ def _load():
     SZ = ctypes.c_size_t
     L.tg_splitk_workspace_bytes.argtypes = [I64, I64, I]
     L.tg_splitk_workspace_bytes.restype = SZ
-    L.tg_gemm_splitk.argtypes = [I, I, I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P, SZ, P]
-    L.tg_gemm_splitk.restype = I
-    L.tg_select_splitk.argtypes = [I, I] + shape_args + [SZ, IP, IP]
-    L.tg_select_splitk.restype = I
-    L.tg_select_plan.argtypes = [I, I] + shape_args + [IP, IP, ctypes.POINTER(SZ)]
+    L.tg_gemm_ws.argtypes = [I, I, I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P, SZ, P]
+    L.tg_gemm_ws.restype = I
+    L.tg_select_plan.argtypes = [I, I] + shape_args + [SZ, IP, IP, IP, ctypes.POINTER(SZ)]
     L.tg_select_plan.restype = I
-    L.tg_scratch_release.argtypes = []
-    L.tg_scratch_release.restype = I
-    L.tg_scratch_held.argtypes = []
-    L.tg_scratch_held.restype = SZ
-    L.tg_set_pack_policy.argtypes = [I]
-    L.tg_set_pack_policy.restype = I
     L.tg_attention_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
                                    ctypes.c_float, I, P]
     L.tg_attention_fwd.restype = I
@@ -171,43 +159,28 @@ def tg_select_config(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_
     return lib.tg_select_config(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype)
 
 
-def tg_select_plan(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, op_a=TG_OP_N, op_b=TG_OP_N):
-    """(status, config id, packed-operand mask (1: A, 2: B), scratch bytes)."""
-    cid, packed, scratch = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_size_t(0)
-    st = lib.tg_select_plan(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
-                            ctypes.byref(cid), ctypes.byref(packed), ctypes.byref(scratch))
-    return st, cid.value, packed.value, scratch.value
-
-
-def tg_scratch_release():
-    return lib.tg_scratch_release()
-
-
-def tg_scratch_held():
-    return lib.tg_scratch_held()
-
-
-def tg_set_pack_policy(policy):
-    return lib.tg_set_pack_policy(policy)
-
-
 def tg_splitk_workspace_bytes(M, N, splits):
     return lib.tg_splitk_workspace_bytes(M, N, splits)
 
 
-def tg_gemm_splitk(config_id, splits, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
-                   workspace, workspace_bytes, stream=0, op_a=TG_OP_N, op_b=TG_OP_N):
-    return lib.tg_gemm_splitk(config_id, splits, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
-                              c_dtype, workspace, workspace_bytes, stream or None)
+def tg_gemm_ws(config_id, splits, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, workspace,
+               workspace_bytes, stream=0, op_a=TG_OP_N, op_b=TG_OP_N):
+    return lib.tg_gemm_ws(config_id, splits, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
+                          c_dtype, workspace, workspace_bytes, stream or None)
 
 
-def tg_select_splitk(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, workspace_bytes,
-                     op_a=TG_OP_N, op_b=TG_OP_N):
-    """Returns (status, config_id, splits)."""
-    cid, sp = ctypes.c_int(-2), ctypes.c_int(-2)
-    st = lib.tg_select_splitk(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
-                              workspace_bytes, ctypes.byref(cid), ctypes.byref(sp))
-    return st, cid.value, sp.value
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def tg_select_plan(A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, workspace_bytes=SIZE_MAX,
+                   op_a=TG_OP_N, op_b=TG_OP_N):
+    """What tg_gemm_ws(-1, 0, ...) runs with that much workspace:
+    (status, config id, slices, packed-operand mask (1: A, 2: B), workspace bytes used)."""
+    cid, sp, packed, used = ctypes.c_int(-2), ctypes.c_int(-2), ctypes.c_int(-1), ctypes.c_size_t(0)
+    st = lib.tg_select_plan(op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                            workspace_bytes, ctypes.byref(cid), ctypes.byref(sp),
+                            ctypes.byref(packed), ctypes.byref(used))
+    return st, cid.value, sp.value, packed.value, used.value
 
 
 def _strides3(st):
@@ -303,9 +276,10 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None, wo
     or a transposed view of a row-major array (passed with TG_OP_T, no copy);
     out: optional preallocated (M, N) float16/float32 row-major tensor.
     config: None (dispatcher's choice) or a configuration id.
-    workspace: optional device tensor (any dtype, contiguous) that allows the
-    K-sliced (split-K) path, tg_gemm_splitk; splits: 0 lets the dispatcher
-    choose, n >= 1 forces n slices (needs a workspace when n > 1).
+    workspace: optional device tensor (any dtype, contiguous) passed to
+    tg_gemm_ws, which may then slice K or pack operands into it; splits: 0
+    lets the dispatcher choose, n >= 1 forces n slices (needs a workspace when
+    n > 1).  workspace_bytes(...) gives the size the fastest plan uses.
     """
     import torch
     if a.dtype != torch.float16 or b.dtype != torch.float16:
@@ -334,8 +308,8 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None, wo
             if not workspace.is_contiguous():
                 raise ValueError("workspace must be contiguous")
             pw, nw = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        st = tg_gemm_splitk(-1 if config is None else config, splits, pa, pb, pbias or None, pc,
-                            M, N, K, lda, ldb, ldc, code, pw or None, nw, s, op_a=op_a, op_b=op_b)
+        st = tg_gemm_ws(-1 if config is None else config, splits, pa, pb, pbias or None, pc,
+                        M, N, K, lda, ldb, ldc, code, pw or None, nw, s, op_a=op_a, op_b=op_b)
     elif config is not None:
         st = tg_gemm_with_config(config, pa, pb, pbias or None, pc, M, N, K, lda, ldb, ldc,
                                  code, s, op_a=op_a, op_b=op_b)
@@ -348,6 +322,23 @@ def gemm(a, b, out=None, out_dtype=None, bias=None, config=None, stream=None, wo
     if st != TG_SUCCESS:
         raise TgError(st, "tg_gemm")
     return out
+
+
+def workspace_bytes(a, b, out_dtype=None, bias=None):
+    """Workspace bytes tg_gemm_ws's fastest plan uses for these operands (0:
+    none).  Touches no device state."""
+    import torch
+    M, K = a.shape
+    N = b.shape[1]
+    pa, lda, op_a = _operand(a, "A")
+    pb, ldb, op_b = _operand(b, "B")
+    code = _dtype_code(out_dtype or torch.float16)
+    # the stand-in C address only has to be aligned: the plan does not read it
+    st, _, _, _, used = tg_select_plan(pa, pb, bias.data_ptr() if bias is not None else None,
+                                       256, M, N, K, lda, ldb, N, code, op_a=op_a, op_b=op_b)
+    if st != TG_SUCCESS:
+        raise TgError(st, "tg_select_plan")
+    return used
 
 
 def gemm_bias_relu(a, b, bias, out=None, out_dtype=None, config=None, stream=None,

@@ -132,6 +132,36 @@ def check_m0(asm_text):
     return bad
 
 
+def kernel_bodies(asm_text):
+    """{kernel symbol: its instruction lines} of the device assembly."""
+    out = {}
+    for part in re.split(r"\n(?=\S+:\s*; @)", asm_text):
+        m = re.match(r"(\S+):\s*; @", part)
+        if m:
+            out[m.group(1)] = [l.strip() for l in part.split("\n")]
+    return out
+
+
+def spill_report(asm_text):
+    """{kernel: (scratch accesses, scratch accesses inside a loop)}.  Scratch
+    (private) memory is where the compiler spills registers; a loop is the
+    range from a block label to the last branch back to it."""
+    rep = {}
+    for name, lines in kernel_bodies(asm_text).items():
+        scratch = [i for i, l in enumerate(lines) if l.startswith("scratch_")]
+        labels, loops = {}, []
+        for i, l in enumerate(lines):
+            m = re.match(r"(\.LBB\w+):", l)
+            if m:
+                labels[m.group(1)] = i
+            b = re.match(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", l)
+            if b and b.group(1) in labels and labels[b.group(1)] < i:
+                loops.append((labels[b.group(1)], i))
+        inside = [i for i in scratch if any(lo <= i <= hi for lo, hi in loops)]
+        rep[name] = (len(scratch), len(inside))
+    return rep
+
+
 def resource_report(asm_text):
     rows = []
     # amdhsa metadata blocks list name, vgpr/agpr/sgpr counts and spill counts

@@ -16,14 +16,13 @@
 #include <stdlib.h>
 
 #include <atomic>
-#include <map>
 #include <memory>
 #include <mutex>
 #include <unordered_map>
 #include <utility>
-#include <vector>
 
 #include "tg.h"
+#include "tg_diag.h"
 #include "tg_attention.h"
 #include "tg_ceiling.h"
 #include "tg_kernels.h"
@@ -539,6 +538,29 @@ tg_status check_pointer(const void *ptr, int dev)
     return TG_SUCCESS;
 }
 
+// ptr is device memory of device dev and [ptr, ptr + bytes) lies inside the
+// allocation that holds it (hipMemGetAddressRange: the whole hipMalloc block,
+// so a framework's sub-allocation is checked against its pool block).
+// TG_ERROR_INVALID_VALUE when the span runs past the allocation's end.
+tg_status check_span(const void *ptr, uint64_t bytes, int dev)
+{
+    if (ptr == nullptr || bytes == 0)
+        return TG_SUCCESS;
+    tg_status st = check_pointer(ptr, dev);
+    if (st != TG_SUCCESS)
+        return st;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return TG_ERROR_NOT_DEVICE_MEMORY;
+    }
+    const uintptr_t lo = (uintptr_t)base, at = (uintptr_t)ptr;
+    if (at < lo || at - lo > size || (uint64_t)(size - (at - lo)) < bytes)
+        return TG_ERROR_INVALID_VALUE;
+    return TG_SUCCESS;
+}
+
 // Kernel arguments of configuration cfg for problem p (no K slicing).
 tg_status make_params(const KernelConfig &cfg, const Problem &p, Params *out)
 {
@@ -570,16 +592,22 @@ tg_status make_params(const KernelConfig &cfg, const Problem &p, Params *out)
     return TG_SUCCESS;
 }
 
+// The problem's buffers are device memory of the current device and every
+// element the call reads or writes lies inside its allocation: A and B over
+// their stored rows (when K > 0), C over its M rows and bias over N floats.
 tg_status check_problem_pointers(const Problem &p, int *dev)
 {
     tg_status st;
     if ((st = check_device(dev)) != TG_SUCCESS)
         return st;
-    const bool need_ab = p.K > 0;
-    if ((need_ab && ((st = check_pointer(p.A, *dev)) != TG_SUCCESS ||
-                     (st = check_pointer(p.B, *dev)) != TG_SUCCESS)) ||
-        (st = check_pointer(p.C, *dev)) != TG_SUCCESS ||
-        (p.fused && (st = check_pointer(p.bias, *dev)) != TG_SUCCESS))
+    const uint64_t es = elem_size(p), ce = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
+    if (p.K > 0 &&
+        ((st = check_span(p.A, es * span_elems(a_rows(p), a_cols(p), p.lda), *dev)) != TG_SUCCESS ||
+         (st = check_span(p.B, es * span_elems(b_rows(p), b_cols(p), p.ldb), *dev)) != TG_SUCCESS))
+        return st;
+    if ((st = check_span(p.C, ce * span_elems(p.M, p.N, p.ldc), *dev)) != TG_SUCCESS)
+        return st;
+    if (p.fused && (st = check_span(p.bias, 4 * (uint64_t)p.N, *dev)) != TG_SUCCESS)
         return st;
     return TG_SUCCESS;
 }
@@ -591,271 +619,6 @@ tg_status launch_config(int id, const Params &k, bool f16_out, bool bias, hipStr
     if (launch == nullptr)
         return TG_ERROR_UNSUPPORTED;
     return launch(k, f16_out, bias, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
-}
-
-// ---- packed operands -----------------------------------------------------------
-// An operand the direct global->LDS copies cannot take (base not 16-byte
-// aligned, or leading dimension or row length not a multiple of 16 bytes) is
-// otherwise served by the register-staged kernels, which hide less memory
-// latency.  The dispatcher may instead copy it into library-held scratch, in a
-// packed layout: the same stored rows, each padded with zeros to a multiple of
-// 16 bytes, which is also the copy's leading dimension (tg_pack.hip).  The
-// direct kernel then runs on the copy; the kernel's K is K rounded up to a
-// whole 16-byte chunk (the padding holds zeros, and the rows past K of an
-// operand whose rows run along K lie past its copy range, which reads zeros).
-// Chosen when the modelled time of the best direct configuration on the copy,
-// plus the copy's modelled time, is below the best modelled time without it.
-// Copy time: a fixed part (the extra launch) and the bytes read and written
-// at an effective rate; fitted to on-device traces of the copy kernel for
-// copies of 0.5 MB .. 0.5 GB (3.4 us + bytes / 6.1e6 per us), rounded up.
-constexpr double kPackFixedUs = 4.0;
-constexpr double kPackBytesPerUs = 5.5e6;
-
-int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
-
-struct PackPlan {
-    int id = -1;                 // direct configuration run on the copies
-    bool pack[2] = {false, false};
-    Problem kp;                  // the problem the kernel sees (copy pointers set at run time)
-    tg::PackOperand op[2];       // the copies' geometry (src set, dst set at run time)
-    int64_t copy_bytes[2] = {0, 0};   // bytes of each copy
-    int64_t range[2] = {0, 0};        // copy ranges of the kernel's operands (bytes)
-    size_t scratch = 0;          // scratch bytes for both copies
-    double t = 0.0;              // modelled time, copies included
-};
-
-bool operand_direct_layout(const Problem &p, bool is_a)
-{
-    const void *ptr = is_a ? p.A : p.B;
-    const OperandShape o = is_a ? OperandShape{p.op_a == 0, p.M, p.lda, 0}
-                                : OperandShape{p.op_b == 1, p.N, p.ldb, 0};
-    return aligned(ptr, 16) && chunks_aligned(o, p);
-}
-
-// Pack policy (TG_PACK_AUTO / _NEVER / _ALWAYS): initial value from the
-// environment variable TG_PACK ("auto", "never", "always"), read once.
-std::atomic<int> g_pack_policy{-1};
-
-int pack_policy()
-{
-    int v = g_pack_policy.load(std::memory_order_relaxed);
-    if (v >= 0)
-        return v;
-    const char *e = getenv("TG_PACK");
-    v = TG_PACK_AUTO;
-    if (e && strcmp(e, "never") == 0)
-        v = TG_PACK_NEVER;
-    else if (e && strcmp(e, "always") == 0)
-        v = TG_PACK_ALWAYS;
-    int expected = -1;
-    g_pack_policy.compare_exchange_strong(expected, v, std::memory_order_relaxed);
-    return g_pack_policy.load(std::memory_order_relaxed);
-}
-
-// The pack plan for p, or false when the policy rules packing out, no direct
-// configuration can run the copies, or (policy auto) the plan is not
-// predicted to be faster than the best modelled configuration without copies.
-bool plan_pack(const Problem &p, PackPlan *out)
-{
-    const int policy = pack_policy();
-    if (policy == TG_PACK_NEVER || p.M == 0 || p.N == 0 || p.K == 0 || operands_aligned(p))
-        return false;
-    double t_plain = 0.0;
-    if (model_lookup(p, &t_plain) < 0 && policy != TG_PACK_ALWAYS)
-        return false;
-    const int64_t es = elem_size(p), ce = 16 / es;
-    PackPlan pl;
-    pl.pack[0] = !operand_direct_layout(p, true);
-    pl.pack[1] = !operand_direct_layout(p, false);
-    Problem kp = p;
-    kp.K = round_up(p.K, ce);
-    // the problem the eligibility check sees: packed rows along M or N are
-    // whole chunks of the copy
-    Problem chk = kp;
-    double bytes = 0.0;
-    for (int w = 0; w < 2; w++) {
-        const bool is_a = w == 0;
-        const bool kmaj = is_a ? p.op_a == 0 : p.op_b == 1;
-        const int64_t rows = is_a ? a_rows(p) : b_rows(p);
-        const int64_t cols = is_a ? a_cols(p) : b_cols(p);
-        const int64_t ld = is_a ? p.lda : p.ldb;
-        if (!pl.pack[w]) {
-            // unpacked: its own rows; an operand whose rows run along K keeps
-            // its K rows in range, so the kernel's extra K rows read zeros
-            pl.range[w] = es * span_elems(rows, cols, ld);
-            continue;
-        }
-        const int64_t cols_p = round_up(cols, ce);
-        const int64_t copy = rows * cols_p * es;
-        if (copy >= kMaxSpan)
-            return false;
-        pl.op[w] = tg::PackOperand{is_a ? p.A : p.B, nullptr, rows, cols, ld, cols_p, (int)es};
-        pl.copy_bytes[w] = copy;
-        pl.range[w] = copy;
-        pl.scratch += (size_t)round_up(copy, 256);
-        bytes += (double)(es * span_elems(rows, cols, ld) + copy);
-        if (is_a) {
-            kp.lda = cols_p;
-            chk.lda = cols_p;
-            if (!kmaj)
-                chk.M = cols_p;
-        } else {
-            kp.ldb = cols_p;
-            chk.ldb = cols_p;
-            if (!kmaj)
-                chk.N = cols_p;
-        }
-    }
-    // stand-in 16-byte-aligned addresses for the eligibility check
-    chk.A = pl.pack[0] ? reinterpret_cast<const void *>(uintptr_t(256)) : p.A;
-    chk.B = pl.pack[1] ? reinterpret_cast<const void *>(uintptr_t(512)) : p.B;
-    if (!operands_aligned(chk))
-        return false;
-    double t_direct = 0.0;
-    int id = model_lookup(chk, &t_direct, true);
-    if (id < 0)
-        return false;
-    // a measured exact-shape record for the copies' problem overrides the
-    // model's kernel (the predicted time still decides whether to pack)
-    if (elem_size(p) == 2) {
-        const int exact = dispatch_exact(chk.M, chk.N, chk.K, chk.fused);
-        if (exact >= 0 && kConfigs[exact].direct && supports(kConfigs[exact], chk))
-            id = exact;
-    }
-    pl.id = id;
-    pl.kp = kp;
-    pl.t = t_direct + kPackFixedUs + bytes / kPackBytesPerUs;
-    if (policy == TG_PACK_AUTO && !(pl.t < t_plain))
-        return false;
-    *out = pl;
-    return true;
-}
-
-// Library-held scratch for the copies: one buffer per (device, stream), grown
-// on demand and kept until tg_scratch_release or the end of the process.
-// Calls on one stream are ordered by the stream, so they share its buffer; the
-// lock is held from taking the buffer until the kernels that use it are
-// enqueued, so two host threads on one stream cannot interleave their copies.
-struct Scratch {
-    void *ptr = nullptr;
-    size_t bytes = 0;
-    bool captured = false;   // a captured graph may refer to this buffer
-};
-struct Retired {
-    int dev;
-    void *ptr;
-    size_t bytes;
-};
-std::mutex g_scratch_mu;
-std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
-std::vector<Retired> g_retired;   // replaced buffers that captured graphs may use
-
-// A buffer of at least `bytes` on the current device `dev` for `stream`
-// (caller holds g_scratch_mu), or nullptr: never allocated while the stream
-// is being captured into a graph, nor when the allocation fails.  A buffer
-// that a captured call used is not freed when it is replaced (a graph may
-// still replay that call) but kept until tg_scratch_release.
-void *scratch_for(int dev, hipStream_t stream, size_t bytes)
-{
-    Scratch &s = g_scratch[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    const bool capturing = cap != hipStreamCaptureStatusNone;
-    if (s.bytes >= bytes) {
-        s.captured = s.captured || capturing;
-        return s.ptr;
-    }
-    if (capturing)
-        return nullptr;
-    if (s.ptr != nullptr) {
-        if (s.captured) {
-            g_retired.push_back(Retired{dev, s.ptr, s.bytes});
-        } else {
-            // earlier work on this stream may still read the old buffer
-            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(s.ptr) != hipSuccess) {
-                (void)hipGetLastError();
-                return nullptr;
-            }
-        }
-        s.ptr = nullptr;
-        s.bytes = 0;
-        s.captured = false;
-    }
-    const size_t want = (size_t)round_up((int64_t)(bytes + bytes / 4), int64_t(1) << 21);
-    void *ptr = nullptr;
-    if (hipMalloc(&ptr, want) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    s.ptr = ptr;
-    s.bytes = want;
-    return ptr;
-}
-
-// Runs the plan: copies, then the direct kernel on them.  TG_ERROR_UNSUPPORTED
-// when no scratch can be had (the caller then runs the problem unpacked).
-tg_status run_packed(const PackPlan &plan, const Problem &p, int dev, hipStream_t stream)
-{
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    char *buf = static_cast<char *>(scratch_for(dev, stream, plan.scratch));
-    if (buf == nullptr)
-        return TG_ERROR_UNSUPPORTED;
-    Problem kp = plan.kp;
-    tg::PackOperand ops[2];
-    int n = 0;
-    size_t at = 0;
-    for (int w = 0; w < 2; w++) {
-        if (!plan.pack[w])
-            continue;
-        ops[n] = plan.op[w];
-        ops[n].dst = buf + at;
-        (w == 0 ? kp.A : kp.B) = buf + at;
-        at += (size_t)round_up(plan.copy_bytes[w], 256);
-        n++;
-    }
-    (void)hipGetLastError();
-    if (tg::launch_pack(ops, n, stream) != hipSuccess)
-        return TG_ERROR_LAUNCH;
-    const KernelConfig &cfg = kConfigs[plan.id];
-    Params k;
-    tg_status st = make_params(cfg, kp, &k);
-    if (st != TG_SUCCESS)
-        return st;
-    k.a_bytes = (uint32_t)plan.range[0];
-    k.b_bytes = (uint32_t)plan.range[1];
-    (void)p;
-    return launch_config(plan.id, k, kp.c_dtype == TG_DTYPE_F16, kp.fused, stream);
-}
-
-tg_status run(int config_id, const Problem &p, hipStream_t stream)
-{
-    tg_status st = validate(p);
-    if (st != TG_SUCCESS)
-        return st;
-    if (config_id < -1 || config_id >= kNumConfigs)
-        return TG_ERROR_INVALID_VALUE;
-    if (p.M == 0 || p.N == 0)
-        return TG_SUCCESS;
-    const int id = config_id >= 0 ? config_id : choose(p);
-    const KernelConfig &cfg = kConfigs[id];
-    if (!supports(cfg, p))
-        return TG_ERROR_UNSUPPORTED;
-    int dev = 0;
-    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
-        return st;
-    PackPlan plan;
-    if (config_id < 0 && tuned_lookup(p) < 0 && plan_pack(p, &plan)) {
-        st = run_packed(plan, p, dev, stream);
-        if (st != TG_ERROR_UNSUPPORTED)
-            return st;
-    }
-    Params k;
-    if ((st = make_params(cfg, p, &k)) != TG_SUCCESS)
-        return st;
-    return launch_config(id, k, p.c_dtype == TG_DTYPE_F16, p.fused, stream);
 }
 
 // ---- split-K ------------------------------------------------------------------
@@ -875,6 +638,8 @@ constexpr double kReduceFixedUs = 4.5;
 constexpr double kReduceBytesPerUs = 4.5e6;
 constexpr double kSliceUs = 0.3;
 
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
 int64_t slice_k(int64_t K, int splits, int bk)
 {
     const int64_t per = (K + splits - 1) / splits;
@@ -883,6 +648,7 @@ int64_t slice_k(int64_t K, int splits, int bk)
 
 int64_t slice_count(int64_t K, int64_t k_split) { return k_split > 0 ? (K + k_split - 1) / k_split : 1; }
 
+// Workspace bytes of the slices' partial products (fp32 or int32, M x N each).
 int64_t partial_bytes(const Problem &p, int64_t slices) { return slices * p.M * p.N * 4; }
 
 double reduce_time(const Problem &p, int64_t slices)
@@ -917,14 +683,17 @@ struct SplitChoice {
 
 // Least predicted time over the modelled configurations that can run the
 // problem and the slice counts whose partials fit in ws_bytes; `only_id` /
-// `only_splits` restrict the search (-1 / 0: free).  Returns id -1 when no
-// modelled configuration applies.
-SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int only_splits)
+// `only_splits` restrict the search (-1 / 0: free), `direct_only` keeps the
+// direct-copy configurations only.  Returns id -1 when no modelled
+// configuration applies.
+SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int only_splits,
+                         bool direct_only = false)
 {
     const int pad = operands_aligned(p) ? 0 : 1;
     SplitChoice best{-1, 1, p.K, 0.0};
     for (const ModelRow &r : kModel) {
-        if ((only_id >= 0 && r.id != only_id) || !row_applies(r, p, pad))
+        if ((only_id >= 0 && r.id != only_id) || !row_applies(r, p, pad) ||
+            (direct_only && !kConfigs[r.id].direct))
             continue;
         const KernelConfig &c = kConfigs[r.id];
         auto consider = [&](int64_t slices, int64_t kk) {
@@ -946,7 +715,7 @@ SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int onl
         for (int i = 0; i < ncand; i++) {
             const int64_t kk = slice_k(p.K, cand[i], c.bk);
             const int64_t slices = slice_count(p.K, kk);
-            if (slices <= 1 || (size_t)partial_bytes(p, slices) > ws_bytes)
+            if (slices <= 1 || (uint64_t)partial_bytes(p, slices) > (uint64_t)ws_bytes)
                 continue;
             consider(slices, kk);
         }
@@ -954,65 +723,261 @@ SplitChoice choose_split(const Problem &p, size_t ws_bytes, int only_id, int onl
     return best;
 }
 
-tg_status run_split(int config_id, int splits, const Problem &p, void *ws, size_t ws_bytes,
-                    hipStream_t stream, int *chosen_id, int *chosen_slices, bool launch)
-{
-    tg_status st = validate(p);
-    if (st != TG_SUCCESS)
-        return st;
-    if (config_id < -1 || config_id >= kNumConfigs || splits < 0 || splits > kMaxSplits)
-        return TG_ERROR_INVALID_VALUE;
-    if (p.M == 0 || p.N == 0) {
-        if (chosen_id)
-            *chosen_id = -1;
-        if (chosen_slices)
-            *chosen_slices = 1;
-        return TG_SUCCESS;
-    }
-    if (config_id >= 0 && !supports(kConfigs[config_id], p))
-        return TG_ERROR_UNSUPPORTED;
-    int id = config_id;
-    int64_t slices = 1, k_split = p.K;
-    if (splits == 0 && p.K > 0) {
-        // the dispatcher's choice, K slicing included; exact records of the
-        // tuning cache and compiled table still decide an unsliced call
-        const SplitChoice sc = choose_split(p, ws ? ws_bytes : 0, config_id, 0);
-        if (sc.id >= 0) {
-            id = sc.id;
-            slices = sc.slices;
-            k_split = sc.k_split;
-        }
-        if (slices <= 1 && config_id < 0)
-            id = choose(p);
-    } else if (splits > 1 && p.K > 0) {
-        if (id < 0) {
-            const SplitChoice sc = choose_split(p, SIZE_MAX, -1, splits);
-            id = sc.id >= 0 ? sc.id : choose(p);
-        }
-        k_split = slice_k(p.K, splits, kConfigs[id].bk);
-        slices = slice_count(p.K, k_split);
-    }
-    if (id < 0)
-        id = choose(p);
-    if (chosen_id)
-        *chosen_id = id;
-    if (chosen_slices)
-        *chosen_slices = (int)slices;
-    if (!launch)
-        return TG_SUCCESS;
-    if (slices <= 1)
-        return run(id, p, stream);
+// ---- packed operands -----------------------------------------------------------
+// An operand the direct global->LDS copies cannot take (base not 16-byte
+// aligned, or leading dimension or row length not a multiple of 16 bytes) is
+// otherwise served by the register-staged kernels, which hide less memory
+// latency.  With a workspace the dispatcher may instead copy it there first,
+// in a packed layout: the same stored rows, each padded with zeros to a
+// multiple of 16 bytes, which is also the copy's leading dimension
+// (tg_pack.hip).  The direct kernel then runs on the copy; the kernel's K is K
+// rounded up to a whole 16-byte chunk (the padding holds zeros, and the rows
+// past K of an operand whose rows run along K lie past its copy range, which
+// reads zeros).  Copy time: a fixed part (the extra launch) and the bytes read
+// and written at an effective rate; fitted to on-device traces of the copy
+// kernel for copies of 0.5 MB .. 0.5 GB (3.4 us + bytes / 6.1e6 per us),
+// rounded up.
+constexpr double kPackFixedUs = 4.0;
+constexpr double kPackBytesPerUs = 5.5e6;
 
-    const KernelConfig &cfg = kConfigs[id];
-    if (ws == nullptr || !aligned(ws, 16) || (size_t)partial_bytes(p, slices) > ws_bytes)
-        return TG_ERROR_INVALID_VALUE;
-    int dev = 0;
-    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS ||
-        (st = check_pointer(ws, dev)) != TG_SUCCESS)
-        return st;
+bool operand_direct_layout(const Problem &p, bool is_a)
+{
+    const void *ptr = is_a ? p.A : p.B;
+    const OperandShape o = is_a ? OperandShape{p.op_a == 0, p.M, p.lda, 0}
+                                : OperandShape{p.op_b == 1, p.N, p.ldb, 0};
+    return aligned(ptr, 16) && chunks_aligned(o, p);
+}
+
+// What one call runs: configuration `id` on the problem `kp` (p itself, or p
+// with packed copies of some operands), unsliced or in `slices` K slices.
+// Workspace layout: the packed copies first (each rounded up to 256 bytes),
+// then the slices' partial products.
+struct Plan {
+    int id = -1;
+    int64_t slices = 1, k_split = 0;
+    bool pack[2] = {false, false};
+    tg::PackOperand op[2] = {};        // the copies (src set, dst set at run time)
+    int64_t copy_bytes[2] = {0, 0};
+    int64_t range[2] = {0, 0};         // buffer ranges of the kernel's operands when packing
+    Problem kp{};                      // the problem the kernel sees (copy pointers at run time)
+    size_t pack_bytes = 0;             // workspace of the copies
+    size_t part_bytes = 0;             // workspace of the partial products
+    double t = 0.0;                    // modelled time (0 when not modelled)
+    size_t ws_used() const { return pack_bytes + part_bytes; }
+};
+
+// Packed geometry of p: which operands are copied, the copies' sizes and the
+// problem the direct kernel sees (`chk`: the same with stand-in 16-byte
+// aligned addresses for the eligibility checks).  False when a copy would
+// span 2 GiB or more, or the copies still do not suit the direct kernels.
+bool pack_geometry(const Problem &p, Plan *pl, Problem *chk)
+{
+    const int64_t es = elem_size(p), ce = 16 / es;
+    pl->pack[0] = !operand_direct_layout(p, true);
+    pl->pack[1] = !operand_direct_layout(p, false);
+    Problem kp = p;
+    kp.K = round_up(p.K, ce);
+    *chk = kp;
+    for (int w = 0; w < 2; w++) {
+        const bool is_a = w == 0;
+        const bool kmaj = is_a ? p.op_a == 0 : p.op_b == 1;
+        const int64_t rows = is_a ? a_rows(p) : b_rows(p);
+        const int64_t cols = is_a ? a_cols(p) : b_cols(p);
+        const int64_t ld = is_a ? p.lda : p.ldb;
+        if (!pl->pack[w]) {
+            // unpacked: its own rows; an operand whose rows run along K keeps
+            // its K rows in range, so the kernel's extra K rows read zeros
+            pl->range[w] = es * span_elems(rows, cols, ld);
+            continue;
+        }
+        const int64_t cols_p = round_up(cols, ce);
+        const int64_t copy = rows * cols_p * es;
+        if (copy >= kMaxSpan)
+            return false;
+        pl->op[w] = tg::PackOperand{is_a ? p.A : p.B, nullptr, rows, cols, ld, cols_p, (int)es};
+        pl->copy_bytes[w] = copy;
+        pl->range[w] = copy;
+        pl->pack_bytes += (size_t)round_up(copy, 256);
+        if (is_a) {
+            kp.lda = cols_p;
+            chk->lda = cols_p;
+            if (!kmaj)
+                chk->M = cols_p;
+        } else {
+            kp.ldb = cols_p;
+            chk->ldb = cols_p;
+            if (!kmaj)
+                chk->N = cols_p;
+        }
+    }
+    chk->A = pl->pack[0] ? reinterpret_cast<const void *>(uintptr_t(256)) : p.A;
+    chk->B = pl->pack[1] ? reinterpret_cast<const void *>(uintptr_t(512)) : p.B;
+    chk->K = kp.K;
+    pl->kp = kp;
+    return operands_aligned(*chk);
+}
+
+double pack_time(const Plan &pl, const Problem &p)
+{
+    const int64_t es = elem_size(p);
+    double bytes = 0.0;
+    for (int w = 0; w < 2; w++)
+        if (pl.pack[w])
+            bytes += (double)(es * span_elems(w ? b_rows(p) : a_rows(p), w ? b_cols(p) : a_cols(p),
+                                              w ? p.ldb : p.lda) +
+                              pl.copy_bytes[w]);
+    return kPackFixedUs + bytes / kPackBytesPerUs;
+}
+
+// The slice count of a plan on problem q (the operands as passed, or their
+// packed copies) for configuration id (-1: the dispatcher's) with ws_bytes of
+// workspace left: splits 0 = the modelled choice among 1 and the slice counts
+// whose partials fit; 1 = unsliced; n > 1 = n slices.
+void plan_slices(Plan *pl, const Problem &q, int id, int splits, size_t ws_bytes)
+{
+    pl->slices = 1;
+    pl->k_split = q.K;
+    if (splits == 0 && q.K > 0 && ws_bytes > 0) {
+        // exact records of the tuning cache and compiled table still decide
+        // an unsliced call of the dispatcher
+        const SplitChoice sc = choose_split(q, ws_bytes, id, 0);
+        if (sc.id >= 0) {
+            pl->id = sc.id;
+            pl->slices = sc.slices;
+            pl->k_split = sc.k_split;
+            pl->t = sc.t;
+        }
+        if (pl->slices <= 1)
+            pl->id = id >= 0 ? id : choose(q);
+    } else if (splits > 1 && q.K > 0) {
+        if (id < 0) {
+            const SplitChoice sc = choose_split(q, SIZE_MAX, -1, splits);
+            id = sc.id >= 0 ? sc.id : choose(q);
+        }
+        pl->id = id;
+        pl->k_split = slice_k(q.K, splits, kConfigs[id].bk);
+        pl->slices = slice_count(q.K, pl->k_split);
+    } else {
+        pl->id = id >= 0 ? id : choose(q);
+    }
+    pl->part_bytes = pl->slices > 1 ? (size_t)partial_bytes(q, pl->slices) : 0;
+}
+
+// The plan of a call without workspace, or of one that names its
+// configuration or slice count (config_id -1: the dispatcher's
+// configuration).  No copies, except that a named direct configuration that
+// cannot take an operand as passed runs on packed copies of the operands
+// that need it, when ws_bytes holds them.
+tg_status plan_fixed(const Problem &p, int config_id, int splits, size_t ws_bytes, Plan *out)
+{
+    Plan pl;
+    pl.kp = p;
+    if (config_id >= 0 && !supports(kConfigs[config_id], p)) {
+        Problem chk;
+        if (!kConfigs[config_id].direct || ws_bytes == 0 || !pack_geometry(p, &pl, &chk) ||
+            !supports(kConfigs[config_id], chk))
+            return TG_ERROR_UNSUPPORTED;
+        if (pl.pack_bytes > ws_bytes)
+            return TG_ERROR_WORKSPACE;
+        plan_slices(&pl, chk, config_id, splits, ws_bytes - pl.pack_bytes);
+        // partials of the real output (chk's M or N may be rounded up to the
+        // copy's row length, so the fit was checked conservatively)
+        pl.part_bytes = pl.slices > 1 ? (size_t)partial_bytes(p, pl.slices) : 0;
+        *out = pl;
+        return TG_SUCCESS;
+    }
+    plan_slices(&pl, p, config_id, splits, ws_bytes);
+    *out = pl;
+    return TG_SUCCESS;
+}
+
+// The dispatcher's plan with a workspace of ws_bytes: the fastest modelled of
+// (a) the operands as passed, unsliced or in K slices whose partials fit, and
+// (b) packed copies of the operands that rule out the direct copies, then a
+// direct configuration on them, unsliced or sliced, copies and partials
+// together within ws_bytes.  A tuning-cache record for the exact problem is
+// run as recorded (unpacked, unsliced).
+Plan plan_auto(const Problem &p, size_t ws_bytes)
+{
+    Plan base;
+    const int tuned = tuned_lookup(p);
+    if (tuned >= 0 && supports(kConfigs[tuned], p)) {
+        base.id = tuned;
+        base.kp = p;
+        base.k_split = p.K;
+        return base;
+    }
+    plan_fixed(p, -1, 0, ws_bytes, &base);
+    if (p.K == 0 || operands_aligned(p))
+        return base;
+    double t_base = base.t;
+    if (base.t == 0.0 && model_lookup(p, &t_base) < 0)
+        return base;   // nothing modelled to compare with
+    Plan pk;
+    Problem chk;
+    if (!pack_geometry(p, &pk, &chk) || pk.pack_bytes > ws_bytes)
+        return base;
+    const SplitChoice sc = choose_split(chk, ws_bytes - pk.pack_bytes, -1, 0, true);
+    if (sc.id < 0)
+        return base;
+    pk.id = sc.id;
+    pk.slices = sc.slices;
+    pk.k_split = sc.k_split;
+    if (sc.slices <= 1) {
+        // a measured exact-shape record for the copies' problem overrides the
+        // model's kernel (the predicted time still decides whether to pack)
+        if (elem_size(p) == 2) {
+            const int exact = dispatch_exact(chk.M, chk.N, chk.K, chk.fused);
+            if (exact >= 0 && kConfigs[exact].direct && supports(kConfigs[exact], chk))
+                pk.id = exact;
+        }
+    } else {
+        pk.part_bytes = (size_t)partial_bytes(p, sc.slices);
+    }
+    pk.t = sc.t + pack_time(pk, p);
+    return pk.t < t_base ? pk : base;
+}
+
+// ---- launches -------------------------------------------------------------------
+// Runs the plan: the copies into the workspace, then the kernel on the
+// problem it sees -- into C, or into the workspace's partial products
+// followed by their reduction into C.  The workspace has been checked.
+tg_status execute(const Plan &pl, const Problem &p, char *ws, hipStream_t stream)
+{
+    Problem kp = pl.kp;
+    const bool packed = pl.pack[0] || pl.pack[1];
+    if (packed) {
+        tg::PackOperand ops[2];
+        int n = 0;
+        size_t at = 0;
+        for (int w = 0; w < 2; w++) {
+            if (!pl.pack[w])
+                continue;
+            ops[n] = pl.op[w];
+            ops[n].dst = ws + at;
+            (w == 0 ? kp.A : kp.B) = ws + at;
+            at += (size_t)round_up(pl.copy_bytes[w], 256);
+            n++;
+        }
+        (void)hipGetLastError();
+        if (tg::launch_pack(ops, n, stream) != hipSuccess)
+            return TG_ERROR_LAUNCH;
+    }
+    const KernelConfig &cfg = kConfigs[pl.id];
+    tg_status st;
+    if (pl.slices <= 1) {
+        Params k;
+        if ((st = make_params(cfg, kp, &k)) != TG_SUCCESS)
+            return st;
+        if (packed) {
+            k.a_bytes = (uint32_t)pl.range[0];
+            k.b_bytes = (uint32_t)pl.range[1];
+        }
+        return launch_config(pl.id, k, kp.c_dtype == TG_DTYPE_F16, kp.fused, stream);
+    }
     // the slices' partial products: M x N, leading dimension N, fp32 (int32)
-    Problem part = p;
-    part.C = ws;
+    Problem part = kp;
+    part.C = ws + pl.pack_bytes;
     part.ldc = p.N;
     part.bias = nullptr;
     part.fused = false;
@@ -1020,20 +985,24 @@ tg_status run_split(int config_id, int splits, const Problem &p, void *ws, size_
     Params k;
     if ((st = make_params(cfg, part, &k)) != TG_SUCCESS)
         return st;
-    k.splits = (int)slices;
-    k.k_split = (int)k_split;
+    if (packed) {
+        k.a_bytes = (uint32_t)pl.range[0];
+        k.b_bytes = (uint32_t)pl.range[1];
+    }
+    k.splits = (int)pl.slices;
+    k.k_split = (int)pl.k_split;
     k.c_slice_bytes = p.M * p.N * 4;
-    if ((st = launch_config(id, k, false, false, stream)) != TG_SUCCESS)
+    if ((st = launch_config(pl.id, k, false, false, stream)) != TG_SUCCESS)
         return st;
     tg::ReduceParams r;
-    r.ws = ws;
+    r.ws = part.C;
     r.slice_elems = p.M * p.N;
     r.bias = p.fused ? p.bias : nullptr;
     r.C = p.C;
     r.M = (int)p.M;
     r.N = (int)p.N;
     r.ldc = (int)p.ldc;
-    r.splits = (int)slices;
+    r.splits = (int)pl.slices;
     r.vec_ws = p.N % 4 == 0;
     const int c_elem = p.c_dtype == TG_DTYPE_F16 ? 2 : 4;
     r.vec_c = p.ldc % 4 == 0 && aligned(p.C, 4 * c_elem);
@@ -1041,6 +1010,67 @@ tg_status run_split(int config_id, int splits, const Problem &p, void *ws, size_
                              : p.c_dtype == TG_DTYPE_F32 ? tg::kOutF32
                                                          : tg::kOutI32;
     return tg::launch_splitk_reduce(r, kind, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
+}
+
+// A call without workspace: tg_gemm, tg_gemm_bias_relu, tg_gemm_ex (config_id
+// -1) and tg_gemm_with_config.
+tg_status run(int config_id, const Problem &p, hipStream_t stream)
+{
+    tg_status st = validate(p);
+    if (st != TG_SUCCESS)
+        return st;
+    if (config_id < -1 || config_id >= kNumConfigs)
+        return TG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0)
+        return TG_SUCCESS;
+    Plan pl;
+    if ((st = plan_fixed(p, config_id, 1, 0, &pl)) != TG_SUCCESS)
+        return st;
+    if (!supports(kConfigs[pl.id], p))
+        return TG_ERROR_UNSUPPORTED;
+    int dev = 0;
+    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
+        return st;
+    return execute(pl, p, nullptr, stream);
+}
+
+// The plan of a workspace call (tg_gemm_ws, tg_select_plan): validation and
+// the choice, no device calls.
+tg_status plan_ws(const Problem &p, int config_id, int splits, size_t ws_bytes, Plan *pl)
+{
+    tg_status st = validate(p);
+    if (st != TG_SUCCESS)
+        return st;
+    if (config_id < -1 || config_id >= kNumConfigs || splits < 0 || splits > kMaxSplits)
+        return TG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0) {
+        *pl = Plan{};
+        return TG_SUCCESS;
+    }
+    if (config_id < 0 && splits == 0)
+        *pl = plan_auto(p, ws_bytes);
+    else if ((st = plan_fixed(p, config_id, splits, ws_bytes, pl)) != TG_SUCCESS)
+        return st;
+    return pl->ws_used() > ws_bytes ? TG_ERROR_WORKSPACE : TG_SUCCESS;
+}
+
+// A workspace call: ws of ws_bytes bytes (device memory of the current device,
+// 16-byte aligned) or NULL with ws_bytes == 0.
+tg_status run_ws(int config_id, int splits, const Problem &p, void *ws, size_t ws_bytes,
+                 hipStream_t stream)
+{
+    if ((ws == nullptr && ws_bytes != 0) || !aligned(ws, 16))
+        return TG_ERROR_INVALID_VALUE;
+    Plan pl;
+    tg_status st = plan_ws(p, config_id, splits, ws_bytes, &pl);
+    if (st != TG_SUCCESS || p.M == 0 || p.N == 0)
+        return st;
+    int dev = 0;
+    if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
+        return st;
+    if (pl.ws_used() > 0 && (st = check_span(ws, pl.ws_used(), dev)) != TG_SUCCESS)
+        return st;
+    return execute(pl, p, static_cast<char *>(ws), stream);
 }
 
 // ---- attention ----------------------------------------------------------------
@@ -1128,10 +1158,15 @@ tg_status tg_attention_fwd(const void *Q, const void *K, const void *V, void *O,
     int dev = 0;
     if ((st = check_device(&dev)) != TG_SUCCESS)
         return st;
-    if ((st = check_pointer(Q, dev)) != TG_SUCCESS || (st = check_pointer(O, dev)) != TG_SUCCESS ||
-        (Lk > 0 && ((st = check_pointer(K, dev)) != TG_SUCCESS ||
-                    (st = check_pointer(V, dev)) != TG_SUCCESS)) ||
-        (st = check_pointer(lse, dev)) != TG_SUCCESS)
+    // every element read or written lies inside its allocation
+    auto extent = [d](const int64_t *s, int64_t b, int64_t h, int64_t l) {
+        return 2 * (uint64_t)((b - 1) * s[0] + (h - 1) * s[1] + (l - 1) * s[2] + d);
+    };
+    if ((st = check_span(Q, extent(q_strides, B, H, Lq), dev)) != TG_SUCCESS ||
+        (st = check_span(O, extent(o_strides, B, H, Lq), dev)) != TG_SUCCESS ||
+        (Lk > 0 && ((st = check_span(K, extent(k_strides, B, Hkv, Lk), dev)) != TG_SUCCESS ||
+                    (st = check_span(V, extent(v_strides, B, Hkv, Lk), dev)) != TG_SUCCESS)) ||
+        (st = check_span(lse, 4 * (uint64_t)(B * H * Lq), dev)) != TG_SUCCESS)
         return st;
     (void)hipGetLastError();
     return tg::launch_attention(a, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
@@ -1184,6 +1219,7 @@ const char *tg_status_string(tg_status s)
     case TG_ERROR_UNSUPPORTED: return "TG_ERROR_UNSUPPORTED: device or problem not supported";
     case TG_ERROR_LAUNCH: return "TG_ERROR_LAUNCH: kernel launch failed";
     case TG_ERROR_FILE: return "TG_ERROR_FILE: file cannot be opened or read";
+    case TG_ERROR_WORKSPACE: return "TG_ERROR_WORKSPACE: the plan needs more workspace than the call provides";
     }
     return "unknown tg_status";
 }
@@ -1220,85 +1256,6 @@ int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void
     if (id < 0 || id >= kNumConfigs || validate(p) != TG_SUCCESS)
         return -1;
     return supports(kConfigs[id], p) ? 1 : 0;
-}
-
-tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
-                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
-                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                         int *config_id, int *packed, size_t *scratch_bytes)
-{
-    if (config_id == nullptr || packed == nullptr || scratch_bytes == nullptr)
-        return TG_ERROR_INVALID_VALUE;
-    *config_id = -1;
-    *packed = 0;
-    *scratch_bytes = 0;
-    Problem p{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
-              op_a, op_b};
-    const tg_status st = validate(p);
-    if (st != TG_SUCCESS)
-        return st;
-    if (M == 0 || N == 0)
-        return TG_SUCCESS;
-    PackPlan plan;
-    if (tuned_lookup(p) < 0 && plan_pack(p, &plan)) {
-        *config_id = plan.id;
-        *packed = (plan.pack[0] ? 1 : 0) | (plan.pack[1] ? 2 : 0);
-        *scratch_bytes = plan.scratch;
-        return TG_SUCCESS;
-    }
-    *config_id = choose(p);
-    return TG_SUCCESS;
-}
-
-tg_status tg_scratch_release(void)
-{
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    std::vector<Retired> all = g_retired;
-    for (const auto &e : g_scratch)
-        if (e.second.ptr != nullptr)
-            all.push_back(Retired{e.first.first, e.second.ptr, e.second.bytes});
-    g_scratch.clear();
-    g_retired.clear();
-    tg_status st = TG_SUCCESS;
-    int cur = 0;
-    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-    std::vector<int> synced;
-    for (const Retired &r : all) {
-        bool done = false;
-        for (int d : synced)
-            done = done || d == r.dev;
-        if (!done) {
-            if (hipSetDevice(r.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-                st = TG_ERROR_LAUNCH;
-            synced.push_back(r.dev);
-        }
-        if (hipFree(r.ptr) != hipSuccess)
-            st = TG_ERROR_LAUNCH;
-    }
-    if (have_cur)
-        (void)hipSetDevice(cur);
-    (void)hipGetLastError();
-    return st;
-}
-
-int tg_set_pack_policy(int policy)
-{
-    if (policy != TG_PACK_AUTO && policy != TG_PACK_NEVER && policy != TG_PACK_ALWAYS)
-        return -1;
-    const int prev = pack_policy();
-    g_pack_policy.store(policy, std::memory_order_relaxed);
-    return prev;
-}
-
-size_t tg_scratch_held(void)
-{
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    size_t n = 0;
-    for (const auto &e : g_scratch)
-        n += e.second.bytes;
-    for (const Retired &r : g_retired)
-        n += r.bytes;
-    return n;
 }
 
 int tg_select_config(tg_op op_a, tg_op op_b, const void *A, const void *B, const float *bias,
@@ -1348,28 +1305,40 @@ size_t tg_splitk_workspace_bytes(int64_t M, int64_t N, int splits)
     return (size_t)splits * (size_t)M * (size_t)N * 4;
 }
 
-tg_status tg_gemm_splitk(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
-                         const void *B, const float *bias, void *C, int64_t M, int64_t N,
-                         int64_t K, int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+tg_status tg_gemm_ws(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
+                     const void *B, const float *bias, void *C, int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream)
 {
-    return run_split(config_id, splits,
-                     Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr,
-                             op_a, op_b},
-                     workspace, workspace_bytes, stream, nullptr, nullptr, true);
+    return run_ws(config_id, splits,
+                  Problem{A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype, bias != nullptr, op_a,
+                          op_b},
+                  workspace, workspace_bytes, stream);
 }
 
-tg_status tg_select_splitk(tg_op op_a, tg_op op_b, const void *A, const void *B,
-                           const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
-                           int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
-                           size_t workspace_bytes, int *config_id, int *splits)
+tg_status tg_select_plan(tg_op op_a, tg_op op_b, const void *A, const void *B,
+                         const float *bias, const void *C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                         size_t workspace_bytes, int *config_id, int *splits, int *packed,
+                         size_t *workspace_used)
 {
-    // a stand-in workspace address: the choice depends only on its size
-    void *ws = workspace_bytes ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
-    return run_split(-1, 0,
-                     Problem{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb, ldc, c_dtype,
-                             bias != nullptr, op_a, op_b},
-                     ws, workspace_bytes, nullptr, config_id, splits, false);
+    if (config_id == nullptr || splits == nullptr || packed == nullptr || workspace_used == nullptr)
+        return TG_ERROR_INVALID_VALUE;
+    *config_id = -1;
+    *splits = 1;
+    *packed = 0;
+    *workspace_used = 0;
+    Plan pl;
+    const tg_status st = plan_ws(Problem{A, B, bias, const_cast<void *>(C), M, N, K, lda, ldb,
+                                         ldc, c_dtype, bias != nullptr, op_a, op_b},
+                                 -1, 0, workspace_bytes, &pl);
+    if (st != TG_SUCCESS)
+        return st;
+    *config_id = pl.id;
+    *splits = (int)pl.slices;
+    *packed = (pl.pack[0] ? 1 : 0) | (pl.pack[1] ? 2 : 0);
+    *workspace_used = pl.ws_used();
+    return TG_SUCCESS;
 }
 
 tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t iters,
@@ -1381,30 +1350,15 @@ tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t i
         iters > (int64_t(1) << 30) || (iters & 1) || workgroups < 1 ||
         workgroups > (int64_t(1) << 20) || iters * workgroups > (int64_t(1) << 32))
         return TG_ERROR_INVALID_VALUE;
-    int dev = 0;
-    tg_status st;
-    if ((st = check_device(&dev)) != TG_SUCCESS || (st = check_pointer(operands, dev)) != TG_SUCCESS ||
-        (st = check_pointer(sink, dev)) != TG_SUCCESS)
-        return st;
-    // both buffers must lie inside their allocations
-    const struct {
-        const void *p;
-        size_t bytes;
-    } spans[2] = {{operands, (size_t)TG_CEILING_OPERAND_BYTES},
-                  {sink, (size_t)workgroups * 256 * sizeof(float)}};
-    for (const auto &sp : spans) {
-        hipDeviceptr_t base = nullptr;
-        size_t size = 0;
-        if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)sp.p) != hipSuccess) {
-            (void)hipGetLastError();
-            return TG_ERROR_NOT_DEVICE_MEMORY;
-        }
-        const uintptr_t lo = (uintptr_t)base, at = (uintptr_t)sp.p;
-        if (at < lo || at - lo > size || size - (at - lo) < sp.bytes)
-            return TG_ERROR_INVALID_VALUE;
-    }
     if (!aligned(operands, 16) || !aligned(sink, 4))
         return TG_ERROR_INVALID_VALUE;
+    int dev = 0;
+    tg_status st;
+    // both buffers must lie inside their allocations
+    if ((st = check_device(&dev)) != TG_SUCCESS ||
+        (st = check_span(operands, TG_CEILING_OPERAND_BYTES, dev)) != TG_SUCCESS ||
+        (st = check_span(sink, (uint64_t)workgroups * 256 * sizeof(float), dev)) != TG_SUCCESS)
+        return st;
     (void)hipGetLastError();
     return tg::launch_mfma_ceiling(mfma, operands, sink, (int)iters, (int)workgroups, stream) ==
                    hipSuccess
@@ -1412,6 +1366,6 @@ tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t i
                : TG_ERROR_LAUNCH;
 }
 
-const char *tg_version(void) { return "tg 0.4.0 (gfx950)"; }
+const char *tg_version(void) { return "tg 0.5.0 (gfx950)"; }
 
 }  // extern "C"

@@ -146,6 +146,7 @@ struct AttnParams {
     uint32_t k_bytes, v_bytes;  // descriptor range of one head's K / V rows
     float scale_log2;           // |scale| * log2(e)
     int negate_q;               // scale < 0: Q is negated on load
+    int zero_q;                 // scale == 0: Q is read as zeros (uniform weights)
     int nqb;                    // query blocks per head
     int causal;
 };
@@ -217,11 +218,12 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         const bool ok = query < p.Lq;
         const _Float16 *qrow = p.Q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? query : 0) * p.qs[2];
         // a negative scale is applied as |scale| to -Q (negation is exact), so
-        // that the scores are always scaled by a non-negative factor
+        // that the scores are always scaled by a positive factor; a zero scale
+        // as the factor 1 on a zero Q, so every visible score is exactly 0
 #pragma unroll
         for (int ks = 0; ks < T::DK; ks++) {
             const half8 v = *(const half8 *)(qrow + 16 * ks + 8 * h);
-            qf[ks] = ok ? (p.negate_q ? -v : v) : half8{};
+            qf[ks] = ok && !p.zero_q ? (p.negate_q ? -v : v) : half8{};
         }
     }
 
@@ -444,13 +446,15 @@ hipError_t launch_attention(const AttentionArgs &a, hipStream_t s)
     }
     p.k_bytes = a.k_bytes;
     p.v_bytes = a.v_bytes;
-    // The kernel scales raw scores by this factor inside the exponent, with
-    // -inf for masked keys; a zero scale (uniform weights) becomes 1e-30,
-    // which keeps -inf * factor = -inf and changes a weight by a relative
-    // 1e-30 |s| at most.
-    p.scale_log2 = fabsf(a.scale) * 1.4426950408889634f;
-    if (p.scale_log2 < 1e-30f)
-        p.scale_log2 = 1e-30f;
+    // The kernel scales raw scores by this positive factor inside the
+    // exponent, with -inf for masked keys.  A scale of magnitude below 2^-100
+    // (zero included) makes every weight exp(scale (s_j - s_max)) round to
+    // exactly 1 in fp32 for any fp16 scores: that case runs with Q read as
+    // zeros and the factor log2(e), whose scores are exactly 0 -- the uniform
+    // weights, computed exactly (a zero factor would turn -inf into NaN).
+    const float mag = fabsf(a.scale);
+    p.zero_q = mag < 0x1p-100f;
+    p.scale_log2 = (p.zero_q ? 1.f : mag) * 1.4426950408889634f;
     p.negate_q = a.scale < 0.f;
     p.nqb = (a.Lq + attn::BQ - 1) / attn::BQ;
     p.causal = a.causal;

@@ -500,8 +500,11 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
 // LDS read as dependent on the copy (it would wait for all outstanding copies
 // before each one); the kernels wait on vmcnt themselves, before the barrier
 // that publishes a stage.  M0 is written here and nowhere else in these
-// kernels (the build checks the device assembly for that).  A scalar write of
-// M0 needs one wait state before a load that uses it as the LDS address.
+// kernels; the compiler reserves M0 and is not told of the write (a clobber
+// of a reserved register is not honoured), so tests/test_device_asm_cpu.py
+// checks the device assembly of every kernel for any other M0 use.  A scalar
+// write of M0 needs one wait state before a load that uses it as the LDS
+// address.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"

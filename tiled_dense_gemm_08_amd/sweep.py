@@ -27,8 +27,8 @@ transpose) and leading dimensions of A and B one element wider than stored
     python -m tiled_dense_gemm_08_amd.sweep --grid --out grid.csv [--unaligned]
     python -m tiled_dense_gemm_08_amd.costmodel grid.csv grid_pad.csv --emit
 
-    # time the dispatcher's own call (tg_gemm_ex), copies of packed operands
-    # included; TG_PACK=always|never|auto sets the pack policy
+    # time the dispatcher's own call with a workspace (tg_gemm_ws: copies of
+    # packed operands and K slices included) and without one (tg_gemm_ex)
     python -m tiled_dense_gemm_08_amd.sweep --dispatch --shape 3001x5003x1031:f32:pad
 
 Timing: `reps` launches are captured into one HIP graph which is replayed, so
@@ -188,21 +188,26 @@ def time_config(cid, sh, bufs, reps, timing="graph"):
 
 
 def time_dispatch(sh, bufs, reps, timing="graph"):
-    """Average milliseconds per dispatcher call (tg_gemm_ex: the library's own
-    choice, copies of packed operands included) and the plan it reports."""
+    """Average milliseconds per dispatcher call with a workspace (tg_gemm_ws:
+    the library's own plan, copies of packed operands and K slices included),
+    the plan it reports, and the milliseconds of the call without one
+    (tg_gemm_ex)."""
     args = _args(sh, bufs)
     plan = tg.tg_select_plan(*args, op_a=sh.op_a, op_b=sh.op_b)
-    ms = time_launch(lambda s: tg.tg_gemm_ex(sh.op_a, sh.op_b, *args, s), reps, timing)
-    return ms, plan
+    ws = torch.empty(max(plan[4], 16) // 4 + 4, dtype=torch.float32, device="cuda")
+    ms = time_launch(lambda s: tg.tg_gemm_ws(-1, 0, *args, ws.data_ptr(), plan[4], s,
+                                             op_a=sh.op_a, op_b=sh.op_b), reps, timing)
+    plain = time_launch(lambda s: tg.tg_gemm_ex(sh.op_a, sh.op_b, *args, s), reps, timing)
+    return ms, plan, plain
 
 
 def time_split(cid, splits, sh, bufs, ws, reps, timing="graph"):
-    """Average milliseconds per tg_gemm_splitk call (cid -1 / splits 0: the
+    """Average milliseconds per tg_gemm_ws call (cid -1 / splits 0: the
     dispatcher's choice) with workspace tensor ws."""
     args = _args(sh, bufs)
     nbytes = ws.numel() * ws.element_size()
-    return time_launch(lambda s: tg.tg_gemm_splitk(cid, splits, *args, ws.data_ptr(), nbytes, s,
-                                                   op_a=sh.op_a, op_b=sh.op_b), reps, timing)
+    return time_launch(lambda s: tg.tg_gemm_ws(cid, splits, *args, ws.data_ptr(), nbytes, s,
+                                               op_a=sh.op_a, op_b=sh.op_b), reps, timing)
 
 
 def search_splits(sh, config_ids, split_counts, reps, timing):
@@ -228,7 +233,7 @@ def search_splits(sh, config_ids, split_counts, reps, timing):
             out[(c, slices)] = time_split(c, sp, sh, bufs, ws, reps, timing)
     a = _args(sh, bufs)
     nbytes = ws.numel() * ws.element_size()
-    st, cid, sl = tg.tg_select_splitk(*a, nbytes, op_a=sh.op_a, op_b=sh.op_b)
+    st, cid, sl, _, _ = tg.tg_select_plan(*a, nbytes, op_a=sh.op_a, op_b=sh.op_b)
     auto = (cid, sl, time_split(-1, 0, sh, bufs, ws, reps, timing))
     rec = {"shape": str(sh), "auto": list(auto[:2]), "auto_ms": round(auto[2], 5)}
     if out:   # none of the named configurations can run this shape: the dispatcher's call only
@@ -389,7 +394,8 @@ def main():
     ap.add_argument("--split-out", metavar="CSV", help="write the sliced timings to CSV")
     ap.add_argument("--out", metavar="CSV", help="write every timing to CSV")
     ap.add_argument("--dispatch", action="store_true",
-                    help="time the dispatcher's own call for each --shape (with TG_PACK)")
+                    help="time the dispatcher's own call for each --shape, with and without "
+                         "a workspace")
     a = ap.parse_args()
     ids = (list(range(tg.tg_num_configs())) if a.configs == "all"
            else [int(x) for x in a.configs.split(",")])
@@ -412,13 +418,15 @@ def main():
     if a.dispatch:
         for sh in shapes:
             bufs = Buffers(sh)
-            ms, (st, cid, packed, scratch) = time_dispatch(sh, bufs, a.reps, a.timing)
+            ms, (st, cid, slices, packed, used), plain = time_dispatch(sh, bufs, a.reps,
+                                                                      a.timing)
             flop = 2.0 * sh.M * sh.N * sh.K
             print(json.dumps({"shape": str(sh), "config": cid,
                               "name": tg.tg_config_info(cid)["name"] if cid >= 0 else None,
-                              "packed": packed, "scratch_bytes": scratch,
+                              "slices": slices, "packed": packed, "workspace_bytes": used,
                               "us": round(ms * 1e3, 2),
-                              "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}), flush=True)
+                              "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                              "us_without_workspace": round(plain * 1e3, 2)}), flush=True)
             del bufs
         return 0
     if a.splits:

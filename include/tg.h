@@ -180,6 +180,30 @@ tg_status tg_gemm_ws(int config_id, int splits, tg_op op_a, tg_op op_b, const vo
                      int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): tg_gemm_ws
+ * with the library's own workspace, a device array of TG_STATIC_SCRATCH_BYTES
+ * in place of the caller's, so the call allocates nothing and the caller
+ * passes only its inputs and outputs.  Each GPU the library runs on holds its
+ * own copy of the array until the process ends.  Arguments, plans and errors
+ * as tg_gemm_ws with workspace_bytes = TG_STATIC_SCRATCH_BYTES: the
+ * dispatcher's plans (config_id -1, splits 0) are those whose workspace fits
+ * the array, and a named plan that needs more is rejected with
+ * TG_ERROR_WORKSPACE before anything is launched.
+ * Every call on one GPU uses that GPU's single array: calls that overlap on
+ * one GPU (on different streams without ordering, or from several host
+ * threads on different streams) race and give wrong results; calls ordered on
+ * one stream do not.  The array keeps the last call's contents; every byte a
+ * call reads it has written first, so nothing needs clearing.
+ * TG_ERROR_UNSUPPORTED when there is no current device, TG_ERROR_LAUNCH when
+ * the runtime cannot give the array's device address. */
+#define TG_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+tg_status tg_gemm_ws_static(int config_id, int splits, tg_op op_a, tg_op op_b, const void *A,
+                            const void *B, const float *bias, void *C,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc, tg_dtype c_dtype,
+                            hipStream_t stream);
+
 /* Partial-product bytes of `splits` K slices: splits * M * N * 4 (0 if
  * splits <= 1 or M, N <= 0; 0 also for splits > 64, which the calls reject). */
 size_t tg_splitk_workspace_bytes(int64_t M, int64_t N, int splits);

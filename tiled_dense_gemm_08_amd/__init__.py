@@ -33,7 +33,7 @@ TG_OP_T = 1
 EXPORTED = ("tg_gemm", "tg_gemm_bias_relu", "tg_gemm_ex", "tg_status_string", "tg_num_configs",
             "tg_config_info", "tg_config_supports", "tg_select_config",
             "tg_gemm_with_config", "tg_tuning_load", "tg_tuning_clear", "tg_tuning_count",
-            "tg_splitk_workspace_bytes", "tg_gemm_ws", "tg_select_plan",
+            "tg_splitk_workspace_bytes", "tg_gemm_ws", "tg_gemm_ws_static", "tg_select_plan",
             "tg_attention_fwd", "tg_mfma_ceiling", "tg_version")
 
 
@@ -91,6 +91,8 @@ def _load():
     L.tg_splitk_workspace_bytes.restype = SZ
     L.tg_gemm_ws.argtypes = [I, I, I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P, SZ, P]
     L.tg_gemm_ws.restype = I
+    L.tg_gemm_ws_static.argtypes = [I, I, I, I, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P]
+    L.tg_gemm_ws_static.restype = I
     L.tg_select_plan.argtypes = [I, I] + shape_args + [SZ, IP, IP, IP, ctypes.POINTER(SZ)]
     L.tg_select_plan.restype = I
     L.tg_attention_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
@@ -168,6 +170,14 @@ def tg_gemm_ws(config_id, splits, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype
     return lib.tg_gemm_ws(config_id, splits, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb, ldc,
                           c_dtype, workspace, workspace_bytes, stream or None)
 
+
+def tg_gemm_ws_static(config_id, splits, A, B, bias, C, M, N, K, lda, ldb, ldc, c_dtype,
+                      stream=0, op_a=TG_OP_N, op_b=TG_OP_N):
+    return lib.tg_gemm_ws_static(config_id, splits, op_a, op_b, A, B, bias, C, M, N, K, lda, ldb,
+                                 ldc, c_dtype, stream or None)
+
+
+TG_STATIC_SCRATCH_BYTES = 64 << 20   # the library's workspace of tg_gemm_ws_static
 
 SIZE_MAX = ctypes.c_size_t(-1).value
 

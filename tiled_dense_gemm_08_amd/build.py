@@ -34,6 +34,7 @@ SHARDS = 8   # kernel compilations run in parallel (tg_kernels.hip, TG_SHARD=i)
 ATTN = os.path.join(CSRC, "tg_attention.hip")
 PACK = os.path.join(CSRC, "tg_pack.hip")
 CEILING = os.path.join(CSRC, "tg_ceiling.hip")
+STATIC = os.path.join(CSRC, "tg_static.hip")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 
@@ -82,7 +83,7 @@ def build_lib():
     api = os.path.join(BUILD_DIR, "tg_api.%s.o" % tag)
     objs.append(api)
     cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", api, os.path.join(CSRC, "tg_api.cpp")])
-    for src in (ATTN, PACK, CEILING):
+    for src in (ATTN, PACK, CEILING, STATIC):
         o = os.path.join(BUILD_DIR, "%s.%s.o" % (os.path.basename(src)[:-4], tag))
         objs.append(o)
         cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", o, src])
@@ -103,7 +104,7 @@ def device_asm(path=None):
     path = path or os.path.join(BUILD_DIR, "tg_kernels.s")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     kern = os.path.join(CSRC, "tg_kernels.hip")
-    extra = (ATTN, PACK, CEILING)
+    extra = (ATTN, PACK, CEILING, STATIC)
     parts = [path + ".%d" % i for i in range(SHARDS)] + [path + ".x%d" % i for i in range(len(extra))]
     _run_all([[HIPCC] + FLAGS + _shard_flags(i) + ["--cuda-device-only", "-S", "-o", parts[i], kern]
               for i in range(SHARDS)] +

@@ -64,16 +64,26 @@
 extern "C" {
 #endif
 
+/* The enumerations are int-sized.  Compiled as C++ they have int as their
+ * fixed underlying type, so that any int a caller passes is a valid value
+ * for the library to receive and reject (without a fixed type, a C++ enum
+ * holds only the values its enumerators' bits span). */
+#ifdef __cplusplus
+#define TG_ENUM(name) enum name : int
+#else
+#define TG_ENUM(name) enum name
+#endif
+
 /* Output type.  TG_DTYPE_I32 selects the int8 product: A and B then hold
  * int8 values and C = op(A).op(B) is accumulated and stored in int32 (exact:
  * K is limited to 131072 so that no partial sum leaves int32). */
-typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2, TG_DTYPE_I32 = 3 } tg_dtype;
+typedef TG_ENUM(tg_dtype_e) { TG_DTYPE_F16 = 1, TG_DTYPE_F32 = 2, TG_DTYPE_I32 = 3 } tg_dtype;
 
 /* Operand orientation for tg_gemm_ex: TG_OP_N uses the stored matrix as is,
  * TG_OP_T uses its transpose. */
-typedef enum { TG_OP_N = 0, TG_OP_T = 1 } tg_op;
+typedef TG_ENUM(tg_op_e) { TG_OP_N = 0, TG_OP_T = 1 } tg_op;
 
-typedef enum {
+typedef TG_ENUM(tg_status_e) {
     TG_SUCCESS = 0,
     TG_ERROR_INVALID_VALUE = 1,
     TG_ERROR_NOT_DEVICE_MEMORY = 2,

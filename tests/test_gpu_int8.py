@@ -125,17 +125,15 @@ def test_int8_padded_and_unaligned(op_a, op_b):
 
 
 @pytest.mark.parametrize("name", ["sq8192_i8", "sq8192_i8_nt"])
-def test_int8_large_sampled(name):
+def test_int8_large_every_output(name):
+    """8192^3 int8 through the dispatcher: every int32 output equal to the
+    exact oracle."""
     w = gen.workload(name)
     M, N, K = w["M"], w["N"], w["K"]
     out = run(w["A"], w["B"], M, N, K, w["op_a"], w["op_b"], what=name)
-    assert not np.any(out == UNWRITTEN)
-    rng = np.random.default_rng(31)
-    r = np.concatenate([rng.integers(0, M, 4000), [0, M - 1, 0, M - 1]])
-    c = np.concatenate([rng.integers(0, N, 4000), [0, 0, N - 1, N - 1]])
-    want = oracle.gemm_i8_entries(w["A"], w["B"], r, c, K, w["lda"], w["ldb"], op_a=w["op_a"],
-                                  op_b=w["op_b"])
-    check(out[r, c], want, name)
+    want = oracle.gemm_i8_ref(w["A"], w["B"], M, N, K, lda=w["lda"], ldb=w["ldb"],
+                              op_a=w["op_a"], op_b=w["op_b"])
+    check(out, want, name)
 
 
 def test_int8_K0_writes_zero():

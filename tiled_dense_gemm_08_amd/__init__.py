@@ -12,6 +12,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtg.so")
+# the LDS-poison debug build of the same sources (build.py), for tests
+POISON_LIB_PATH = os.path.join(HERE, "libtg_poison.so")
 
 TG_DTYPE_F16 = 1
 TG_DTYPE_F32 = 2
@@ -51,7 +53,8 @@ class ConfigDesc(ctypes.Structure):
                 ("name", ctypes.c_char_p)]
 
 
-def _load():
+def load_library(path=LIB_PATH):
+    """A build of the library at `path` with every C ABI function declared."""
     # The library must run on the same HIP runtime as the framework that owns
     # the device memory.  PyTorch ships its own libamdhip64; importing it
     # first makes libtg.so bind to that copy instead of loading a second
@@ -60,10 +63,10 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libtg.so is not built (%s); run "
-                          "`python tiled_dense_gemm_08_amd/build.py`" % LIB_PATH)
-    L = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run `python tiled_dense_gemm_08_amd/build.py`"
+                          % path)
+    L = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     gemm_args = [I64, I64, I64, I64, I64, I64, I, P]
     L.tg_gemm.argtypes = [P, P, P] + gemm_args
@@ -111,7 +114,7 @@ def _load():
     return L
 
 
-lib = _load()
+lib = load_library()
 
 
 # ------------------------------------------------------------ raw C ABI --

@@ -1,14 +1,19 @@
-"""Build libtg.so for gfx950 in-tree with hipcc.
+"""Build libtg.so for gfx950 in-tree with hipcc, and its LDS-poison debug
+twin libtg_poison.so (the same sources with -DTG_LDS_POISON: LDS is filled
+with NaN before every write of it, so a read of LDS bytes that the current K
+step did not write shows up as NaN in C; the GPU tests compare it with the
+normal library bit for bit).
 
-    python tiled_dense_gemm_08_amd/build.py          # library
+    python tiled_dense_gemm_08_amd/build.py          # both libraries
     python tiled_dense_gemm_08_amd/build.py --asm    # also write the device asm
                                                      # and print register use
 
 (run by path: importing the package itself needs the built library)
 
-The device assembly is also checked for M0: the direct-load kernels write M0
-from inline assembly right before each global->LDS copy, so no other
-instruction of the kernels may read or write it.
+The device assembly can also be checked for M0 (check_m0): the direct-load
+kernels write M0 from inline assembly right before each global->LDS copy, so
+no other instruction of the kernels may read or write it;
+tests/test_device_asm_cpu.py runs that check and the spill check.
 """
 import argparse
 import os
@@ -21,6 +26,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtg.so")
+POISON_LIB = os.path.join(HERE, "libtg_poison.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -52,12 +58,20 @@ def _run(cmd):
     return out
 
 
-def _run_all(cmds):
-    """Run the commands concurrently; raise if any fails."""
-    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
-             for c in cmds]
-    failed = []
-    for c, pr in procs:
+def _run_all(cmds, jobs=None):
+    """Run the commands, at most `jobs` (default: the CPUs this process may
+    use) at a time; raise if any fails."""
+    try:
+        jobs = jobs or len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        jobs = jobs or os.cpu_count() or 1
+    pending, running, failed = list(cmds), [], []
+    while pending or running:
+        while pending and len(running) < jobs:
+            c = pending.pop(0)
+            running.append((c, subprocess.Popen(c, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+        c, pr = running.pop(0)
         out, _ = pr.communicate()
         if pr.returncode != 0:
             failed.append((c, _filter(out)))
@@ -71,32 +85,41 @@ def _shard_flags(i):
     return ["-DTG_SHARD=%d" % i, "-DTG_SHARDS=%d" % SHARDS]
 
 
-def build_lib():
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    tag = "%d" % os.getpid()
+def _lib_commands(lib, extra, tag):
+    """Object files and compile commands of one library variant."""
     kern = os.path.join(CSRC, "tg_kernels.hip")
+    name = os.path.basename(lib)[:-3]
     objs, cmds = [], []
     for i in range(SHARDS):
-        o = os.path.join(BUILD_DIR, "tg_kernels_%d.%s.o" % (i, tag))
+        o = os.path.join(BUILD_DIR, "%s_kernels_%d.%s.o" % (name, i, tag))
         objs.append(o)
-        cmds.append([HIPCC] + FLAGS + _shard_flags(i) + ["-fPIC", "-c", "-o", o, kern])
-    api = os.path.join(BUILD_DIR, "tg_api.%s.o" % tag)
-    objs.append(api)
-    cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", api, os.path.join(CSRC, "tg_api.cpp")])
-    for src in (ATTN, PACK, CEILING, STATIC):
-        o = os.path.join(BUILD_DIR, "%s.%s.o" % (os.path.basename(src)[:-4], tag))
+        cmds.append([HIPCC] + FLAGS + extra + _shard_flags(i) + ["-fPIC", "-c", "-o", o, kern])
+    for src in (os.path.join(CSRC, "tg_api.cpp"), ATTN, PACK, CEILING, STATIC):
+        o = os.path.join(BUILD_DIR, "%s_%s.%s.o" % (name, os.path.basename(src).split(".")[0],
+                                                    tag))
         objs.append(o)
-        cmds.append([HIPCC] + FLAGS + ["-fPIC", "-c", "-o", o, src])
+        cmds.append([HIPCC] + FLAGS + extra + ["-fPIC", "-c", "-o", o, src])
+    return objs, cmds
+
+
+def build_lib(poison=True):
+    """libtg.so and (poison=True) libtg_poison.so; returns the paths."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    variants = [(LIB, [])] + ([(POISON_LIB, ["-DTG_LDS_POISON"])] if poison else [])
+    plan = [(lib,) + _lib_commands(lib, extra, tag) for lib, extra in variants]
     try:
-        _run_all(cmds)
-        tmp = LIB + ".tmp" + tag
-        _run([HIPCC, "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", tmp] + objs)
-        os.replace(tmp, LIB)
+        _run_all([c for _, _, cmds in plan for c in cmds])
+        for lib, objs, _ in plan:
+            tmp = lib + ".tmp" + tag
+            _run([HIPCC, "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", tmp] + objs)
+            os.replace(tmp, lib)
     finally:
-        for o in objs:
-            if os.path.exists(o):
-                os.remove(o)
-    return LIB
+        for _, objs, _ in plan:
+            for o in objs:
+                if os.path.exists(o):
+                    os.remove(o)
+    return [lib for lib, _ in variants]
 
 
 def device_asm(path=None):
@@ -175,7 +198,7 @@ def resource_report(asm_text):
 
 
 def build(asm=False):
-    lib = build_lib()
+    lib = build_lib()[0]
     if asm:
         path = device_asm()
         text = open(path).read()

@@ -77,6 +77,34 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS writes have completed.
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+#ifdef TG_LDS_POISON
+// Debug builds (-DTG_LDS_POISON): LDS is filled with fp16 NaN (all ones)
+// before it is written, so that an LDS read of bytes that no copy of the
+// current K step wrote -- a stage read before its copies landed, or a copy
+// that leaves bytes untouched -- reaches the MFMAs as NaN and shows in C.
+__device__ __forceinline__ void poison16(uint32_t lds)
+{
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    *(__attribute__((address_space(3))) u4 *)(uintptr_t)lds = u4{~0u, ~0u, ~0u, ~0u};
+}
+
+// The whole of a workgroup's LDS, at kernel start.
+template <int BYTES, int THREADS>
+__device__ __forceinline__ void poison_all(char *smem)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+    for (int i = threadIdx.x; i < BYTES / 16; i += THREADS)
+        poison16(base + 16 * i);
+    __syncthreads();
+}
+#endif
+
 // ---------------------------------------------------------------- swizzles --
 // A tile in LDS: BM rows of BK fp16 (k contiguous), 16-byte chunks XOR-
 // swizzled by row.  A fragment read has MI lanes on MI consecutive rows at
@@ -640,14 +668,23 @@ struct DirectLoader {
         if constexpr (T < C::A_LOADS) {
             const __amdgpu_buffer_rsrc_t ra = ACopy::rsrc((const char *)p.A, p.lda, p.a_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : a_off(p, T, m0);
-            dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o,
-                  lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024);
+            const uint32_t dst = lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024;
+#ifdef TG_LDS_POISON
+            poison16(dst + 16 * (threadIdx.x & 63));   // the bytes this lane's copy writes
+            wait_lgkmcnt0();
+#endif
+            dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o, dst);
         } else {
             constexpr int t = T - C::A_LOADS;
             const __amdgpu_buffer_rsrc_t rb = BCopy::rsrc((const char *)p.B, p.ldb, p.b_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : b_off(p, t, n0);
-            dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o,
-                  lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024);
+            const uint32_t dst =
+                lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024;
+#ifdef TG_LDS_POISON
+            poison16(dst + 16 * (threadIdx.x & 63));
+            wait_lgkmcnt0();
+#endif
+            dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o, dst);
         }
     }
 
@@ -950,6 +987,9 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
         k_slice<C>(p);
     static_assert((C::STAGES * C::KS) % 2 == 0, "register double buffer parity per loop body");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+#ifdef TG_LDS_POISON
+    poison_all<C::LDS_BYTES, C::THREADS>(smem);
+#endif
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * C::BM, n0 = tn * C::BN;
@@ -1231,6 +1271,21 @@ struct StagedLoader {
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const bool edge = !interior(p, m0, n0, kt);
+#ifdef TG_LDS_POISON
+        // the stage's bytes this thread writes below, first as NaN
+        {
+            const uint32_t base =
+                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+#pragma unroll
+            for (int t = 0; t < C::A_LOADS; t++)
+                poison16(base + S * C::A_BYTES + (wave * C::A_LOADS + t) * 1024 + lane * 16);
+#pragma unroll
+            for (int t = 0; t < C::B_LOADS; t++)
+                poison16(base + C::STAGES * C::A_BYTES + S * C::B_BYTES +
+                         (wave * C::B_LOADS + t) * 1024 + lane * 16);
+            wait_lgkmcnt0();
+        }
+#endif
         const int k0 = kt * C::BK;
         const int ra = AS::rows_in(m0, p.M, k0, p.K), qa = AS::cols_in(m0, p.M, k0, p.K);
         const int rb = BS::rows_in(n0, p.N, k0, p.K), qb = BS::cols_in(n0, p.N, k0, p.K);
@@ -1305,6 +1360,9 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
         k_slice<C>(p);
     static_assert(C::STAGES == 2, "the register-staged path double-buffers LDS");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+#ifdef TG_LDS_POISON
+    poison_all<C::LDS_BYTES, C::THREADS>(smem);
+#endif
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * C::BM, n0 = tn * C::BN;
@@ -1345,6 +1403,60 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_staged(Params p)
     epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, st.acc);
 }
 
+// ============================================================================
+// Single-stage reference kernel: one LDS buffer and no overlap of copies with
+// compute.  Every K step: the register-staged loads of the step (any
+// alignment, as above), a barrier (every wave is past its last fragment read
+// of the previous step), the LDS writes, a barrier, then the step's k-steps,
+// each reading its fragments and issuing its MFMAs in turn.  The plainest
+// schedule of the tiled product: the pipelined kernels are checked against it
+// bit for bit on integer inputs.
+// ============================================================================
+template <class C, typename OutT, bool BIAS, bool SPLIT>
+__global__ void __launch_bounds__(C::THREADS, 1) gemm_single(Params p)
+{
+    if constexpr (SPLIT)
+        k_slice<C>(p);
+    static_assert(C::STAGES == 1, "one LDS stage");
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+#ifdef TG_LDS_POISON
+    poison_all<C::LDS_BYTES, C::THREADS>(smem);
+#endif
+    int tm, tn;
+    tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    PipeState<C> st;
+#pragma unroll
+    for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++)
+            st.acc[i][j] = typename C::acc_t{};
+
+    const int nk = (p.K + C::BK - 1) / C::BK;
+    if (nk > 0) {
+        fragment_offsets<C>(wm, wn, st.a_off, st.b_off);
+        StagedLoader<C> ld;
+        ld.init(p);
+        for (int kt = 0; kt < nk; kt++) {
+            ld.load(p, m0, n0, kt);
+            lds_barrier();   // every wave is past the previous step's reads
+            ld.template store<0>(p, smem, m0, n0, kt);
+            lds_barrier();   // the step is in LDS
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ks++) {
+                read_frags<C>(a_stage<C, 0>(smem), b_stage<C, 0>(smem), ks, st.a_off, st.b_off,
+                              st.fa[0], st.fb[0]);
+                mfma_range<C, 0, C::MT * C::NT>(st.fa[0], st.fb[0], st.acc);
+            }
+        }
+        lds_barrier();   // every wave past its last fragment read
+    }
+    epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, st.acc);
+}
+
 // ------------------------------------------------------------ instances --
 template <class C, int TA, int TB>
 using WithOps = Cfg<C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N, C::STAGES, C::MI, C::SCHED, TA, TB,
@@ -1359,29 +1471,30 @@ hipError_t launch_ops(const Params &p, bool f16_out, bool bias, hipStream_t s)
         hipLaunchKernelGGL((KERNEL<C, OUT, B, SPLIT>), grid, block, 0, s, p);        \
         return hipGetLastError();                                                    \
     } while (0)
+#define TG_KIND(OUT, B, SPLIT)                                                       \
+    do {                                                                             \
+        if constexpr (KIND == 2)                                                     \
+            TG_GO(gemm_pipe, OUT, B, SPLIT);                                         \
+        else if constexpr (KIND == 1)                                                \
+            TG_GO(gemm_single, OUT, B, SPLIT);                                       \
+        else                                                                         \
+            TG_GO(gemm_staged, OUT, B, SPLIT);                                       \
+    } while (0)
     if (p.splits > 1) {   // K slices: fp32 (int32) partial products, no bias
         if (f16_out || bias)
             return hipErrorInvalidValue;
         using PartT = std::conditional_t<C::ES == 1, int32_t, float>;
-        if constexpr (KIND == 2)
-            TG_GO(gemm_pipe, PartT, false, true);
-        else
-            TG_GO(gemm_staged, PartT, false, true);
+        TG_KIND(PartT, false, true);
     }
     if constexpr (C::ES == 1) {   // int8 operands: int32 C, no bias
         if (f16_out || bias)
             return hipErrorInvalidValue;
-        if constexpr (KIND == 2)
-            TG_GO(gemm_pipe, int32_t, false, false);
-        else
-            TG_GO(gemm_staged, int32_t, false, false);
-    } else if constexpr (KIND == 2) {
-        if (f16_out) { if (bias) TG_GO(gemm_pipe, _Float16, true, false); else TG_GO(gemm_pipe, _Float16, false, false); }
-        else { if (bias) TG_GO(gemm_pipe, float, true, false); else TG_GO(gemm_pipe, float, false, false); }
+        TG_KIND(int32_t, false, false);
     } else {
-        if (f16_out) { if (bias) TG_GO(gemm_staged, _Float16, true, false); else TG_GO(gemm_staged, _Float16, false, false); }
-        else { if (bias) TG_GO(gemm_staged, float, true, false); else TG_GO(gemm_staged, float, false, false); }
+        if (f16_out) { if (bias) TG_KIND(_Float16, true, false); else TG_KIND(_Float16, false, false); }
+        else { if (bias) TG_KIND(float, true, false); else TG_KIND(float, false, false); }
     }
+#undef TG_KIND
 #undef TG_GO
 }
 
@@ -1542,12 +1655,14 @@ const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
 
 #if TG_SHARD == 0 && !defined(__HIP_DEVICE_COMPILE__)
 #define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
-    {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) != 0,                                    \
+    {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) == 2,                                    \
      Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>::LDS_BYTES, OPS, ES,                   \
      (KIND == 2 ? (ES == 1 ? "i8_pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI \
                              "_c" #SCH                                                     \
                            : "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI   \
                              "_c" #SCH)                                                    \
+     : KIND == 1 ? (ES == 1 ? "i8_single_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI \
+                            : "single_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI)    \
                 : (ES == 1 ? "i8_staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI   \
                            : "staged_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_mi" #MI))},
 

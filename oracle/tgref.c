@@ -282,13 +282,16 @@ static int64_t dot_i8(const int8_t *A, const int8_t *B, int op_a, int op_b, int6
     return s;
 }
 
+/* The worker sees op(A) as M x K and op(B) as N x K (k contiguous in both):
+ * the caller copies the operands into that layout first, so each dot product
+ * runs over two contiguous rows.  The sums are the same exact ascending-k
+ * sums as dot_i8 on the operands as stored. */
 static void *gemm_i8_worker(void *p)
 {
     gemm_i8_job *jb = (gemm_i8_job *)p;
     for (int64_t i = jb->row_begin; i < jb->row_end; i++)
         for (int64_t j = 0; j < jb->N; j++)
-            jb->C[i * jb->ldc + j] =
-                dot_i8(jb->A, jb->B, jb->op_a, jb->op_b, jb->lda, jb->ldb, jb->K, i, j);
+            jb->C[i * jb->ldc + j] = dot_i8(jb->A, jb->B, 0, 1, jb->K, jb->K, jb->K, i, j);
     return NULL;
 }
 
@@ -308,13 +311,27 @@ int tgref_gemm_i8_ex(int op_a, int op_b, const int8_t *A, const int8_t *B, int64
         nthreads = 1;
     if (nthreads > M)
         nthreads = (int)M;
+    /* op(A) as M x K and op(B) as N x K, both k-contiguous */
+    int8_t *a = (int8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    int8_t *bt = (int8_t *)malloc((size_t)(N * K > 0 ? N * K : 1));
+    if (!a || !bt) {
+        free(a);
+        free(bt);
+        return -1;
+    }
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t k = 0; k < K; k++)
+            a[i * K + k] = op_a ? A[k * lda + i] : A[i * lda + k];
+    for (int64_t k = 0; k < K; k++)
+        for (int64_t j = 0; j < N; j++)
+            bt[j * K + k] = op_b ? B[j * ldb + k] : B[k * ldb + j];
     pthread_t th[64];
     gemm_i8_job jobs[64];
     if (nthreads > 64)
         nthreads = 64;
     int started[64] = {0};
     for (int t = 0; t < nthreads; t++) {
-        jobs[t] = (gemm_i8_job){A, B, op_a, op_b, C, N, K, lda, ldb, ldc,
+        jobs[t] = (gemm_i8_job){a, bt, 0, 1, C, N, K, K, K, ldc,
                                 M * t / nthreads, M * (t + 1) / nthreads};
         if (pthread_create(&th[t], NULL, gemm_i8_worker, &jobs[t]) == 0)
             started[t] = 1;
@@ -324,6 +341,8 @@ int tgref_gemm_i8_ex(int op_a, int op_b, const int8_t *A, const int8_t *B, int64
     for (int t = 0; t < nthreads; t++)
         if (started[t])
             pthread_join(th[t], NULL);
+    free(a);
+    free(bt);
     return 0;
 }
 

@@ -126,15 +126,18 @@ __device__ __forceinline__ int swz_a(int row)
 // 16-lane group, 4 rows (k % 4 = 0..3) of 32 bytes, and groups sit on rows 8
 // apart; the swizzle (multiples of 2 chunks, so the 32-byte pairs stay whole)
 // spreads rows {0..3, 8..11} over 8 distinct 32-byte slots.  It must stay
-// below the BN/8 chunks of a row, so 64-wide tiles use only the k % 4 part.
-// It is unchanged by k += 4 and k += 16.
+// below the BN/8 chunks of a row: a 64-wide row is 128 bytes, half of the
+// banks, so rows of either parity share the 4 slots of their half, and the
+// swizzle on k bits 1 and 3 gives each slot 2 of the 16 rows a read touches
+// (XOR by k % 4 alone gave 4: the groups 8 rows apart coincided).  Both are
+// unchanged by k += 4, 16 and 32.
 template <int BN>
 __device__ __forceinline__ int swz_b(int k)
 {
     if constexpr (BN >= 128)
         return 2 * (k & 3) + 8 * ((k >> 3) & 1);
     else
-        return 2 * (k & 3);
+        return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1);
 }
 
 // Same for 1-byte elements (R bytes per row): the 8-bit transpose read has,

@@ -12,11 +12,13 @@ GEMM + bias + ReLU as a record of its own ("fused").
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--config ID]
 
-Reported per workload: whole-job TFLOP/s (2MNK per step) over exactly K timed
-steps, the dominant kernel's MFMA roofline fraction measured with HIP events
-on the launch stream, 5 further loops of at least 100 ms each (per-launch
-median and minimum), the matrix cores' own rate on the workload's values,
-and the CPU oracle timed on the whole product on the host cores.  The GPU's
+Reported per workload: 5 loops of at least 100 ms each (per-launch median
+and minimum; run first, they also bring the shader clock to its sustained
+level), then whole-job TFLOP/s (2MNK per step) over exactly K timed steps
+after W warm-up steps, the dominant kernel's MFMA roofline fraction measured
+with HIP events on the launch stream, the matrix cores' own rate on the
+workload's values, and the CPU oracle timed on the whole product on the host
+cores.  The GPU's
 output of the first call is compared with that oracle output entry by entry
 (the parity gate); a failing gate prints no throughput.
 """
@@ -48,8 +50,10 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # digest of the kernel sources and the configuration's row: a kernel changed
 # since the counters were taken reports null.
 TRAFFIC_BYTES = {
-    # FETCH_SIZE 792936 KiB x 2.0 + WRITE_SIZE 131072 KiB x 1.0 (profiles/)
-    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c0", "2e13aea2d5ceab3e"): 1758151229,
+    # FETCH_SIZE 791288 KiB x 2.0 + WRITE_SIZE 137216 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c2", "0a8bd70be5904950"): 1761066880,
+    # FETCH_SIZE 304676 KiB x 2.0 + WRITE_SIZE 90816 KiB x 1.0 (profiles/)
+    ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x4_mi16_c2", "0a8bd70be5904950"): 716971904,
 }
 
 
@@ -57,7 +61,7 @@ TRAFFIC_BYTES = {
 # its sources.
 ATTN_TRAFFIC_BYTES = {
     # FETCH_SIZE 49244 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
-    ("attn_b2h16l4096d128", "ca1c153ab08ea7a4"): 134930432,
+    ("attn_b2h16l4096d128", "5369187d8d08194a"): 134930432,
 }
 
 
@@ -350,6 +354,19 @@ def gemm_record(a, name, steps, warmup):
     torch.cuda.synchronize()
     out = C.cpu().numpy()
 
+    # ---- 5 loops of at least 100 ms each (the first 100 ms loop sizes them);
+    # they also bring the clocks to the steady state of a sustained GEMM
+    # before the timed steps (the shader clock ramps up over the first tens of
+    # milliseconds of work after an idle period)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    step()
+    ev1.record(stream)
+    ev1.synchronize()
+    first_ms = ev0.elapsed_time(ev1)
+    loops = timed_loops(step, stream, max(1, int(np.ceil(100.0 / max(first_ms, 1e-3)))))
+
     # ---- timing: warmup, then exactly `steps` launches between two synchronisations
     for _ in range(warmup):
         step()
@@ -369,7 +386,6 @@ def gemm_record(a, name, steps, warmup):
     elapsed = max(wall, gpu_ms / 1e3)
     value = flop * steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
-    loops = timed_loops(step, stream, max(1, int(np.ceil(0.1 / per_launch_s))))
     board = None if a.no_board else board_sample(step, stream)
     ceiling = None
     if not is_i8:
@@ -532,6 +548,16 @@ def bench_attention(a):
         print(json.dumps({"error": "parity gate failed", "workload": a.workload}))
         return 1
 
+    # ---- 5 loops of at least 100 ms each, which also settle the clocks
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    step()
+    ev1.record(stream)
+    ev1.synchronize()
+    loops = timed_loops(step, stream,
+                        max(1, int(np.ceil(100.0 / max(ev0.elapsed_time(ev1), 1e-3)))))
+
     # ---- timing
     for _ in range(a.warmup):
         step()
@@ -550,7 +576,6 @@ def bench_attention(a):
     elapsed = max(wall, gpu_ms / 1e3)
     value = flop * a.steps / elapsed / 1e12
     achieved = flop / (gpu_ms / 1e3 / a.steps) / 1e12
-    loops = timed_loops(step, stream, max(1, int(np.ceil(0.1 / (gpu_ms / 1e3 / a.steps)))))
     board = None if a.no_board else board_sample(step, stream)
     # the matrix cores' rate on operands from Q and K (the score product's
     # inputs; both products run on 32x32x16)

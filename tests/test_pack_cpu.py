@@ -152,3 +152,22 @@ def test_invalid_arguments_and_empty_problems():
     assert tg.lib.tg_select_plan(0, 0, PA, PB, None, PC, 64, 64, 64, 64, 64, 64, F32, 0,
                                  ctypes.byref(c), ctypes.byref(c), None,
                                  None) == tg.TG_ERROR_INVALID_VALUE
+
+
+def test_cached_plans_follow_tuning_cache_changes(tmp_path):
+    """Plans are cached per host thread; loading or clearing the tuning cache
+    must change what the next identical call runs."""
+    lda, ldb = lds(2048, 2048, 2048, 0, 0)
+    auto = plan(2048, 2048, 2048, dtype=F16)
+    assert plan(2048, 2048, 2048, dtype=F16) == auto   # a cache hit gives the same plan
+    other = [c for c in tg.configs() if c["direct_lds"] and c["elem_bytes"] == 2
+             and c["id"] != auto[0]][0]
+    f = tmp_path / "t.tgtune"
+    f.write_text("%s\n2048 2048 2048 N N f16 0 %d %s 1.0\n" % (MAGIC, other["id"], other["name"]))
+    tg.load_tuning(str(f))
+    assert plan(2048, 2048, 2048, dtype=F16) == (other["id"], 1, 0, 0)
+    tg.tg_tuning_clear()
+    assert plan(2048, 2048, 2048, dtype=F16) == auto
+    # the plan follows the operands' alignment, which is part of the key
+    assert plan(2048, 2048, 2048, dtype=F16, pa=PA + 2)[2] == 1
+    assert plan(2048, 2048, 2048, dtype=F16) == auto

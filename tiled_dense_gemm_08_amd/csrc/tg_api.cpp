@@ -292,6 +292,7 @@ constexpr size_t kMaxTuneLine = 1024;
 std::mutex g_tune_mu;
 std::shared_ptr<const TuneTable> g_tune;   // guarded by g_tune_mu; null = empty
 std::atomic<bool> g_tune_any{false};
+std::atomic<uint64_t> g_tune_gen{0};       // bumped by every change of the table
 std::once_flag g_tune_env_once;
 
 TuneKey tune_key(const Problem &p)
@@ -440,6 +441,7 @@ void publish(std::shared_ptr<const TuneTable> t)
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_tune = std::move(t);
     g_tune_any.store(g_tune != nullptr && !g_tune->empty(), std::memory_order_release);
+    g_tune_gen.fetch_add(1, std::memory_order_acq_rel);
 }
 
 // TG_TUNING_FILE: loaded once, before the first call that reads or changes
@@ -1012,6 +1014,75 @@ tg_status execute(const Plan &pl, const Problem &p, char *ws, hipStream_t stream
     return tg::launch_splitk_reduce(r, kind, stream) == hipSuccess ? TG_SUCCESS : TG_ERROR_LAUNCH;
 }
 
+// ---- plan cache -----------------------------------------------------------------
+// Choosing a plan walks the cost model's rows and slice counts (a few
+// microseconds, as long as a small GEMM takes on the device).  A plan is a
+// function of the problem's sizes, leading dimensions, orientation, output
+// type, epilogue, the low four bits of the A and B addresses (which decide
+// the load path), the named configuration and slice count, the workspace
+// size and the tuning cache's contents; each host thread keeps its last few
+// plans under that key and rebinds the buffer pointers on a hit.
+struct PlanKey {
+    int64_t M, N, K, lda, ldb, ldc;
+    int op_a, op_b, c_dtype, fused, config_id, splits;
+    uint32_t align;
+    uint64_t ws_bytes, tune_gen;
+    bool operator==(const PlanKey &o) const
+    {
+        return M == o.M && N == o.N && K == o.K && lda == o.lda && ldb == o.ldb &&
+               ldc == o.ldc && op_a == o.op_a && op_b == o.op_b && c_dtype == o.c_dtype &&
+               fused == o.fused && config_id == o.config_id && splits == o.splits &&
+               align == o.align && ws_bytes == o.ws_bytes && tune_gen == o.tune_gen;
+    }
+};
+
+struct PlanSlot {
+    bool used = false;
+    PlanKey key{};
+    Plan plan;
+};
+
+constexpr int kPlanSlots = 8;
+thread_local PlanSlot t_plans[kPlanSlots];
+thread_local int t_plan_next = 0;
+
+PlanKey plan_key(const Problem &p, int config_id, int splits, size_t ws_bytes)
+{
+    ensure_env_cache();
+    const uint32_t align = (uint32_t)((reinterpret_cast<uintptr_t>(p.A) & 15) |
+                                      ((reinterpret_cast<uintptr_t>(p.B) & 15) << 4));
+    return PlanKey{p.M, p.N, p.K, p.lda, p.ldb, p.ldc, p.op_a, p.op_b, (int)p.c_dtype,
+                   p.fused ? 1 : 0, config_id, splits, align, (uint64_t)ws_bytes,
+                   g_tune_gen.load(std::memory_order_acquire)};
+}
+
+// A cached plan for p, with p's pointers bound in, or false.
+bool plan_cached(const PlanKey &k, const Problem &p, Plan *out)
+{
+    for (const PlanSlot &sl : t_plans) {
+        if (sl.used && sl.key == k) {
+            *out = sl.plan;
+            out->kp.A = p.A;   // packed operands get their copies' addresses at run time
+            out->kp.B = p.B;
+            out->kp.C = p.C;
+            out->kp.bias = p.bias;
+            out->op[0].src = p.A;
+            out->op[1].src = p.B;
+            return true;
+        }
+    }
+    return false;
+}
+
+void plan_remember(const PlanKey &k, const Plan &pl)
+{
+    PlanSlot &sl = t_plans[t_plan_next];
+    t_plan_next = (t_plan_next + 1) % kPlanSlots;
+    sl.used = true;
+    sl.key = k;
+    sl.plan = pl;
+}
+
 // A call without workspace: tg_gemm, tg_gemm_bias_relu, tg_gemm_ex (config_id
 // -1) and tg_gemm_with_config.
 tg_status run(int config_id, const Problem &p, hipStream_t stream)
@@ -1024,10 +1095,14 @@ tg_status run(int config_id, const Problem &p, hipStream_t stream)
     if (p.M == 0 || p.N == 0)
         return TG_SUCCESS;
     Plan pl;
-    if ((st = plan_fixed(p, config_id, 1, 0, &pl)) != TG_SUCCESS)
-        return st;
-    if (!supports(kConfigs[pl.id], p))
-        return TG_ERROR_UNSUPPORTED;
+    const PlanKey key = plan_key(p, config_id, 1, 0);
+    if (!plan_cached(key, p, &pl)) {
+        if ((st = plan_fixed(p, config_id, 1, 0, &pl)) != TG_SUCCESS)
+            return st;
+        if (!supports(kConfigs[pl.id], p))
+            return TG_ERROR_UNSUPPORTED;
+        plan_remember(key, pl);
+    }
     int dev = 0;
     if ((st = check_problem_pointers(p, &dev)) != TG_SUCCESS)
         return st;
@@ -1047,10 +1122,14 @@ tg_status plan_ws(const Problem &p, int config_id, int splits, size_t ws_bytes, 
         *pl = Plan{};
         return TG_SUCCESS;
     }
-    if (config_id < 0 && splits == 0)
-        *pl = plan_auto(p, ws_bytes);
-    else if ((st = plan_fixed(p, config_id, splits, ws_bytes, pl)) != TG_SUCCESS)
-        return st;
+    const PlanKey key = plan_key(p, config_id, splits, ws_bytes);
+    if (!plan_cached(key, p, pl)) {
+        if (config_id < 0 && splits == 0)
+            *pl = plan_auto(p, ws_bytes);
+        else if ((st = plan_fixed(p, config_id, splits, ws_bytes, pl)) != TG_SUCCESS)
+            return st;
+        plan_remember(key, *pl);
+    }
     return pl->ws_used() > ws_bytes ? TG_ERROR_WORKSPACE : TG_SUCCESS;
 }
 

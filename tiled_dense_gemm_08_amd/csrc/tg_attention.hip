@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tg_attention.h"
 
 namespace tg {
@@ -57,6 +59,7 @@ struct Tile {
     // fewer registers let more waves share a SIMD instead (measured faster).
     static constexpr bool PIPE = D == 128;
     static constexpr int KST = PIPE ? 3 : 2;     // K ring depth; V: two stages
+    static constexpr int U = PIPE ? 2 : 1;       // tiles per unrolled loop body
     static constexpr int LDS = (KST + 2) * BYTES;
     static constexpr int LOADS = BYTES / 1024 / WAVES;   // copies per wave per tile
     static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
@@ -256,7 +259,10 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         acc_s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], acc_s, 0, 0, 0);
     };
 
-    float16v s[2] = {float16v{}, float16v{}};
+    // Scores of the current and of the next key tile, double-buffered: the
+    // pipelined loop is unrolled by two tiles, so that the two buffers trade
+    // roles without register moves (and the V stage offsets are fixed).
+    float16v sa[2] = {float16v{}, float16v{}}, sb[2] = {float16v{}, float16v{}};
     if (T::PIPE && nblk > 0) {
         wait_vmcnt0();
         lds_barrier();
@@ -264,10 +270,15 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         for (int ks = 0; ks < T::DK; ks++)
 #pragma unroll
             for (int t = 0; t < 2; t++)
-                score_mfma(smem, ks, t, s[t]);
+                score_mfma(smem, ks, t, sa[t]);
     }
 
-    for (int j = 0; j < nblk; j++) {
+    // key tile j, where J = j mod U
+    auto step = [&](auto jc, int j) {
+        constexpr int J = decltype(jc)::value;
+        const int JV = T::U == 2 ? J : j;   // V stage parity
+        float16v(&s)[2] = (T::PIPE && (J & 1)) ? sb : sa;    // tile j's scores
+        float16v(&sn)[2] = (T::PIPE && (J & 1)) ? sa : sb;   // tile j+1's (pipelined)
         if (!T::PIPE || j > 0) {
             wait_vmcnt0();
             // pipelined: K tile j+1 and V tile j in LDS; plain: K and V tile j.
@@ -277,20 +288,20 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         if constexpr (T::PIPE) {
             if (j + 2 < nblk)
                 copy_tile<D, false>(Kh, p.ks[2], (j + 2) * BKV, p.Lk, p.k_bytes,
-                                    lds0 + ((j + 2) % 3) * T::BYTES);
+                                    lds0 + ((j + 2) % T::KST) * T::BYTES);
         } else {
             if (j + 1 < nblk)
                 copy_tile<D, false>(Kh, p.ks[2], (j + 1) * BKV, p.Lk, p.k_bytes,
-                                    lds0 + ((j + 1) & 1) * T::BYTES);
+                                    lds0 + ((j + 1) % T::KST) * T::BYTES);
         }
         if (j + 1 < nblk)
             copy_tile<D, true>(Vh, p.vs[2], (j + 1) * BKV, p.Lk, p.v_bytes,
-                               lds_v + ((j + 1) & 1) * T::BYTES);
-        const char *k_next = smem + ((j + 1) % 3) * T::BYTES;   // stale on the last tile
-        const char *vs_tile = smem + T::KST * T::BYTES + (j & 1) * T::BYTES;
+                               lds_v + ((JV + 1) & 1) * T::BYTES);
+        const char *k_next = smem + ((j + 1) % T::KST) * T::BYTES;   // stale on the last tile
+        const char *vs_tile = smem + T::KST * T::BYTES + (JV & 1) * T::BYTES;
         const int kv0 = j * BKV;
         if constexpr (!T::PIPE) {
-            const char *k_tile = smem + (j & 1) * T::BYTES;
+            const char *k_tile = smem + (j % T::KST) * T::BYTES;
             s[0] = float16v{};
             s[1] = float16v{};
 #pragma unroll
@@ -346,7 +357,6 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         // The next tile's scores on the matrix cores, interleaved with this
         // tile's weights exp2(s scale log2e - m), row sum and fp16 weights
         // on the vector unit.
-        float16v sn[2] = {float16v{}, float16v{}};
         half8 pf[4];
         float rs = 0.f;
         if constexpr (!T::PIPE) {
@@ -360,6 +370,9 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
                     pf[2 * t + r / 8][r % 8] = (_Float16)w;
                 }
             }
+        } else {
+            sn[0] = float16v{};
+            sn[1] = float16v{};
         }
         // pipelined: 2 DK MFMAs and 32 weights, 32 / (2 DK) weights per MFMA
         constexpr int NM = 2 * T::DK, WPM = 32 / NM;
@@ -396,11 +409,18 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], acc[dt], 0, 0, 0);
             }
         }
-        if constexpr (T::PIPE) {
-            s[0] = sn[0];
-            s[1] = sn[1];
-        }
+    };
+
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    int j = 0;
+    for (; j + T::U <= nblk; j += T::U) {
+        step(J0{}, j);
+        if constexpr (T::U == 2)
+            step(J1{}, j + 1);
     }
+    if (T::U == 2 && j < nblk)
+        step(J0{}, j);
 
     // O = O^T / l, row by row; lse = (m + log2 l) ln 2
     const float lsum = l + __shfl_xor(l, 32);

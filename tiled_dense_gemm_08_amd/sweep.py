@@ -141,9 +141,8 @@ def time_launch(launch, reps, timing="graph"):
         if st != tg.TG_SUCCESS:
             raise tg.TgError(st, "timed call")
 
-    # the first launch runs outside capture, on the stream the capture uses:
-    # argument errors surface here, and the library's per-stream scratch for
-    # packed operands exists before capture (none is allocated under capture)
+    # the first launch runs outside capture, on the stream the capture uses,
+    # so that argument errors surface before any graph is recorded
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):

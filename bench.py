@@ -186,6 +186,15 @@ def board_sample(step, stream, max_s=15.0):
             "launches_during_sample": n, "source": "amd-smi metric -p -c, one sample"}
 
 
+def at_sampled_clock(board, achieved, peak):
+    """Add to the board sample the kernel's fraction of the peak scaled to
+    the sampled shader clock (the peak's clock is the nominal 2.4 GHz)."""
+    if board and board.get("gfx_clock_mhz_mean"):
+        board["frac_of_peak_at_sampled_clock"] = round(
+            achieved / (peak * board["gfx_clock_mhz_mean"] / (PEAK_GHZ * 1e3)), 4)
+    return board
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -482,7 +491,7 @@ def gemm_record(a, name, steps, warmup):
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
-        "board_under_load": board,
+        "board_under_load": at_sampled_clock(board, achieved, peak),
     }
 
 
@@ -630,7 +639,7 @@ def bench_attention(a):
                      "traffic": ATTN_TRAFFIC_BYTES.get((a.workload, attention_source_digest()))},
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
-        "board_under_load": board,
+        "board_under_load": at_sampled_clock(board, achieved, PEAK_TFLOPS),
     }
     print(json.dumps(line))
     return 0

@@ -17,8 +17,9 @@ and minimum; run first, they also bring the shader clock to its sustained
 level), then whole-job TFLOP/s (2MNK per step) over exactly K timed steps
 after W warm-up steps, the dominant kernel's MFMA roofline fraction measured
 with HIP events on the launch stream, the matrix cores' own rate on the
-workload's values, and the CPU oracle timed on the whole product on the host
-cores.  The GPU's
+workload's values, the board's power and clock under load, launches timed
+alone after a scrub of the caches ("cold"), and the CPU oracle timed on the
+whole product on the host cores.  The GPU's
 output of the first call is compared with that oracle output entry by entry
 (the parity gate); a failing gate prints no throughput.
 """
@@ -215,6 +216,9 @@ def parse():
     ap.add_argument("--no-board", action="store_true",
                     help="skip the amd-smi power and clock sample (its extra launches "
                          "crowd profiler traces)")
+    ap.add_argument("--cold-launches", type=int, default=10, metavar="N",
+                    help="GEMM workloads: also time N launches each after a 512 MiB scrub of "
+                         "the caches (0: skip)")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the matrix cores' rate (tg_mfma_ceiling) on the "
                          "workload's A and B values and on zero operands, then exit")
@@ -277,9 +281,33 @@ def main():
             return 1
         line["fused"] = {k: fused[k] for k in ("value", "unit", "ms_per_step", "config",
                                                "loops", "roofline", "cpu_baseline",
-                                               "mfma_ceiling", "board_under_load")}
+                                               "mfma_ceiling", "board_under_load", "cold")}
     print(json.dumps(line))
     return 0
+
+
+def cold_launches(step, stream, flop, n, scrub_mib=512):
+    """n launches, each after writing scrub_mib MiB elsewhere (more than the
+    L2 caches and the 256 MB last-level cache hold, so that the operands come
+    from HBM), each timed alone with HIP events on the launch stream."""
+    if n <= 0:
+        return None
+    import torch
+    scrub = torch.empty(scrub_mib << 20, dtype=torch.uint8, device=stream.device)
+    ms = []
+    for i in range(n):
+        scrub.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del scrub
+    med = float(np.median(ms))
+    return {"launches": n, "scrub_mib": scrub_mib, "median_ms": round(med, 5),
+            "min_ms": round(min(ms), 5), "tflops_median": round(flop / (med / 1e3) / 1e12, 2)}
 
 
 def timed_loops(step, stream, launches, n=5):
@@ -396,6 +424,7 @@ def gemm_record(a, name, steps, warmup):
     value = flop * steps / elapsed / 1e12
     achieved = flop / per_launch_s / 1e12
     board = None if a.no_board else board_sample(step, stream)
+    cold = cold_launches(step, stream, flop, a.cold_launches)
     ceiling = None
     if not is_i8:
         ceiling = mfma_ceiling(w["A"], w["B"], stream)
@@ -492,6 +521,7 @@ def gemm_record(a, name, steps, warmup):
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
         "board_under_load": at_sampled_clock(board, achieved, peak),
+        "cold": cold,
     }
 
 

@@ -1,6 +1,7 @@
 """bench.py's command-line contract on the CPU: more than one GPU is refused
-with a message (this build has no multi-GPU path), and every named workload
-is accepted by the parser."""
+with a message (this build has no multi-GPU path), every named workload is
+accepted by the parser, and the fraction of peak at the sampled clock scales
+with the clock."""
 import os
 import subprocess
 import sys
@@ -28,3 +29,14 @@ def test_every_workload_is_a_parser_choice():
     text = " ".join(r.stdout.split())
     for name in list(gen.WORKLOADS) + list(gen.ATTN_WORKLOADS):
         assert name in text, name
+
+
+def test_fraction_of_peak_at_the_sampled_clock():
+    sys.path.insert(0, ROOT)
+    import bench
+    board = {"gfx_clock_mhz_mean": 1200}
+    # half the nominal clock: the fraction doubles
+    assert bench.at_sampled_clock(board, 0.25 * bench.PEAK_TFLOPS,
+                                  bench.PEAK_TFLOPS)["frac_of_peak_at_sampled_clock"] == 0.5
+    assert bench.at_sampled_clock(None, 1.0, 2.0) is None
+    assert "frac_of_peak_at_sampled_clock" not in bench.at_sampled_clock({}, 1.0, 2.0)

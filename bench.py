@@ -94,27 +94,27 @@ def kernel_source_digest(config_id):
 
 
 def mfma_ceiling(a_bits, b_bits, stream, iters=20000, workgroups=1024, reps=3):
-    """The matrix cores' sustained fp16 rate (tg_mfma_ceiling) on operand
-    fragments taken from the workload's own A and B values, for both MFMA
-    shapes: the ceiling a GEMM on such data can approach under the board's
-    power limit.  TFLOP/s, median of `reps` launches after one warm-up."""
+    """The matrix cores' sustained rate (tg_mfma_ceiling) on operand
+    fragments taken from the workload's own A and B values: for fp16 (uint16
+    bit patterns) both MFMA shapes, for int8 the 16x16x64 one.  The ceiling
+    a GEMM on such data can approach under the board's power limit.
+    TFLOP/s (TOPS), median of `reps` launches after one warm-up."""
     import torch
 
     import tiled_dense_gemm_08_amd as tg
-    n = tg.TG_CEILING_OPERAND_BYTES // 4     # fp16 values per operand
+    int8 = np.asarray(a_bits).dtype.itemsize == 1
+    n = tg.TG_CEILING_OPERAND_BYTES // 2 // np.asarray(a_bits).dtype.itemsize   # values per operand
     a = np.ascontiguousarray(a_bits).reshape(-1)[:n]
     b = np.ascontiguousarray(b_bits).reshape(-1)[:n]
     if a.size < n or b.size < n:
         return None
-    # thread t, set s: 8 A chunks then 8 B chunks of 8 values
-    buf = np.empty((256, 2, 2, 8, 8), np.uint16)
-    buf[:, :, 0] = a.view(np.uint16).reshape(256, 2, 8, 8)
-    buf[:, :, 1] = b.view(np.uint16).reshape(256, 2, 8, 8)
-    ops = torch.from_numpy(buf.reshape(-1).view(np.int16)).to("cuda:0")
-    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda:0")
-    flop = workgroups * 4.0 * iters * 2 * 128 * 128 * 32
+    # the first half of the buffer holds A's values, the second B's
+    buf = np.concatenate([a.view(np.uint8), b.view(np.uint8)])
+    ops = torch.from_numpy(buf).to("cuda:0")
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda:0")
+    flop = workgroups * 8.0 * iters * 2 * 128 * 64 * (64 if int8 else 32)
     out = {}
-    for mi in (32, 16):
+    for mi in ((64,) if int8 else (32, 16)):
         times = []
         for r in range(reps + 1):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -129,7 +129,8 @@ def mfma_ceiling(a_bits, b_bits, stream, iters=20000, workgroups=1024, reps=3):
             if r:
                 times.append(e0.elapsed_time(e1))
         times.sort()
-        out["tflops_%dx%dx%d" % (mi, mi, 512 // mi)] = round(flop / (times[len(times) // 2] / 1e3) / 1e12, 1)
+        key = "tops_16x16x64_i8" if mi == 64 else "tflops_%dx%dx%d" % (mi, mi, 512 // mi)
+        out[key] = round(flop / (times[len(times) // 2] / 1e3) / 1e12, 1)
     return out
 
 
@@ -232,11 +233,13 @@ def ceiling_only(a):
     import torch
     w = gen.workload(a.workload)
     stream = torch.cuda.current_stream()
-    zeros = np.zeros(1 << 16, np.uint16)
+    i8 = w["A"].dtype.itemsize == 1
+    zeros = np.zeros(1 << 17, np.int8) if i8 else np.zeros(1 << 16, np.uint16)
     print(json.dumps({"workload": a.workload,
                       "mfma_ceiling_workload_values": mfma_ceiling(w["A"], w["B"], stream),
                       "mfma_ceiling_zero_operands": mfma_ceiling(zeros, zeros, stream),
-                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s"}))
+                      "peak": PEAK_TOPS_INT8 if i8 else PEAK_TFLOPS,
+                      "unit": "TOPS" if i8 else "TFLOP/s"}))
     return 0
 
 
@@ -264,8 +267,8 @@ def main():
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
     if a.ceiling_only:
-        if a.workload in gen.ATTN_WORKLOADS or gen.WORKLOADS[a.workload]["kind"] == "i8":
-            print("--ceiling-only needs an fp16 GEMM workload", file=sys.stderr)
+        if a.workload in gen.ATTN_WORKLOADS:
+            print("--ceiling-only needs a GEMM workload", file=sys.stderr)
             return 2
         return ceiling_only(a)
     if a.workload in gen.ATTN_WORKLOADS:
@@ -425,15 +428,21 @@ def gemm_record(a, name, steps, warmup):
     achieved = flop / per_launch_s / 1e12
     board = None if a.no_board else board_sample(step, stream)
     cold = cold_launches(step, stream, flop, a.cold_launches)
-    ceiling = None
-    if not is_i8:
-        ceiling = mfma_ceiling(w["A"], w["B"], stream)
-        if ceiling:
-            mi = 16 if "_mi16_" in info["name"] else 32
+    ceiling = mfma_ceiling(w["A"], w["B"], stream)
+    if ceiling:
+        mi = 16 if "_mi16_" in info["name"] else 32
+        if is_i8:
+            # the int8 ceiling loop runs 16x16x64, the shape of the int8 kernels
+            # the dispatcher picks
+            own = ceiling["tops_16x16x64_i8"]
+            shape = "%dx%dx%d_i8" % (mi, mi, 1024 // mi)
+            vals = "65536 int8 values"
+        else:
             own = ceiling["tflops_%dx%dx%d" % (mi, mi, 512 // mi)]
-            ceiling.update({"operands": "32768 values each of A and B (their first elements)",
-                            "kernel_mfma": "%dx%dx%d" % (mi, mi, 512 // mi),
-                            "frac_of_ceiling": round(achieved / own, 4)})
+            shape = "%dx%dx%d" % (mi, mi, 512 // mi)
+            vals = "32768 values"
+        ceiling.update({"operands": vals + " each of A and B (their first elements)",
+                        "kernel_mfma": shape, "frac_of_ceiling": round(achieved / own, 4)})
 
     # ---- CPU oracle: the whole product on the host cores, then the gate
     threads = oracle.default_threads()

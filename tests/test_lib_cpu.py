@@ -196,6 +196,8 @@ def test_int8_validation_without_gpu():
 
 @pytest.mark.parametrize("args", [
     (8, PA, PC, 2, 1), (0, PA, PC, 2, 1),            # unknown MFMA shape
+    (128, PA, PC, 2, 1),
+    (64, 0, PC, 2, 1), (64, PA, PC, 3, 1),           # the int8 shape: same rules
     (32, 0, PC, 2, 1), (32, PA, 0, 2, 1),            # NULL buffers
     (32, PA, PC, 0, 1), (32, PA, PC, 3, 1),          # iters not even and >= 2
     (16, PA, PC, (1 << 30) + 2, 1),                  # too many iters

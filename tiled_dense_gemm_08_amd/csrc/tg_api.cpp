@@ -1425,7 +1425,8 @@ tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t i
 {
     // iters * workgroups is capped at 2^32 (about ten seconds of matrix-core
     // work) so that one call cannot hold the device for minutes
-    if ((mfma != 16 && mfma != 32) || operands == nullptr || sink == nullptr || iters < 2 ||
+    if ((mfma != 16 && mfma != 32 && mfma != 64) || operands == nullptr || sink == nullptr ||
+        iters < 2 ||
         iters > (int64_t(1) << 30) || (iters & 1) || workgroups < 1 ||
         workgroups > (int64_t(1) << 20) || iters * workgroups > (int64_t(1) << 32))
         return TG_ERROR_INVALID_VALUE;
@@ -1436,7 +1437,7 @@ tg_status tg_mfma_ceiling(int mfma, const void *operands, float *sink, int64_t i
     // both buffers must lie inside their allocations
     if ((st = check_device(&dev)) != TG_SUCCESS ||
         (st = check_span(operands, TG_CEILING_OPERAND_BYTES, dev)) != TG_SUCCESS ||
-        (st = check_span(sink, (uint64_t)workgroups * 256 * sizeof(float), dev)) != TG_SUCCESS)
+        (st = check_span(sink, (uint64_t)workgroups * 512 * sizeof(float), dev)) != TG_SUCCESS)
         return st;
     (void)hipGetLastError();
     return tg::launch_mfma_ceiling(mfma, operands, sink, (int)iters, (int)workgroups, stream) ==

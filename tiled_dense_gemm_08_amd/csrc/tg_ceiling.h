@@ -8,9 +8,10 @@
 
 namespace tg {
 
-// `workgroups` workgroups of 256 threads; thread t of every workgroup reads
-// the 512 bytes at operands + 512 t (131072 bytes in all) and writes one
-// float to sink[256 * workgroup + t].  mfma: 16 (16x16x32) or 32 (32x32x16);
+// `workgroups` workgroups of 512 threads; every thread reads 16-byte chunks
+// of the 131072-byte operand buffer (A fragments from its first half, B
+// fragments from its second) and writes one float to sink[512 * workgroup +
+// t].  mfma: 16 (16x16x32 fp16), 32 (32x32x16 fp16) or 64 (16x16x64 int8);
 // iters > 0 and even.  Arguments are validated by the caller.
 hipError_t launch_mfma_ceiling(int mfma, const void *operands, float *sink, int iters,
                                int workgroups, hipStream_t s);

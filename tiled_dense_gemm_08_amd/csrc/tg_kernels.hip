@@ -142,12 +142,19 @@ __device__ __forceinline__ int swz_b(int k)
 
 // Same for 1-byte elements (R bytes per row): the 8-bit transpose read has,
 // per 16-lane group, 8 rows (k % 8 = 0..7) of 16 bytes; XOR by k % 8 puts them
-// on 8 distinct 16-byte slots.  Unchanged by k += 8.
+// on 8 distinct 16-byte slots.  The groups sit 16 rows apart: with 256-byte
+// rows (16 slots) k bit 4 also moves to the other half of the row, so that
+// neighbouring groups do not land on the same banks (bank conflicts per
+// active LDS cycle on 8192^3 int8: 0.25 with k % 8 alone).  Unchanged by
+// k += 8 and k += 64.
 template <int R>
 __device__ __forceinline__ int swz_b8(int k)
 {
     constexpr int CHUNKS = R / 16;
-    return k & (CHUNKS >= 8 ? 7 : CHUNKS - 1);
+    if constexpr (CHUNKS >= 16)
+        return (k & 7) ^ (8 * ((k >> 4) & 1));
+    else
+        return k & (CHUNKS >= 8 ? 7 : CHUNKS - 1);
 }
 
 // The swizzle of an mn-major tile of R elements of ES bytes per row.

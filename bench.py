@@ -51,10 +51,10 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # digest of the kernel sources and the configuration's row: a kernel changed
 # since the counters were taken reports null.
 TRAFFIC_BYTES = {
-    # FETCH_SIZE 791288 KiB x 2.0 + WRITE_SIZE 137216 KiB x 1.0 (profiles/)
-    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c2", "0a8bd70be5904950"): 1761066880,
-    # FETCH_SIZE 304676 KiB x 2.0 + WRITE_SIZE 90816 KiB x 1.0 (profiles/)
-    ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x4_mi16_c2", "0a8bd70be5904950"): 716971904,
+    # FETCH_SIZE 794525.6 KiB x 2.0 + WRITE_SIZE 137216 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 1767697536,
+    # FETCH_SIZE 304672.8 KiB x 2.0 + WRITE_SIZE 90816 KiB x 1.0 (profiles/)
+    ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 716965504,
 }
 
 

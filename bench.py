@@ -61,8 +61,8 @@ TRAFFIC_BYTES = {
 # The same for the fused attention kernel, keyed by workload and a digest of
 # its sources.
 ATTN_TRAFFIC_BYTES = {
-    # FETCH_SIZE 49249.5 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
-    ("attn_b2h16l4096d128", "fffb0a56ef4a04dc"): 134941696,
+    # FETCH_SIZE 49308.5 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
+    ("attn_b2h16l4096d128", "0c9e527802ea2d50"): 135062528,
 }
 
 

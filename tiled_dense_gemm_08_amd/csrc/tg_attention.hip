@@ -262,7 +262,37 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
     // Scores of the current and of the next key tile, double-buffered: the
     // pipelined loop is unrolled by two tiles, so that the two buffers trade
     // roles without register moves (and the V stage offsets are fixed).
+    // Tile maximum of the raw scores of key tile jt (rows of the lane's
+    // query, both halves of the wave).  Only tiles that reach past Lk or
+    // across the causal diagonal of the wave's first query mask anything (a
+    // uniform branch: the others skip the per-key test).
+    auto tile_max = [&](float16v(&sc)[2], int jt) {
+        const int kvt = jt * BKV;
+        const bool edge = kvt + BKV > p.Lk || (CAUSAL && kvt + BKV - 1 > q0 + shift);
+        float mxt = -INFINITY;
+        if (edge) {
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = kvt + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = key < p.Lk && (!CAUSAL || key <= query + shift);
+                    sc[t][r] = vis ? sc[t][r] : -INFINITY;
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                mxt = fmaxf(mxt, sc[t][r]);
+        return fmaxf(mxt, __shfl_xor(mxt, 32));
+    };
+
     float16v sa[2] = {float16v{}, float16v{}}, sb[2] = {float16v{}, float16v{}};
+    // pipelined: the maximum of the tile whose scores are ready, taken while
+    // the previous tile's second product runs
+    float mx_next = -INFINITY;
     if (T::PIPE && nblk > 0) {
         wait_vmcnt0();
         lds_barrier();
@@ -271,6 +301,7 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
 #pragma unroll
             for (int t = 0; t < 2; t++)
                 score_mfma(smem, ks, t, sa[t]);
+        mx_next = tile_max(sa, 0);
     }
 
     // key tile j, where J = j mod U
@@ -311,28 +342,7 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
                     score_mfma(k_tile, ks, t, s[t]);
         }
 
-        // Tile maximum of the raw scores.  Only tiles that reach past Lk or
-        // across the causal diagonal of the wave's first query mask anything
-        // (a uniform branch: the others skip the per-key test).
-        const bool edge = kv0 + BKV > p.Lk || (CAUSAL && kv0 + BKV - 1 > q0 + shift);
-        float mx = -INFINITY;
-        if (edge) {
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = key < p.Lk && (!CAUSAL || key <= query + shift);
-                    s[t][r] = vis ? s[t][r] : -INFINITY;
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int r = 0; r < 16; r++)
-                mx = fmaxf(mx, s[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx = T::PIPE ? mx_next : tile_max(s, j);
 
         // Lazy rescale: the weights are taken relative to a reference m that
         // moves only when some row's maximum exceeds it by more than 2^8, so
@@ -408,6 +418,10 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
                     half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], acc[dt], 0, 0, 0);
             }
+        }
+        if constexpr (T::PIPE) {
+            if (j + 1 < nblk)
+                mx_next = tile_max(sn, j + 1);
         }
     };
 

@@ -57,6 +57,22 @@ TRAFFIC_BYTES = {
     ("sq8192", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 1767697536,
     # FETCH_SIZE 304672.8 KiB x 2.0 + WRITE_SIZE 90816 KiB x 1.0 (profiles/)
     ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 716965504,
+    # the GEMM on the packed copies: FETCH_SIZE 28684.6 KiB x 2.0 + WRITE_SIZE
+    # 60697.9 KiB x 1.0 (the operand copy kernel before it: 8344.3 and
+    # 16212.3 KiB)
+    ("ragged3001x5003x1031", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 120900672,
+    # FETCH_SIZE 6200.0 KiB x 2.0 + WRITE_SIZE 4096.0 KiB x 1.0
+    ("sq1024", "pipe_64x64x64_s4_w2x2_mi16_c0", "3472bf1c22d27237"): 16891904,
+    # FETCH_SIZE 424.0 KiB x 2.0 + WRITE_SIZE 256.0 KiB x 1.0
+    ("sq256", "pipe_64x64x64_s2_w2x2_mi16_c0", "e89e48b0ab050bdf"): 1130496,
+    # FETCH_SIZE 786691.7 KiB x 2.0 + WRITE_SIZE 131072.0 KiB x 1.0
+    ("sq8192_nt", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 1745362240,
+    # FETCH_SIZE 790693.9 KiB x 2.0 + WRITE_SIZE 139264.0 KiB x 1.0
+    ("sq8192_tn", "pipe_256x256x64_s2_w2x4_mi16_c2", "e39902fa8b058ae8"): 1761947392,
+    # FETCH_SIZE 394135.8 KiB x 2.0 + WRITE_SIZE 262144.0 KiB x 1.0
+    ("sq8192_i8", "i8_pipe_256x256x128_s2_w2x4_mi16_c2", "b460cd43105ba436"): 1075625600,
+    # FETCH_SIZE 393547.1 KiB x 2.0 + WRITE_SIZE 262144.0 KiB x 1.0
+    ("sq8192_i8_nt", "i8_pipe_256x256x128_s2_w2x4_mi16_c2", "b460cd43105ba436"): 1074419904,
 }
 
 
@@ -65,6 +81,10 @@ TRAFFIC_BYTES = {
 ATTN_TRAFFIC_BYTES = {
     # FETCH_SIZE 49308.5 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
     ("attn_b2h16l4096d128", "0c9e527802ea2d50"): 135062528,
+    # FETCH_SIZE 78275.2 KiB x 2.0 + WRITE_SIZE 33280.0 KiB x 1.0
+    ("attn_b2h16l4096d128_causal", "0c9e527802ea2d50"): 194386432,
+    # FETCH_SIZE 24626.5 KiB x 2.0 + WRITE_SIZE 16896.0 KiB x 1.0
+    ("attn_b4h16l2048d64", "0c9e527802ea2d50"): 67736576,
 }
 
 

@@ -79,12 +79,12 @@ TRAFFIC_BYTES = {
 # The same for the fused attention kernel, keyed by workload and a digest of
 # its sources.
 ATTN_TRAFFIC_BYTES = {
-    # FETCH_SIZE 49308.5 KiB x 2.0 + WRITE_SIZE 33280 KiB x 1.0 (profiles/)
-    ("attn_b2h16l4096d128", "0c9e527802ea2d50"): 135062528,
-    # FETCH_SIZE 78275.2 KiB x 2.0 + WRITE_SIZE 33280.0 KiB x 1.0
-    ("attn_b2h16l4096d128_causal", "0c9e527802ea2d50"): 194386432,
+    # FETCH_SIZE 49298.0 KiB x 2.0 + WRITE_SIZE 33280.0 KiB x 1.0 (profiles/)
+    ("attn_b2h16l4096d128", "047d310d5a7a704f"): 135041024,
+    # FETCH_SIZE 80101.0 KiB x 2.0 + WRITE_SIZE 33285.4 KiB x 1.0
+    ("attn_b2h16l4096d128_causal", "047d310d5a7a704f"): 198131136,
     # FETCH_SIZE 24626.5 KiB x 2.0 + WRITE_SIZE 16896.0 KiB x 1.0
-    ("attn_b4h16l2048d64", "0c9e527802ea2d50"): 67736576,
+    ("attn_b4h16l2048d64", "047d310d5a7a704f"): 67736576,
 }
 
 

@@ -331,15 +331,29 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         const char *k_next = smem + ((j + 1) % T::KST) * T::BYTES;   // stale on the last tile
         const char *vs_tile = smem + T::KST * T::BYTES + (JV & 1) * T::BYTES;
         const int kv0 = j * BKV;
+        // Causal: a tile whose first key lies past the diagonal of the wave's
+        // last query is masked for every query of the wave (a wave-uniform
+        // test). Its weights are all 0, so the wave skips its scores, exp2
+        // and V product, which would only add zeros; so do the later tiles.
+        // The wave still takes part in the copies and barriers.
+        const bool dead = CAUSAL && kv0 > q0 + 31 + shift;
+        const bool dead_next = CAUSAL && kv0 + BKV > q0 + 31 + shift;
         if constexpr (!T::PIPE) {
-            const char *k_tile = smem + (j % T::KST) * T::BYTES;
-            s[0] = float16v{};
-            s[1] = float16v{};
+            if (!dead) {
+                const char *k_tile = smem + (j % T::KST) * T::BYTES;
+                s[0] = float16v{};
+                s[1] = float16v{};
 #pragma unroll
-            for (int ks = 0; ks < T::DK; ks++)
+                for (int ks = 0; ks < T::DK; ks++)
 #pragma unroll
-                for (int t = 0; t < 2; t++)
-                    score_mfma(k_tile, ks, t, s[t]);
+                    for (int t = 0; t < 2; t++)
+                        score_mfma(k_tile, ks, t, s[t]);
+            }
+        }
+        if (dead) {
+            if constexpr (T::PIPE)
+                mx_next = -INFINITY;   // the next tile's maximum: nothing visible
+            return;
         }
 
         const float mx = T::PIPE ? mx_next : tile_max(s, j);
@@ -385,22 +399,36 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
             sn[1] = float16v{};
         }
         // pipelined: 2 DK MFMAs and 32 weights, 32 / (2 DK) weights per MFMA
+        // (the MFMAs left out when the next tile is dead for the wave)
         constexpr int NM = 2 * T::DK, WPM = 32 / NM;
-        half8 kf_next = T::PIPE ? *(const half8 *)(k_next + koff[0]) : half8{};
+        auto weights_and_scores = [&](auto mf) {
+            constexpr bool MF = decltype(mf)::value;
+            half8 kf_next = MF ? *(const half8 *)(k_next + koff[0]) : half8{};
 #pragma unroll
-        for (int i = 0; i < (T::PIPE ? NM : 0); i++) {
-            const int ks = i / 2, t = i % 2;
-            const half8 kf = kf_next;
-            if (i + 1 < NM)
-                kf_next = *(const half8 *)(k_next + koff[(i + 1) / 2] + ((i + 1) % 2) * 32 * T::ROWB);
-            sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sn[t], 0, 0, 0);
+            for (int i = 0; i < NM; i++) {
+                if constexpr (MF) {
+                    const int ks = i / 2, t = i % 2;
+                    const half8 kf = kf_next;
+                    if (i + 1 < NM)
+                        kf_next = *(const half8 *)(k_next + koff[(i + 1) / 2] +
+                                                   ((i + 1) % 2) * 32 * T::ROWB);
+                    sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sn[t], 0, 0, 0);
+                }
 #pragma unroll
-            for (int u = 0; u < WPM; u++) {
-                const int e = i * WPM + u, tt = e / 16, r = e % 16;
-                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], p.scale_log2, -m_w));
-                rs += w;
-                pf[2 * tt + r / 8][r % 8] = (_Float16)w;
+                for (int u = 0; u < WPM; u++) {
+                    const int e = i * WPM + u, tt = e / 16, r = e % 16;
+                    const float w =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], p.scale_log2, -m_w));
+                    rs += w;
+                    pf[2 * tt + r / 8][r % 8] = (_Float16)w;
+                }
             }
+        };
+        if constexpr (T::PIPE) {
+            if (!dead_next)
+                weights_and_scores(std::true_type{});
+            else
+                weights_and_scores(std::false_type{});
         }
         l += rs;
 
@@ -421,7 +449,7 @@ __global__ void __launch_bounds__(THREADS, 1) attn_fwd(AttnParams p)
         }
         if constexpr (T::PIPE) {
             if (j + 1 < nblk)
-                mx_next = tile_max(sn, j + 1);
+                mx_next = dead_next ? -INFINITY : tile_max(sn, j + 1);
         }
     };
 

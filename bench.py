@@ -18,10 +18,8 @@ level), then whole-job TFLOP/s (2MNK per step) over exactly K timed steps
 after W warm-up steps, the dominant kernel's MFMA roofline fraction measured
 with HIP events on the launch stream, the matrix cores' own rate on the
 workload's values, the board's power and clock under load, launches timed
-alone after a scrub of the caches ("cold"), torch's library call for the same
-operation timed in alternation with the step on the same tensors
-("library"), and the CPU oracle timed on the whole product on the host
-cores.  The GPU's
+alone after a scrub of the caches ("cold"), and the CPU oracle timed on the
+whole product on the host cores.  The GPU's
 output of the first call is compared with that oracle output entry by entry
 (the parity gate); a failing gate prints no throughput.
 """
@@ -156,143 +154,6 @@ def mfma_ceiling(a_bits, b_bits, stream, iters=20000, workgroups=1024, reps=3):
     return out
 
 
-def alternate(impls, stream, flop, rounds=6, target_ms=50.0):
-    """Rounds of loops of back-to-back launches of each zero-argument call in
-    `impls`, the order reversed every other round, each loop between its own
-    pair of events on `stream` and about `target_ms` long: the median rate of
-    each, in units of 1e12 (flop per call)."""
-    import torch
-    names = list(impls)
-    n = {}
-    for k in names:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        impls[k]()
-        e0.record(stream)
-        impls[k]()
-        e1.record(stream)
-        e1.synchronize()
-        n[k] = max(3, int(np.ceil(target_ms / max(e0.elapsed_time(e1), 1e-3))))
-    rates = {k: [] for k in names}
-    for r in range(rounds):
-        for k in (names if r % 2 == 0 else names[::-1]):
-            for _ in range(3):
-                impls[k]()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(n[k]):
-                impls[k]()
-            e1.record(stream)
-            e1.synchronize()
-            rates[k].append(flop / (e0.elapsed_time(e1) / n[k] / 1e3) / 1e12)
-    return {k: float(np.median(v)) for k, v in rates.items()}
-
-
-def blas_backend():
-    import torch
-    try:
-        return str(torch.backends.cuda.preferred_blas_library()).split(".")[-1]
-    except Exception:  # noqa: BLE001 - informational only
-        return None
-
-
-def library_gemm(w, A, B, bias, C, step, stream, flop, rounds):
-    """The same product through torch's library GEMM on the same device
-    tensors (the library picks its own kernel), timed in alternation with
-    `step`: context for the kernel's rate, not part of the hot path.  The
-    library's result is compared with C (which holds `step`'s output)."""
-    import torch
-    M, N, K = w["M"], w["N"], w["K"]
-    la = torch.as_strided(A, (M, K), (1, w["lda"]) if w["op_a"] else (w["lda"], 1))
-    lb = torch.as_strided(B, (K, N), (1, w["ldb"]) if w["op_b"] else (w["ldb"], 1))
-    C2 = torch.empty_like(C)
-    # (call, description) candidates, the form that writes into C2 first
-    if w["c_dtype"] == "i32":
-        cands = [(lambda: torch._int_mm(la, lb, out=C2), "torch._int_mm"),
-                 (lambda: torch._int_mm(la, lb), "torch._int_mm (allocates its output)")]
-    elif w["c_dtype"] == "f32":
-        cands = [(lambda: torch.mm(la, lb, out_dtype=torch.float32, out=C2),
-                  "torch.mm(out_dtype=float32)"),
-                 (lambda: torch.mm(la, lb, out_dtype=torch.float32),
-                  "torch.mm(out_dtype=float32) (allocates its output)")]
-    elif bias is not None:
-        b16 = bias.half()
-        what = "torch._addmm_activation (bias + ReLU in the library's epilogue, bias rounded to fp16)"
-        cands = [(lambda: torch._addmm_activation(b16, la, lb, out=C2), what),
-                 (lambda: torch._addmm_activation(b16, la, lb), what + " (allocates its output)")]
-    else:
-        cands = [(lambda: torch.matmul(la, lb, out=C2), "torch.matmul")]
-    rec = {"blas": blas_backend()}
-    call = None
-    for fn, what in cands:
-        try:
-            res = fn()
-            torch.cuda.synchronize()
-        except Exception as e:  # noqa: BLE001 - a library without this form
-            rec["error"] = repr(e)[:200]
-            continue
-        call, rec["call"] = fn, what
-        rec.pop("error", None)
-        if res is not None and res.data_ptr() != C2.data_ptr():
-            C2 = res
-        break
-    if call is None:
-        return rec
-    step()
-    torch.cuda.synchronize()
-    if w["c_dtype"] == "i32":
-        rec["identical_output"] = bool(torch.equal(C, C2))
-    else:
-        rec["max_abs_diff"] = float((C.float() - C2.float()).abs().max())
-    r = alternate({"ours": step, "library": call}, stream, flop, rounds)
-    rec.update({"rounds": rounds, "value": round(r["library"], 2),
-                "unit": "TOPS" if w["c_dtype"] == "i32" else "TFLOP/s",
-                "ours_in_alternation": round(r["ours"], 2),
-                "ours_over_library": round(r["ours"] / r["library"], 4)})
-    return rec
-
-
-def library_attention(w, tq, tk, tv, to, step, stream, flop, rounds):
-    """The same attention through torch's scaled_dot_product_attention,
-    restricted to its flash backend (no fallback to the unfused math path),
-    on the same device tensors, timed in alternation with `step`; its output
-    is compared with `to` (which holds `step`'s)."""
-    import torch
-    from torch.nn.attention import SDPBackend, sdpa_kernel
-    B, H, Hkv, Lq, Lk, d = (w[k] for k in ("B", "H", "Hkv", "Lq", "Lk", "d"))
-
-    def view(t, hh, L, st):
-        return torch.as_strided(t.view(torch.float16), (B, hh, L, d), tuple(st) + (1,))
-
-    q, k, v = view(tq, H, Lq, w["qs"]), view(tk, Hkv, Lk, w["ks"]), view(tv, Hkv, Lk, w["vs"])
-    rec = {"call": "torch.nn.functional.scaled_dot_product_attention, flash backend only"}
-    if w["causal"] and Lq != Lk:
-        rec["error"] = "the library's causal mask is aligned at the top left; this one is not"
-        return rec
-    gqa = {"enable_gqa": True} if Hkv != H else {}
-
-    def call():
-        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-            return torch.nn.functional.scaled_dot_product_attention(
-                q, k, v, is_causal=bool(w["causal"]), scale=1.0 / np.sqrt(d), **gqa)
-    try:
-        o2 = call()
-        torch.cuda.synchronize()
-    except Exception as e:  # noqa: BLE001 - a build without the flash backend
-        rec["error"] = repr(e)[:200]
-        return rec
-    step()
-    torch.cuda.synchronize()
-    ours = to.view(torch.float16).view(B, H, Lq, d)
-    rec["max_abs_diff"] = float((ours.float() - o2.float()).abs().max())
-    r = alternate({"ours": step, "library": call}, stream, flop, rounds)
-    rec.update({"rounds": rounds, "value": round(r["library"], 2), "unit": "TFLOP/s",
-                "ours_in_alternation": round(r["ours"], 2),
-                "ours_over_library": round(r["ours"] / r["library"], 4)})
-    return rec
-
-
 def device_info():
     import torch
     p = torch.cuda.get_device_properties(0)
@@ -379,9 +240,6 @@ def parse():
     ap.add_argument("--cold-launches", type=int, default=10, metavar="N",
                     help="GEMM workloads: also time N launches each after a 512 MiB scrub of "
                          "the caches (0: skip)")
-    ap.add_argument("--library-rounds", type=int, default=6, metavar="N",
-                    help="rounds of alternating loops against torch's library call for the "
-                         "same operation on the same tensors (0: skip)")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the matrix cores' rate (tg_mfma_ceiling) on the "
                          "workload's A and B values and on zero operands, then exit")
@@ -446,8 +304,7 @@ def main():
             return 1
         line["fused"] = {k: fused[k] for k in ("value", "unit", "ms_per_step", "config",
                                                "loops", "roofline", "cpu_baseline",
-                                               "mfma_ceiling", "board_under_load", "cold",
-                                               "library")}
+                                               "mfma_ceiling", "board_under_load", "cold")}
     print(json.dumps(line))
     return 0
 
@@ -607,9 +464,6 @@ def gemm_record(a, name, steps, warmup):
         ceiling.update({"operands": vals + " each of A and B (their first elements)",
                         "kernel_mfma": shape, "frac_of_ceiling": round(achieved / own, 4)})
 
-    library = (library_gemm(w, A, B, bias, C, step, stream, flop, a.library_rounds)
-               if a.library_rounds > 0 else None)
-
     # ---- CPU oracle: the whole product on the host cores, then the gate
     threads = oracle.default_threads()
     cpu = None
@@ -697,7 +551,6 @@ def gemm_record(a, name, steps, warmup):
         "mfma_ceiling": ceiling,
         "board_under_load": at_sampled_clock(board, achieved, peak),
         "cold": cold,
-        "library": library,
     }
 
 
@@ -800,9 +653,6 @@ def bench_attention(a):
                         "kernel_mfma": "32x32x16",
                         "frac_of_ceiling": round(achieved / ceiling["tflops_32x32x16"], 4)})
 
-    library = (library_attention(w, tq, tk, tv, to, step, stream, flop, a.library_rounds)
-               if a.library_rounds > 0 else None)
-
     # ---- CPU oracle baseline: whole query rows, sampled
     cpu = None
     if not a.no_cpu:
@@ -849,7 +699,6 @@ def bench_attention(a):
         "cpu_baseline": cpu,
         "mfma_ceiling": ceiling,
         "board_under_load": at_sampled_clock(board, achieved, PEAK_TFLOPS),
-        "library": library,
     }
     print(json.dumps(line))
     return 0

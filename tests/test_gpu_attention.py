@@ -111,6 +111,11 @@ CASES = [
     (1, 1, 1, 1, 77, 64, True),
     (1, 2, 1, 257, 64, 128, False),
     (1, 1, 1, 130, 0, 64, False),        # no keys at all
+    # causal over several query blocks, odd key-tile counts: the waves skip
+    # the tiles past their own diagonal, in both halves of the unrolled loop
+    (1, 2, 2, 1000, 1000, 128, True),
+    (1, 3, 3, 700, 900, 128, True),
+    (1, 2, 1, 900, 700, 64, True),
 ]
 
 

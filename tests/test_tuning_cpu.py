@@ -282,6 +282,11 @@ def model_choice(rows, M, N, K, cands, pad):
     return min(cands, key=t)
 
 
+# Configurations the dispatcher runs only on the exact shapes its table
+# lists (no cost-model row): the 4-wave schedule-3 kernel.
+TABLE_ONLY = {26}
+
+
 def test_model_rows_are_valid():
     rows = costmodel.read_model()
     assert rows
@@ -296,9 +301,10 @@ def test_model_rows_are_valid():
         # only the register-staged kernels run on padded operands
         assert not (pad and info["direct_lds"])
     for c in CONFIGS.values():
-        if "single_" in c["name"]:
+        if "single_" in c["name"] or c["id"] in TABLE_ONLY:
             # the single-stage reference kernels are for checking the others,
-            # never chosen by the dispatcher, so they have no model row
+            # never chosen by the dispatcher, so they have no model row; the
+            # table-only kernels are chosen by exact shape only
             assert not any(k[0] == c["id"] for k in rows), c["name"]
             continue
         assert (c["id"], False) in rows or (c["id"], True) in rows, c["name"]

@@ -204,10 +204,13 @@ template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_, int
 struct Cfg {
     static constexpr int ES = ES_;
     // copy issue: 0 burst after the barrier, 1 spread, 2 interleaved with the
-    // MFMA rows that follow the barrier.  With A stored K x M (TA) schedule 2
-    // spills registers inside the K loop (an mn-major A block is two
-    // transpose reads and has its own offset register), so those
-    // orientations keep schedule 0.
+    // MFMA rows that follow the barrier, 3 spread as in 1 with the next
+    // k-step's fragment reads placed one by one between the MFMAs and the
+    // MFMAs written as assembly on accumulators pinned to their registers
+    // (the one-wave-per-SIMD 16x16x32 kernels, see mfma()).  With A stored
+    // K x M (TA) schedule 2 spills registers inside the K loop (an mn-major A
+    // block is two transpose reads and has its own offset register), so
+    // those orientations keep schedule 0.
     static constexpr int SCHED = SCHED_ == 2 && TA_ ? 0 : SCHED_;
     // Operand orientation: TA = 1 when A is stored K x M (the product uses its
     // transpose), TB = 1 when B is stored N x K.  The LDS tile of an operand is
@@ -369,10 +372,24 @@ __device__ __forceinline__ void read_frags(const char *as, const char *bs, int k
 }
 
 // half8 is the 16-byte fragment container for both element sizes.
+//
+// Schedule 3 issues the 16x16x32 MFMA as assembly with the accumulator tied
+// in place ("+a": the same accumulation registers in and out).  A wave of
+// these kernels holds a 128 x 128 fp32 tile, all 256 accumulation registers;
+// with the builtin and the fragment reads placed between the MFMAs, the
+// register allocator moved hundreds of accumulator registers per loop body
+// through the other registers.  The compiler does not see these MFMAs, so the
+// kernel keeps their hazards itself: the fragment registers they read come
+// from LDS reads that the compiler's waits cover, each accumulator is
+// written by one MFMA per k-step (64 MFMAs apart), and acc_fence() puts wait
+// states between the accumulators' other writers and readers and the MFMAs.
 template <class C>
 __device__ __forceinline__ typename C::acc_t mfma(half8 b, half8 a, typename C::acc_t c)
 {
-    if constexpr (C::ES == 1) {
+    if constexpr (C::ES == 2 && C::MI == 16 && C::SCHED == 3) {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+        return c;
+    } else if constexpr (C::ES == 1) {
         const int4v bi = __builtin_bit_cast(int4v, b), ai = __builtin_bit_cast(int4v, a);
         if constexpr (C::MI == 16)
             return __builtin_amdgcn_mfma_i32_16x16x64_i8(bi, ai, c, 0, 0, 0);
@@ -382,6 +399,28 @@ __device__ __forceinline__ typename C::acc_t mfma(half8 b, half8 a, typename C::
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
     } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    }
+}
+
+// Schedule 3: wait states between the assembly MFMAs and the compiler's own
+// accesses of the accumulators (their zeroing before the K loop, their reads
+// in the epilogue).  Every accumulator passes through an empty statement
+// ordered after (AFTER) or before the s_nop, so no such access can move to
+// the other side of it; 48 wait states cover the longest MFMA-to-VALU rule
+// of the 16x16x32 shape.
+template <class C, bool AFTER>
+__device__ __forceinline__ void acc_fence(typename C::acc_t (&acc)[C::MT][C::NT])
+{
+    if constexpr (C::SCHED == 3) {
+        if constexpr (AFTER)
+            asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");
+#pragma unroll
+        for (int i = 0; i < C::MT; i++)
+#pragma unroll
+            for (int j = 0; j < C::NT; j++)
+                asm volatile("" : "+a"(acc[i][j]));
+        if constexpr (!AFTER)
+            asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");
     }
 }
 
@@ -812,6 +851,37 @@ __device__ __forceinline__ void mfma_window(const Params &p, DirectLoader<C> &ld
     }
 }
 
+// Schedule 3: MFMAs [I, HI) of the k-step as mfma_window, with the fragment
+// reads of k-step ksn of tiles (as, bs) placed between them: read r (the B
+// blocks first, then the A blocks in row order, the order in which the next
+// k-step's rows need them) after MFMA IB + (r + 1) RI - 1, each pinned to its
+// place.  One wave per SIMD has no second wave to issue its reads while its
+// MFMAs wait; issued in one burst they filled the LDS command FIFO.
+template <class C, int W, int OFF, int I, int HI, int P, int IB, int RI>
+__device__ __forceinline__ void mfma_window_rd(const Params &p, DirectLoader<C> &ld, int kt0,
+                                               int nk, int m0, int n0, PipeState<C> &st,
+                                               const char *as, const char *bs, int ksn)
+{
+    if constexpr (I < HI) {
+        constexpr int mt = I / C::NT, nt = I % C::NT;
+        st.acc[mt][nt] = mfma<C>(st.fb[P][nt], st.fa[P][mt], st.acc[mt][nt]);
+        constexpr int q = I - IB + 1;
+        if constexpr (q > 0 && q % RI == 0 && q / RI <= C::MT + C::NT) {
+            constexpr int r = q / RI - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (r < C::NT)
+                st.fb[1 - P][r] = read_block<C, C::B_KMAJ, C::BN>(bs, ksn, st.b_off, r);
+            else
+                st.fa[1 - P][r - C::NT] =
+                    read_block<C, C::A_KMAJ, C::BM>(as, ksn, st.a_off, r - C::NT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        window_copies<C, W, OFF>(p, ld, kt0, nk, m0, n0);
+        mfma_window_rd<C, W, OFF + 1, I + 1, HI, P, IB, RI>(p, ld, kt0, nk, m0, n0, st, as, bs,
+                                                            ksn);
+    }
+}
+
 // LDS read instructions of one fragment block: 1 (k-major, ds_read_b128) or
 // 2 (mn-major, two transpose reads).
 template <class C, bool KMAJ>
@@ -946,23 +1016,39 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
     constexpr bool BARRIER = ks + 1 == C::KS && (!FINAL || S + 1 < C::STAGES);
     if constexpr (C::ROLL) {
         pipe_kstep_roll<C, U, FINAL>(p, ld, smem, kt0, nk, m0, n0, st);
-    } else if constexpr (C::SCHED == 1) {
+    } else if constexpr (C::SCHED == 1 || C::SCHED == 3) {
         // position of this k-step's first MFMA in window S-1
         constexpr int OFF = H + ks * NMF;
+        constexpr int NB = C::MT + C::NT;   // fragment blocks per k-step
         if constexpr (!BARRIER) {
-            if constexpr (ks + 1 < C::KS)
-                read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off,
-                              st.b_off, st.fa[1 - P], st.fb[1 - P]);
-            mfma_window<C, S - 1, OFF, 0, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
+            if constexpr (C::SCHED == 3 && ks + 1 < C::KS) {
+                static_assert(NMF >= NB, "a read slot per block");
+                mfma_window_rd<C, S - 1, OFF, 0, NMF, P, 0, NMF / NB>(
+                    p, ld, kt0, nk, m0, n0, st, a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1);
+            } else {
+                if constexpr (ks + 1 < C::KS)
+                    read_frags<C>(a_stage<C, S>(smem), b_stage<C, S>(smem), ks + 1, st.a_off,
+                                  st.b_off, st.fa[1 - P], st.fb[1 - P]);
+                mfma_window<C, S - 1, OFF, 0, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P],
+                                                   st.acc);
+            }
         } else {
             constexpr int SN = (S + 1) % C::STAGES;
             mfma_window<C, S - 1, OFF, 0, H>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<(C::STAGES - 2) * C::LOADS>();   // my copies of the next step landed
             lds_barrier();                               // everyone's did; stage S is free
-            read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
-                          st.fa[1 - P], st.fb[1 - P]);
-            mfma_window<C, S, 0, H, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
+            if constexpr (C::SCHED == 3) {
+                // the next stage's first fragments between the rest of this
+                // k-step's MFMAs
+                static_assert(NMF - H >= NB, "a read slot per block");
+                mfma_window_rd<C, S, 0, H, NMF, P, H, (NMF - H) / NB>(
+                    p, ld, kt0, nk, m0, n0, st, a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0);
+            } else {
+                read_frags<C>(a_stage<C, SN>(smem), b_stage<C, SN>(smem), 0, st.a_off, st.b_off,
+                              st.fa[1 - P], st.fb[1 - P]);
+                mfma_window<C, S, 0, H, NMF>(p, ld, kt0, nk, m0, n0, st.fa[P], st.fb[P], st.acc);
+            }
         }
     } else if constexpr (ks + 1 < C::KS) {
         // next k-step of the same K step: prefetch its fragments
@@ -989,7 +1075,7 @@ __device__ __forceinline__ void pipe_kstep(const Params &p, DirectLoader<C> &ld,
 template <class C>
 constexpr int prologue_after_step0()
 {
-    if constexpr (C::SCHED == 1) {
+    if constexpr (C::SCHED == 1 || C::SCHED == 3) {
         int early = 0;
         for (int t = 0; t < C::LOADS; t++)
             early += Spread<C>::pos(t) < Spread<C>::H;
@@ -1066,10 +1152,11 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
 
     const int nk = (p.K + C::BK - 1) / C::BK;
     if (nk > 0) {
+        acc_fence<C, false>(st.acc);
         fragment_offsets<C>(wm, wn, st.a_off, st.b_off);
         DirectLoader<C> ld;
         ld.init(p, smem, m0, n0);
-        if constexpr (C::SCHED == 1) {
+        if constexpr (C::SCHED == 1 || C::SCHED == 3) {
             // steps 0 .. STAGES-2 whole; of step STAGES-1 the copies whose
             // window position precedes the loop (the rest come from window -1
             // of the first loop body)
@@ -1100,6 +1187,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) gemm_pipe(Params p)
         // wave finish its fragment reads before LDS is reused for the epilogue
         wait_vmcnt<0>();
         lds_barrier();
+        acc_fence<C, true>(st.acc);
     }
     epilogue<C, OutT, BIAS>(p, smem, m0 + wm * C::TM, n0 + wn * C::TN, st.acc);
 }

@@ -283,8 +283,8 @@ def model_choice(rows, M, N, K, cands, pad):
 
 
 # Configurations the dispatcher runs only on the exact shapes its table
-# lists (no cost-model row): the 4-wave schedule-3 kernel.
-TABLE_ONLY = {26}
+# lists (no cost-model row): none at present.
+TABLE_ONLY = set()
 
 
 def test_model_rows_are_valid():

@@ -299,6 +299,8 @@ typedef struct {
     int lds_bytes;                   /* LDS per workgroup */
     int ops;                         /* orientations compiled: bit (1 << (2*op_a + op_b)) */
     int elem_bytes;                  /* operand element: 2 fp16, 1 int8 (int32 C) */
+    int whole_k;                     /* 1: runs only K that is a multiple of block_k
+                                        (tg_config_supports answers 0 otherwise) */
     const char *name;                /* static string */
 } tg_config_desc;
 
@@ -309,7 +311,8 @@ int tg_num_configs(void);
 tg_status tg_config_info(int id, tg_config_desc *out);
 
 /* Whether configuration `id` can run this problem (orientation compiled;
- * alignment and leading-dimension requirements of its load path): 1 yes,
+ * alignment and leading-dimension requirements of its load path; K in whole
+ * K steps where whole_k is set): 1 yes,
  * 0 no, -1 invalid arguments.  Arguments as for tg_gemm_ex. */
 int tg_config_supports(int id, tg_op op_a, tg_op op_b, const void *A, const void *B,
                        const float *bias, const void *C, int64_t M, int64_t N, int64_t K,

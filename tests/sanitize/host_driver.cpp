@@ -249,9 +249,9 @@ int main(int argc, char **argv)
     tg_config_desc d;
     for (int i = 0; i < tg_num_configs(); i++)
         if (tg_config_info(i, &d) == TG_SUCCESS)
-            printf("config %d %d %d %d %d %d %d %d %d %d %d %d %s\n", d.id, d.block_m, d.block_n,
-                   d.block_k, d.stages, d.waves_m, d.waves_n, d.mfma, d.direct_lds, d.lds_bytes,
-                   d.ops, d.elem_bytes, d.name);
+            printf("config %d %d %d %d %d %d %d %d %d %d %d %d %d %s\n", d.id, d.block_m,
+                   d.block_n, d.block_k, d.stages, d.waves_m, d.waves_n, d.mfma, d.direct_lds,
+                   d.lds_bytes, d.ops, d.elem_bytes, d.whole_k, d.name);
     invalid_arguments();
     attention_arguments();
     plans();

@@ -18,6 +18,7 @@ namespace tg {
 #define TG_STUB_LDS(BM, BN, BK, ST, ES) ((ST) * ((BM) * (BK) + (BK) * (BN)) * (ES))
 #define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) == 2, TG_STUB_LDS(BM, BN, BK, ST, ES), OPS, ES,        \
+     (SCH) == 3,                                                                                 \
      (KIND == 2 ? (ES == 1 ? "i8_pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI \
                              "_c" #SCH                                                     \
                            : "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI   \

@@ -8,7 +8,9 @@ current K step did not write would show up as NaN or as a different value.
 
 Each configuration is named in tg_gemm_ws, so a direct-copy configuration
 runs on packed copies of the operands it cannot take as passed (odd K or N)
-and the register-staged and single-stage ones on the operands as passed.
+and the register-staged and single-stage ones on the operands as passed. The
+configurations that serve only K in whole K steps (copy schedule 3) run the
+same M and N with K rounded up to a whole number of steps.
 """
 import sys
 
@@ -77,9 +79,12 @@ def run(L, info, A, B, M, N, K, op_a, op_b, c_dtype, bias):
 def cases(info, shapes):
     """(M, N, K, op_a, op_b, c_dtype, fused) of the configuration's runs:
     orientations rotate over the shapes (as stored when the configuration is
-    not compiled for the rotated one)."""
+    not compiled for the rotated one); K rounded up to whole K steps for the
+    configurations that need them (M and N stay odd)."""
     out = []
     for j, (M, N, K) in enumerate(shapes):
+        if info["whole_k"]:
+            K = -(-K // info["block_k"]) * info["block_k"]
         op_a, op_b = OPS[j % 4]
         if not info["ops"] >> (2 * op_a + op_b) & 1:
             op_a, op_b = 0, 0

@@ -55,7 +55,8 @@ F16_CASES = [(300, 520, 264, 1, 3, (0, 0, 0)),      # padded leading dimensions
              (129, 257, 131, 3, 5, (1, 3, 1)),      # odd K, unaligned bases
              (77, 45, 29, 0, 0, (0, 0, 0)),         # packed rows, lengths not whole chunks
              (1, 9, 7, 0, 0, (0, 0, 0)),            # rows shorter than a chunk
-             (640, 384, 1031, 1, 0, (2, 0, 0))]
+             (640, 384, 1031, 1, 0, (2, 0, 0)),
+             (264, 392, 320, 1, 3, (1, 0, 0))]      # K in whole 64-deep steps
 
 
 @pytest.mark.parametrize("op_a,op_b", OPS)
@@ -64,8 +65,11 @@ def test_packed_fp16_matches_oracle_and_staged(op_a, op_b):
     tg_gemm_ws, on operands it cannot take as passed: packed copies."""
     n = 0
     for cid in direct_configs(2, op_a, op_b):
-        name = tg.tg_config_info(cid)["name"]
+        info = tg.tg_config_info(cid)
+        name = info["name"]
         for (M, N, K, pa, pb, offs) in F16_CASES:
+            if info["whole_k"] and K % info["block_k"]:
+                continue        # runs only K in whole K steps
             lda = (M if op_a else K) + pa
             ldb = (K if op_b else N) + pb
             for kind, c_dtype, fused in [("uniform", "f32", False), ("int", "f16", True),
@@ -112,9 +116,12 @@ def run_i8_ws(As, Bs, M, N, K, op_a, op_b, lda, ldb, offs, cid, what):
 @pytest.mark.parametrize("op_a,op_b", OPS)
 def test_packed_int8_is_exact(op_a, op_b):
     for cid in direct_configs(1, op_a, op_b):
+        info = tg.tg_config_info(cid)
         for (M, N, K, pa, pb, offs) in [(300, 520, 272, 1, 1, (0, 0)),
                                         (129, 257, 65, 0, 0, (1, 3)),
                                         (100, 70, 1031, 5, 0, (0, 0))]:
+            if info["whole_k"] and K % info["block_k"]:
+                continue
             lda = (M if op_a else K) + pa
             ldb = (K if op_b else N) + pb
             A, B = gen.operands_i8(M, N, K, 6000 + M + N + K)
@@ -156,7 +163,8 @@ class Problem:
         self.cref = oracle.gemm_ref(self.A, self.B, M, N, K)
         # a named direct configuration: always the packed copy of A (and of B
         # when N is not a multiple of 8)
-        self.cid = direct_configs(2, 0, 0)[0]
+        self.cid = [c for c in direct_configs(2, 0, 0)
+                    if not tg.tg_config_info(c)["whole_k"] or K % tg.tg_config_info(c)["block_k"] == 0][0]
         self.ws = torch.empty(((M + K) * (max(K, N) + 8) * 2 + 4096) // 4, dtype=torch.float32,
                               device="cuda")
 

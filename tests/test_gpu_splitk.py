@@ -102,11 +102,14 @@ def configs(es, op_a, op_b):
 @pytest.mark.parametrize("op_a,op_b", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_every_fp16_config_sliced(op_a, op_b):
     """K = 1000 in 3 slices: slice length a multiple of the K step, a ragged
-    last slice; fp32 and fp16 C, with and without bias."""
-    M, N, K = 200, 264, 1000
-    A, B = host_operands(M, N, K, op_a, op_b, "f16", 71)
+    last slice; fp32 and fp16 C, with and without bias. A configuration that
+    runs only K in whole K steps takes K = 1024 (slices of 6, 6 and 4
+    steps) instead."""
+    M, N = 200, 264
     bias = gen.bias_vector(N, 72, integer=True)
     for c in configs(2, op_a, op_b):
+        K = 1024 if c["whole_k"] else 1000
+        A, B = host_operands(M, N, K, op_a, op_b, "f16", 71)
         for dtype, b in (("f32", None), ("f16", bias)):
             what = "config %d %s bias=%s" % (c["id"], dtype, b is not None)
             out = run(A, B, M, N, K, dtype, op_a, op_b, bias=b, config=c["id"], splits=3,

@@ -114,6 +114,8 @@ def test_every_cached_config_is_launched_correctly(tmp_path, spec):
     for c in tg.configs():
         if c["elem_bytes"] != want_es or not c["ops"] >> (2 * sh.op_a + sh.op_b) & 1:
             continue
+        if c["whole_k"] and sh.K % c["block_k"]:
+            continue
         path = str(tmp_path / ("c%d.tgtune" % c["id"]))
         sweep.write_cache(path, {sh.key(): (c["id"], c["name"], 1.0)})
         assert tg.load_tuning(path) == (1, 0)

@@ -127,6 +127,25 @@ def test_direct_path_requirements():
     assert tg.tg_config_supports(d, *args[:4], -1, *args[5:]) == -1
 
 
+def test_whole_k_configuration_needs_k_in_whole_steps():
+    """The schedule-3 kernel (configuration 26, 64-deep K steps) has no test
+    for chunks past K in its copies, so it serves only K that is a multiple
+    of 64, in every orientation; other K goes to the other kernels."""
+    cid = [c["id"] for c in tg.configs() if c["name"] == "pipe_256x256x64_s2_w2x2_mi16_c3"][0]
+    for op_a in (0, 1):
+        for op_b in (0, 1):
+            for K, ok in ((1024, 1), (1088, 1), (1032, 0), (1000, 0), (64, 1), (8, 0)):
+                lda = 1024 if op_a else K
+                ldb = K if op_b else 1024
+                assert tg.tg_config_supports(cid, PA, PB, None, PC, 1024, 1024, K, lda, ldb, 1024,
+                                             F32, op_a=op_a, op_b=op_b) == ok, (op_a, op_b, K)
+    # the dispatcher still serves such K, on another kernel
+    assert tg.tg_select_config(PA, PB, None, PC, 8192, 8192, 8184, 8184, 8192, 8192,
+                               tg.TG_DTYPE_F16) != cid
+    assert tg.tg_select_config(PA, PB, None, PC, 8192, 8192, 8192, 8192, 8192, 8192,
+                               tg.TG_DTYPE_F16) == cid
+
+
 @pytest.mark.parametrize("M,N,K,lda,ldb,fused,direct", [
     (256, 256, 256, 256, 256, False, True),
     (1024, 1024, 1024, 1024, 1024, False, True),

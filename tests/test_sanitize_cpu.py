@@ -97,6 +97,6 @@ def test_host_code_under_sanitizers(host_driver):
     # its configuration table is the library's
     rows = [l.split()[1:] for l in r.stdout.splitlines() if l.startswith("config ")]
     fields = ["id", "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n", "mfma",
-              "direct_lds", "lds_bytes", "ops", "elem_bytes", "name"]
+              "direct_lds", "lds_bytes", "ops", "elem_bytes", "whole_k", "name"]
     lib_rows = [[str(c[f]) for f in fields] for c in tg.configs()]
     assert rows == lib_rows

@@ -50,7 +50,7 @@ class ConfigDesc(ctypes.Structure):
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("mfma", ctypes.c_int), ("direct_lds", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("ops", ctypes.c_int), ("elem_bytes", ctypes.c_int),
-                ("name", ctypes.c_char_p)]
+                ("whole_k", ctypes.c_int), ("name", ctypes.c_char_p)]
 
 
 def load_library(path=LIB_PATH):

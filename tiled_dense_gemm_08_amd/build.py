@@ -141,14 +141,15 @@ def device_asm(path=None):
 
 
 def check_m0(asm_text):
-    """Every M0 use must be `s_mov_b32 m0, sX`, one wait state (`s_nop 0`),
-    then the buffer_load ... lds that consumes it."""
+    """Every M0 use must be a write of it (`s_mov_b32 m0, sX`, or
+    `s_add_u32 m0, sX, imm` in the copies that form the address in M0), one
+    wait state (`s_nop 0`), then the buffer_load ... lds that consumes it."""
     lines = [l.strip() for l in asm_text.splitlines()
              if l.strip() and not l.strip().startswith((";", "."))]
     bad = []
     for i, l in enumerate(lines):
         if re.search(r"\bm0\b", l):
-            ok = (l.startswith("s_mov_b32 m0,") and i + 2 < len(lines)
+            ok = (l.startswith(("s_mov_b32 m0,", "s_add_u32 m0,")) and i + 2 < len(lines)
                   and lines[i + 1] == "s_nop 0"
                   and lines[i + 2].startswith("buffer_load_dword") and lines[i + 2].endswith("lds"))
             if not ok:

@@ -146,6 +146,8 @@ bool supports(const KernelConfig &c, const Problem &p)
 {
     if (!(c.ops & (1 << (2 * p.op_a + p.op_b))) || c.es != elem_size(p))
         return false;
+    if (c.whole_k && p.K % c.bk != 0)
+        return false;
     const OperandShape a{p.op_a == 0, p.M, p.lda, c.bm};
     const OperandShape b{p.op_b == 1, p.N, p.ldb, c.bn};
     if (!c.direct)
@@ -1322,6 +1324,7 @@ tg_status tg_config_info(int id, tg_config_desc *out)
     out->lds_bytes = c.lds_bytes;
     out->ops = c.ops;
     out->elem_bytes = c.es;
+    out->whole_k = c.whole_k;
     out->name = c.name;
     return TG_SUCCESS;
 }

@@ -56,6 +56,7 @@ struct KernelConfig {
     int lds_bytes;
     int ops;          // bit 2*trans_a + trans_b set: that orientation is compiled
     int es;           // operand element size: 2 fp16, 1 int8
+    int whole_k;      // 1: serves only K that is a multiple of bk
     const char *name;
 };
 

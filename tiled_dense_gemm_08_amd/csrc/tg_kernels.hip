@@ -238,6 +238,10 @@ struct Cfg {
     // fragments, refill copies) interleaved with the MFMAs that need no new
     // data instead of issued ahead of them (post_barrier_rows).
     static constexpr bool ROLL = MI_ == 16 && WM_ * WN_ == 8 && (SCHED_ == 0 || SCHED_ == 2);
+    // Schedule 3 serves only K that is a whole number of K steps (the host
+    // checks it): its copies then need no per-lane test for chunks past K,
+    // an instruction per copy that its single wave per SIMD would pay for.
+    static constexpr bool WHOLE_K = SCHED_ == 3;
     static constexpr int A_BYTES = BM * BK * ES;
     static constexpr int B_BYTES = BK * BN * ES;
     static constexpr int KROWB = BK * ES;                  // bytes of a k-major tile row
@@ -598,6 +602,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
                  : "memory");
 }
 
+// dma16 with the LDS address formed in M0 itself, base + IMM: one scalar
+// instruction less per copy (the schedule-3 kernels, one wave per SIMD).
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t base)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(base), "n"(IMM)
+                 : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
@@ -672,7 +687,7 @@ struct OperandCopy {
     // K tail of a k-major tile: this lane's chunk lies past K.
     __device__ __forceinline__ bool dead(int kt, int nk, int K) const
     {
-        if constexpr (KMAJ)
+        if constexpr (KMAJ && !C::WHOLE_K)
             return (kt == nk - 1) && (kc >= K - kt * C::BK);
         else
             return false;
@@ -725,23 +740,31 @@ struct DirectLoader {
         if constexpr (T < C::A_LOADS) {
             const __amdgpu_buffer_rsrc_t ra = ACopy::rsrc((const char *)p.A, p.lda, p.a_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : a_off(p, T, m0);
-            const uint32_t dst = lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024;
+            [[maybe_unused]] const uint32_t dst =
+                lds0 + S * C::A_BYTES + (wave * C::A_LOADS + T) * 1024;
 #ifdef TG_LDS_POISON
             poison16(dst + 16 * (threadIdx.x & 63));   // the bytes this lane's copy writes
             wait_lgkmcnt0();
 #endif
-            dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o, dst);
+            if constexpr (C::SCHED == 3)
+                dma16_at<S * C::A_BYTES + T * 1024>(ra, o, lds0 + wave * C::A_LOADS * 1024);
+            else
+                dma16(ra, a.dead(kt, nk, p.K) ? kOOB : o, dst);
         } else {
             constexpr int t = T - C::A_LOADS;
             const __amdgpu_buffer_rsrc_t rb = BCopy::rsrc((const char *)p.B, p.ldb, p.b_bytes, kt, nk);
             const uint32_t o = KEEP ? voff[T] : b_off(p, t, n0);
-            const uint32_t dst =
+            [[maybe_unused]] const uint32_t dst =
                 lds0 + C::STAGES * C::A_BYTES + S * C::B_BYTES + (wave * C::B_LOADS + t) * 1024;
 #ifdef TG_LDS_POISON
             poison16(dst + 16 * (threadIdx.x & 63));
             wait_lgkmcnt0();
 #endif
-            dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o, dst);
+            if constexpr (C::SCHED == 3)
+                dma16_at<C::STAGES * C::A_BYTES + S * C::B_BYTES + t * 1024>(
+                    rb, o, lds0 + wave * C::B_LOADS * 1024);
+            else
+                dma16(rb, b.dead(kt, nk, p.K) ? kOOB : o, dst);
         }
     }
 
@@ -1806,6 +1829,7 @@ const LaunchFn TG_CAT(kShardLaunch, TG_SHARD)[] = {
 #define TG_CONFIG_ROW(ID, BM, BN, BK, WM, WN, ST, MI, KIND, SCH, OPS, ES)                          \
     {ID, BM, BN, BK, ST, WM, WN, MI, (KIND) == 2,                                    \
      Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>::LDS_BYTES, OPS, ES,                   \
+     Cfg<BM, BN, BK, WM, WN, ST, MI, SCH, 0, 0, ES>::WHOLE_K,                              \
      (KIND == 2 ? (ES == 1 ? "i8_pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI \
                              "_c" #SCH                                                     \
                            : "pipe_" #BM "x" #BN "x" #BK "_s" #ST "_w" #WM "x" #WN "_mi" #MI   \

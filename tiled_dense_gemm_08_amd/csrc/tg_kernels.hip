@@ -497,6 +497,10 @@ __device__ __forceinline__ void store4(char *dst, V v)
     }
 }
 
+// 16 bytes of C at the alignment of its element (fp16; fp32 and int32).
+typedef float chunk16_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef float chunk16_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // Largest power-of-two fraction of the wave tile's rows that fits the budget.
 constexpr int pass_rows(int tm, int fit)
 {
@@ -531,6 +535,10 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
     static_assert((PR * CPR) % 64 == 0, "whole read-back instructions");
     constexpr int RUNS = C::ACC / 4;
     constexpr int MT_PASS = PR / C::MI;
+    constexpr int NIT = PR * CPR / 64;                     // read-back instructions per pass
+    constexpr int BATCH = NIT < 4 ? NIT : 4;
+    static_assert(NIT % BATCH == 0, "whole read-back batches");
+    using chunk_t = typename std::conditional<ES == 2, chunk16_a2, chunk16_a4>::type;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     char *region = smem + wave * REGION;
 
@@ -554,24 +562,43 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
         }
         // LDS -> C, 16 bytes per lane, consecutive lanes along a row.  A wave's
         // LDS accesses complete in order, so no barrier is needed: the region
-        // is private to this wave.
+        // is private to this wave.  The reads go out in batches, outside any
+        // bounds test, so that one wait covers a batch; the pass's rows and
+        // the wave tile's columns wholly inside C (wave-uniform) take their
+        // stores without per-chunk tests, marked non-temporal: C is not read
+        // again here, and a round of tiles writes as much C as an XCD's L2
+        // holds, which as ordinary stores evicts the operand panels the next
+        // round's tiles read.
+        const bool whole = m_base + (pass + 1) * PR <= p.M && n_base + C::TN <= p.N;
 #pragma unroll
-        for (int it = 0; it < PR * CPR / 64; it++) {
-            const int q = it * 64 + lane;
-            const int r = q / CPR, cc = q % CPR;
-            const float4v v = *(const float4v *)(region + r * ROWB + cc * 16);
-            const int row = m_base + pass * PR + r;
-            const int col = n_base + cc * (16 / ES);
-            if (row < p.M) {
+        for (int b0 = 0; b0 < NIT; b0 += BATCH) {
+            float4v v[BATCH];
+#pragma unroll
+            for (int j = 0; j < BATCH; j++) {
+                const int q = (b0 + j) * 64 + lane;
+                v[j] = *(const float4v *)(region + (q / CPR) * ROWB + (q % CPR) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < BATCH; j++) {
+                const int q = (b0 + j) * 64 + lane;
+                const int r = q / CPR, cc = q % CPR;
+                const int row = m_base + pass * PR + r;
+                const int col = n_base + cc * (16 / ES);
                 OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
-                if (col + 16 / ES <= p.N) {
-                    __builtin_memcpy(dst, &v, 16);   // any alignment of the element size
-                } else {
-                    const OutT *e = (const OutT *)&v;
+                if (whole) {
+                    // one 16-byte store, aligned or not (the memory system
+                    // serves misaligned vector stores to global memory)
+                    __builtin_nontemporal_store(v[j], (chunk_t *)dst);
+                } else if (row < p.M) {
+                    if (col + 16 / ES <= p.N) {
+                        __builtin_memcpy(dst, &v[j], 16);   // any alignment of the element size
+                    } else {
+                        const OutT *e = (const OutT *)&v[j];
 #pragma unroll
-                    for (int j = 0; j < 16 / ES; j++)
-                        if (col + j < p.N)
-                            dst[j] = e[j];
+                        for (int i = 0; i < 16 / ES; i++)
+                            if (col + i < p.N)
+                                dst[i] = e[i];
+                    }
                 }
             }
         }

@@ -497,10 +497,6 @@ __device__ __forceinline__ void store4(char *dst, V v)
     }
 }
 
-// 16 bytes of C at the alignment of its element (fp16; fp32 and int32).
-typedef float chunk16_a2 __attribute__((ext_vector_type(4), aligned(2)));
-typedef float chunk16_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
 // Largest power-of-two fraction of the wave tile's rows that fits the budget.
 constexpr int pass_rows(int tm, int fit)
 {
@@ -538,9 +534,11 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
     constexpr int NIT = PR * CPR / 64;                     // read-back instructions per pass
     constexpr int BATCH = NIT < 4 ? NIT : 4;
     static_assert(NIT % BATCH == 0, "whole read-back batches");
-    using chunk_t = typename std::conditional<ES == 2, chunk16_a2, chunk16_a4>::type;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     char *region = smem + wave * REGION;
+    // every row of C starts on a 16-byte boundary (so do the wave tile's
+    // 16-byte chunks: its first column is a multiple of 8 elements)
+    const bool c_lines = ((uintptr_t)p.C & 15) == 0 && (p.ldc * ES) % 16 == 0;
 
 #pragma unroll
     for (int pass = 0; pass < C::TM / PR; pass++) {
@@ -563,13 +561,17 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
         // LDS -> C, 16 bytes per lane, consecutive lanes along a row.  A wave's
         // LDS accesses complete in order, so no barrier is needed: the region
         // is private to this wave.  The reads go out in batches, outside any
-        // bounds test, so that one wait covers a batch; the pass's rows and
-        // the wave tile's columns wholly inside C (wave-uniform) take their
-        // stores without per-chunk tests, marked non-temporal: C is not read
-        // again here, and a round of tiles writes as much C as an XCD's L2
-        // holds, which as ordinary stores evicts the operand panels the next
-        // round's tiles read.
-        const bool whole = m_base + (pass + 1) * PR <= p.M && n_base + C::TN <= p.N;
+        // bounds test, so that one wait covers a batch.  Where the pass's
+        // rows and the wave tile's columns lie wholly inside C and C's rows
+        // start on 16-byte boundaries (wave-uniform), the stores take no
+        // per-chunk tests and are marked non-temporal: C is not read again
+        // here, and a round of tiles writes as much C as an XCD's L2 holds,
+        // which as ordinary stores evicts the operand panels the next
+        // round's tiles read.  Misaligned rows keep ordinary stores, whose
+        // partial lines L2 merges (as non-temporal stores they reached
+        // memory separately: 17 % more bytes written).
+        const bool stream =
+            c_lines && m_base + (pass + 1) * PR <= p.M && n_base + C::TN <= p.N;
 #pragma unroll
         for (int b0 = 0; b0 < NIT; b0 += BATCH) {
             float4v v[BATCH];
@@ -585,10 +587,8 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
                 const int row = m_base + pass * PR + r;
                 const int col = n_base + cc * (16 / ES);
                 OutT *dst = (OutT *)p.C + (int64_t)row * p.ldc + col;
-                if (whole) {
-                    // one 16-byte store, aligned or not (the memory system
-                    // serves misaligned vector stores to global memory)
-                    __builtin_nontemporal_store(v[j], (chunk_t *)dst);
+                if (stream) {
+                    __builtin_nontemporal_store(v[j], (float4v *)dst);   // 16-byte aligned
                 } else if (row < p.M) {
                     if (col + 16 / ES <= p.N) {
                         __builtin_memcpy(dst, &v[j], 16);   // any alignment of the element size

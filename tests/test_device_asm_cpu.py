@@ -8,6 +8,8 @@ compiles gfx950 code without a GPU).
 * Register spills: no kernel may touch scratch (private) memory inside a
   loop, where it would run once per K step; the kernels that spill outside
   their loops are listed here.
+* C stores: every GEMM kernel's epilogue has its non-temporal 16-byte store
+  (wave tiles wholly inside C, rows on 16-byte boundaries).
 """
 import importlib.util
 import os
@@ -76,3 +78,16 @@ def test_spill_report_sees_a_planted_loop_spill(asm):
     text = ("k:   ; @k\n.LBB0_1:\n\tv_add_u32 v1, v2, v3\n"
             "\tscratch_store_dword off, v1, off\n\ts_cbranch_scc1 .LBB0_1\n\ts_endpgm\n")
     assert b.spill_report(text) == {"k": (1, 1)}
+
+
+def test_every_gemm_kernel_streams_whole_c_chunks(asm):
+    _, text = asm
+    starts = [m for m in re.finditer(r"^(_ZN2tg\w*gemm_(?:pipe|staged|single)\w*):", text, re.M)]
+    assert len(starts) > 100
+    missing = []
+    for i, m in enumerate(starts):
+        end = starts[i + 1].start() if i + 1 < len(starts) else len(text)
+        body = text[m.end():end]
+        if not re.search(r"^\s*global_store_dwordx4 [^\n]*\bnt\b", body, re.M):
+            missing.append(m.group(1))
+    assert missing == [], missing[:3]

@@ -225,6 +225,33 @@ def test_padded_leading_dims_and_unaligned_bases(M, N, K, offs):
                a_off=offs[0], b_off=offs[1], c_off=offs[2], what="padded-int")
 
 
+# The epilogue stores C with non-temporal 16-byte stores only where a wave
+# tile lies wholly inside C and every row of C starts on a 16-byte boundary;
+# elsewhere (misaligned base or leading dimension, edge tiles) chunk by chunk
+# with ordinary stores.  Both paths must write the same C.
+STORE_PATH_KERNELS = ["pipe_256x256x64_s2_w2x2_mi16_c3", "pipe_256x256x64_s2_w2x4_mi16_c2",
+                      "pipe_64x64x64_s4_w2x2_mi16_c0", "pipe_64x64x64_s2_w2x2_mi16_c0"]
+
+
+@pytest.mark.parametrize("name", STORE_PATH_KERNELS)
+def test_streamed_and_plain_c_stores_agree(name):
+    cid = [c["id"] for c in tg.configs() if c["name"] == name][0]
+    M, N, K = 520, 776, 256   # whole tiles and wave tiles, and ragged edge tiles
+    A, B = gen.operands(M, N, K, "int", 81)
+    bias = gen.bias_vector(N, 82, integer=True)
+    for c_dtype in ("f16", "f32"):
+        ref, _ = run(A, B, M, N, K, c_dtype, bias=bias, config=cid, what="%s aligned C" % name)
+        parity.check(ref, oracle.gemm_ref(A, B, M, N, K, bias=bias), K, c_dtype, True,
+                     what="%s aligned C" % name)
+        # misaligned base, misaligned rows, padded aligned rows
+        for ldc, c_off in ((N, 1), (N + 1, 0), (N + 8, 0)):
+            what = "%s ldc=%d c_off=%d %s" % (name, ldc, c_off, c_dtype)
+            assert supports(cid, M, N, K, K, N, ldc, c_dtype, True), what
+            out, _ = run(A, B, M, N, K, c_dtype, bias=bias, ldc=ldc, c_off=c_off, config=cid,
+                         what=what)
+            assert np.array_equal(out, ref), what
+
+
 def test_K0_writes_zero_or_relu_bias():
     M, N = 70, 90
     A = np.zeros((M, 0), np.uint16)

@@ -119,9 +119,12 @@ def test_every_fp16_config_sliced(op_a, op_b):
 
 @pytest.mark.parametrize("op_a,op_b", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_every_int8_config_sliced(op_a, op_b):
-    M, N, K = 208, 272, 1040
-    A, B = host_operands(M, N, K, op_a, op_b, "i32", 73)
+    """K = 1040 in 4 slices (K = 1024 for a configuration that runs only K in
+    whole K steps)."""
+    M, N = 208, 272
     for c in configs(1, op_a, op_b):
+        K = 1024 if c["whole_k"] else 1040
+        A, B = host_operands(M, N, K, op_a, op_b, "i32", 73)
         what = "int8 config %d" % c["id"]
         out = run(A, B, M, N, K, "i32", op_a, op_b, config=c["id"], splits=4, what=what)
         check_exact(out, A, B, M, N, K, "i32", op_a, op_b, None, what)

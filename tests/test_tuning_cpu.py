@@ -265,7 +265,7 @@ def exact_shapes():
     text = open(os.path.join(ROOT, "tiled_dense_gemm_08_amd", "csrc",
                              "tg_dispatch_table.inc")).read()
     return {tuple(int(x) for x in m) for m in
-            re.findall(r"\{(\d+), (\d+), (\d+), 0, \d+\}", text)}
+            re.findall(r"\{(\d+), (\d+), (\d+), 0, 2, \d+\}", text)}
 
 
 def aligned_operands(M, N, K, op_a=0, op_b=0, es=2):
@@ -283,8 +283,8 @@ def model_choice(rows, M, N, K, cands, pad):
 
 
 # Configurations the dispatcher runs only on the exact shapes its table
-# lists (no cost-model row): none at present.
-TABLE_ONLY = set()
+# lists (no cost-model row): the 4-wave int8 kernel (int8 8192^3).
+TABLE_ONLY = {27}
 
 
 def test_model_rows_are_valid():

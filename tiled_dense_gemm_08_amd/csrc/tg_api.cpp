@@ -488,11 +488,9 @@ int choose(const Problem &p)
     const int tuned = tuned_lookup(p);
     if (tuned >= 0 && supports(kConfigs[tuned], p))
         return tuned;
-    if (elem_size(p) == 2) {
-        const int exact = dispatch_exact(p.M, p.N, p.K, p.fused);
-        if (exact >= 0 && supports(kConfigs[exact], p))
-            return exact;
-    }
+    const int exact = dispatch_exact(p.M, p.N, p.K, p.fused, elem_size(p));
+    if (exact >= 0 && supports(kConfigs[exact], p))
+        return exact;
     const int modelled = model_lookup(p);
     if (modelled >= 0)
         return modelled;
@@ -930,11 +928,9 @@ Plan plan_auto(const Problem &p, size_t ws_bytes)
     if (sc.slices <= 1) {
         // a measured exact-shape record for the copies' problem overrides the
         // model's kernel (the predicted time still decides whether to pack)
-        if (elem_size(p) == 2) {
-            const int exact = dispatch_exact(chk.M, chk.N, chk.K, chk.fused);
-            if (exact >= 0 && kConfigs[exact].direct && supports(kConfigs[exact], chk))
-                pk.id = exact;
-        }
+        const int exact = dispatch_exact(chk.M, chk.N, chk.K, chk.fused, elem_size(chk));
+        if (exact >= 0 && kConfigs[exact].direct && supports(kConfigs[exact], chk))
+            pk.id = exact;
     } else {
         pk.part_bytes = (size_t)partial_bytes(p, sc.slices);
     }

@@ -393,6 +393,9 @@ __device__ __forceinline__ typename C::acc_t mfma(half8 b, half8 a, typename C::
     if constexpr (C::ES == 2 && C::MI == 16 && C::SCHED == 3) {
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
         return c;
+    } else if constexpr (C::ES == 1 && C::MI == 16 && C::SCHED == 3) {
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+        return c;
     } else if constexpr (C::ES == 1) {
         const int4v bi = __builtin_bit_cast(int4v, b), ai = __builtin_bit_cast(int4v, a);
         if constexpr (C::MI == 16)

@@ -146,6 +146,24 @@ def test_whole_k_configuration_needs_k_in_whole_steps():
                                tg.TG_DTYPE_F16) == cid
 
 
+def test_int8_whole_k_configuration_and_its_table_entry():
+    """The int8 schedule-3 kernel (configuration 27, 128-deep K steps) serves
+    only K in whole steps; the exact-shape table names it for int8 8192^3 in
+    the two orientations it is compiled for, and the other two fall back."""
+    cid = [c["id"] for c in tg.configs() if c["name"] == "i8_pipe_256x256x128_s2_w2x2_mi16_c3"][0]
+    info = tg.tg_config_info(cid)
+    assert info["whole_k"] == 1 and info["elem_bytes"] == 1 and info["block_k"] == 128
+    assert info["ops"] == 3
+    I32 = tg.TG_DTYPE_I32
+    for K, ok in ((1024, 1), (1152, 1), (1088, 0), (1000, 0)):
+        assert tg.tg_config_supports(cid, PA, PB, None, PC, 512, 512, K, K, 512, 512, I32) == ok, K
+    for op_a in (0, 1):
+        for op_b in (0, 1):
+            sel = tg.tg_select_config(PA, PB, None, PC, 8192, 8192, 8192, 8192, 8192, 8192, I32,
+                                      op_a=op_a, op_b=op_b)
+            assert (sel == cid) == (op_a == 0), (op_a, op_b, sel)
+
+
 @pytest.mark.parametrize("M,N,K,lda,ldb,fused,direct", [
     (256, 256, 256, 256, 256, False, True),
     (1024, 1024, 1024, 1024, 1024, False, True),

@@ -543,6 +543,26 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
     // 16-byte chunks: its first column is a multiple of 8 elements)
     const bool c_lines = ((uintptr_t)p.C & 15) == 0 && (p.ldc * ES) % 16 == 0;
 
+    // The bias of the lane's columns, loaded once for every pass: with the
+    // wave tile's columns inside N and a 16-byte aligned bias
+    // (wave-uniform), as 16-byte loads that one wait covers.
+    float4v bvs[BIAS ? C::NT : 1][BIAS ? RUNS : 1];
+    if constexpr (BIAS) {
+        if (p.vec_bias && n_base + C::TN <= p.N) {
+#pragma unroll
+            for (int nt = 0; nt < C::NT; nt++)
+#pragma unroll
+                for (int run = 0; run < RUNS; run++)
+                    bvs[nt][run] = *(const float4v *)(p.bias + n_base + run_col<C>(nt, run));
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < C::NT; nt++)
+#pragma unroll
+                for (int run = 0; run < RUNS; run++)
+                    bvs[nt][run] = load_bias4(p, n_base + run_col<C>(nt, run));
+        }
+    }
+
 #pragma unroll
     for (int pass = 0; pass < C::TM / PR; pass++) {
         // registers -> LDS (row-major, padded rows)
@@ -552,7 +572,7 @@ __device__ __forceinline__ void epilogue(const Params &p, char *smem, int m_base
             for (int run = 0; run < RUNS; run++) {
                 float4v bv = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (BIAS)
-                    bv = load_bias4(p, n_base + run_col<C>(nt, run));
+                    bv = bvs[nt][run];
 #pragma unroll
                 for (int i = 0; i < MT_PASS; i++) {
                     const int mt = pass * MT_PASS + i;

@@ -51,26 +51,26 @@ PEAK_TOPS_INT8 = 2 * PEAK_TFLOPS
 # digest of the kernel sources and the configuration's row: a kernel changed
 # since the counters were taken reports null.
 TRAFFIC_BYTES = {
-    # FETCH_SIZE 796926.0 KiB x 2.0 + WRITE_SIZE 132131.0 KiB x 1.0 (profiles/)
-    ("sq8192", "pipe_256x256x64_s2_w2x2_mi16_c3", "42bbd520dd82bc2c"): 1767406592,
-    # FETCH_SIZE 303454.6 KiB x 2.0 + WRITE_SIZE 88105.4 KiB x 1.0
-    ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x2_mi16_c3", "42bbd520dd82bc2c"): 711694950,
-    # the GEMM on the packed copies: FETCH_SIZE 28449.7 KiB x 2.0 + WRITE_SIZE
-    # 60210.2 KiB x 1.0 (the operand copy kernel before it: 8344.3 and
+    # FETCH_SIZE 798314.3 KiB x 2.0 + WRITE_SIZE 132105.6 KiB x 1.0 (profiles/)
+    ("sq8192", "pipe_256x256x64_s2_w2x2_mi16_c3", "8162f970308eed35"): 1770223821,
+    # FETCH_SIZE 304142.3 KiB x 2.0 + WRITE_SIZE 89453.9 KiB x 1.0
+    ("fused4096x11008x4096", "pipe_256x256x64_s2_w2x2_mi16_c3", "8162f970308eed35"): 714484224,
+    # the GEMM on the packed copies: FETCH_SIZE 28456.4 KiB x 2.0 + WRITE_SIZE
+    # 60208.3 KiB x 1.0 (the operand copy kernel before it: 8344.3 and
     # 16212.2 KiB)
-    ("ragged3001x5003x1031", "pipe_256x256x64_s2_w2x4_mi16_c2", "dfee942c74bcd22d"): 119920230,
-    # FETCH_SIZE 6201.5 KiB x 2.0 + WRITE_SIZE 4096.0 KiB x 1.0
-    ("sq1024", "pipe_64x64x64_s4_w2x2_mi16_c0", "9a1f3fbeb58247bd"): 16894976,
-    # FETCH_SIZE 426.5 KiB x 2.0 + WRITE_SIZE 256.0 KiB x 1.0
-    ("sq256", "pipe_64x64x64_s2_w2x2_mi16_c0", "79eb1f0dfc533728"): 1135616,
-    # FETCH_SIZE 793445.9 KiB x 2.0 + WRITE_SIZE 132139.8 KiB x 1.0
-    ("sq8192_nt", "pipe_256x256x64_s2_w2x2_mi16_c3", "42bbd520dd82bc2c"): 1760288358,
-    # FETCH_SIZE 786666.0 KiB x 2.0 + WRITE_SIZE 131147.2 KiB x 1.0
-    ("sq8192_tn", "pipe_256x256x64_s2_w2x2_mi16_c3", "42bbd520dd82bc2c"): 1745386701,
-    # FETCH_SIZE 393473.1 KiB x 2.0 + WRITE_SIZE 262830.2 KiB x 1.0
-    ("sq8192_i8", "i8_pipe_256x256x128_s2_w2x2_mi16_c3", "23b35fe9575369c7"): 1074971034,
-    # FETCH_SIZE 393584.1 KiB x 2.0 + WRITE_SIZE 262938.0 KiB x 1.0
-    ("sq8192_i8_nt", "i8_pipe_256x256x128_s2_w2x2_mi16_c3", "23b35fe9575369c7"): 1075308749,
+    ("ragged3001x5003x1031", "pipe_256x256x64_s2_w2x4_mi16_c2", "1c4a839d6ac169e6"): 119932006,
+    # FETCH_SIZE 6201.0 KiB x 2.0 + WRITE_SIZE 4096.0 KiB x 1.0
+    ("sq1024", "pipe_64x64x64_s4_w2x2_mi16_c0", "9a2d7a2d08b6a5a0"): 16893952,
+    # FETCH_SIZE 425.0 KiB x 2.0 + WRITE_SIZE 256.0 KiB x 1.0
+    ("sq256", "pipe_64x64x64_s2_w2x2_mi16_c0", "d5b2facb7243ae47"): 1132544,
+    # FETCH_SIZE 810773.4 KiB x 2.0 + WRITE_SIZE 132102.9 KiB x 1.0
+    ("sq8192_nt", "pipe_256x256x64_s2_w2x2_mi16_c3", "8162f970308eed35"): 1795737293,
+    # FETCH_SIZE 786666.5 KiB x 2.0 + WRITE_SIZE 131117.6 KiB x 1.0
+    ("sq8192_tn", "pipe_256x256x64_s2_w2x2_mi16_c3", "8162f970308eed35"): 1745357414,
+    # FETCH_SIZE 393474.4 KiB x 2.0 + WRITE_SIZE 262984.3 KiB x 1.0
+    ("sq8192_i8", "i8_pipe_256x256x128_s2_w2x2_mi16_c3", "4039f9e177d55852"): 1075131494,
+    # FETCH_SIZE 393575.5 KiB x 2.0 + WRITE_SIZE 263129.8 KiB x 1.0
+    ("sq8192_i8_nt", "i8_pipe_256x256x128_s2_w2x2_mi16_c3", "4039f9e177d55852"): 1075487539,
 }
 
 
